@@ -1,0 +1,43 @@
+"""Independent fp64 brute-force check of the C oracle.  Test infrastructure only.
+
+Dequantizes both operands to fp64 with NumPy's own binary16 decoding and forms
+the product with a plain matrix multiply:
+
+    W[r, 32b + j] = (nibble_{r,b,j} - 8) * d_w[r, b]      (Q4_0, GGUF element order)
+    X[n, 32b + j] = q_{n,b,j} * d_x[n, b]                   (Q8_0)
+    y64 = X @ W.T                                           (fp64)
+
+This reaches the GEMV result by a different route from ``q4_oracle.c``
+(dequantize-then-matmul instead of per-block integer sums), so agreement pins
+the oracle's block decoding, offset handling and scaling.  It shares no code
+with the oracle or with the GPU path.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def dequant_q4_0(w: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """Q4_0 blocks [rows][cols/32][18] -> fp64 [rows][cols]."""
+    w = np.asarray(w, dtype=np.uint8).reshape(rows, cols // 32, 18)
+    d = w[:, :, 0:2].copy().view("<f2")[:, :, 0].astype(np.float64)  # NumPy binary16 decode
+    qs = w[:, :, 2:].astype(np.int64)
+    lo = qs & 0x0F          # elements 0..15
+    hi = qs >> 4            # elements 16..31
+    nib = np.concatenate([lo, hi], axis=2)  # [rows][nb][32]
+    return ((nib - 8).astype(np.float64) * d[:, :, None]).reshape(rows, cols)
+
+
+def dequant_q8_0(xq8: np.ndarray, n: int, cols: int) -> np.ndarray:
+    """Q8_0 blocks [n][cols/32][34] -> fp64 [n][cols]."""
+    x = np.asarray(xq8, dtype=np.uint8).reshape(n, cols // 32, 34)
+    d = x[:, :, 0:2].copy().view("<f2")[:, :, 0].astype(np.float64)
+    q = x[:, :, 2:].copy().view(np.int8).astype(np.float64)
+    return (q * d[:, :, None]).reshape(n, cols)
+
+
+def gemv64(w: np.ndarray, xq8: np.ndarray, rows: int, cols: int, n: int) -> np.ndarray:
+    """fp64 y [n][rows] by dequantize-then-matmul."""
+    W = dequant_q4_0(w, rows, cols)
+    X = dequant_q8_0(xq8, n, cols)
+    return X @ W.T

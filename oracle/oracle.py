@@ -1,0 +1,202 @@
+"""ctypes front end of the plain C oracle (``q4_oracle.c``).  Test infrastructure only.
+
+The oracle is a slow, obviously correct CPU implementation of what the GPU path
+computes (the "minfer" README on the nano-inference page: the Q4_0 weight
+format of the GGUF loader bullet, the int8 activations of milestone M3.5, the
+per-block integer sums with the (nibble - 8) offset of milestone M9, and the
+block sizes of milestone M14).  Only ``tests/``, ``__graft_entry__.smoke()``
+and ``bench.py``'s ``cpu_baseline`` leg may import this module; the product
+path never does.  It shares no code with the HIP library.
+
+Canonical layouts used here:
+  Q4_0 weights : uint8 [rows][cols/32][18]  (fp16 d little-endian, 16 nibble bytes)
+  Q8_0 blocks  : uint8 [n][cols/32][34]     (fp16 d little-endian, 32 int8 q)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q4_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+QK = 32
+Q4_BLOCK_BYTES = 18
+Q8_BLOCK_BYTES = 34
+
+
+def build(force: bool = True) -> str:
+    """Compile q4_oracle.c with plain gcc (no fast-math, no contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _bind(path: str):
+    L = ctypes.CDLL(path)
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    L.q4o_fp16_to_f32.argtypes = [ctypes.c_uint16]
+    L.q4o_fp16_to_f32.restype = ctypes.c_float
+    L.q4o_f32_to_fp16.argtypes = [ctypes.c_float]
+    L.q4o_f32_to_fp16.restype = ctypes.c_uint16
+    L.q4o_fp16_to_f32_array.argtypes = [p, p, i64]
+    L.q4o_f32_to_fp16_array.argtypes = [p, p, i64]
+    L.q4o_quantize_q8_0.argtypes = [p, p, i64]
+    L.q4o_quantize_q8_0_block.argtypes = [p, p]
+    L.q4o_decode_q4_0.argtypes = [p, p, p, i64]
+    L.q4o_block_dot.argtypes = [p, p]
+    L.q4o_block_dot.restype = ctypes.c_int32
+    L.q4o_block_sums.argtypes = [p, p, i64, i64, ctypes.c_int, p]
+    L.q4o_gemv.argtypes = [p, p, i64, i64, ctypes.c_int, p, p, p]
+    L.q4o_gemv_rows.argtypes = [p, p, i64, ctypes.c_int, p, i64, p, p]
+    L.q4o_set_threads.argtypes = [ctypes.c_int]
+    L.q4o_max_threads.restype = ctypes.c_int
+    return L
+
+
+def lib():
+    """The default oracle library (built from q4_oracle.c if missing or stale)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        _lib = _bind(_LIB_PATH)
+    return _lib
+
+
+class _Use:
+    """Temporarily route this module's functions to another build of the oracle
+    (used only by the test that plants mistakes in a copy of the oracle)."""
+
+    def __init__(self, path: str):
+        self.L = _bind(path)
+
+    def __enter__(self):
+        global _lib
+        self.prev, _lib = _lib, self.L
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.prev
+
+
+def using(path: str) -> _Use:
+    return _Use(path)
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def set_threads(n: int) -> None:
+    lib().q4o_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().q4o_max_threads())
+
+
+# ---------------------------------------------------------------- binary16
+
+def fp16_to_f32(h: np.ndarray) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, np.float32)
+    lib().q4o_fp16_to_f32_array(_ptr(h), _ptr(out), h.size)
+    return out
+
+
+def f32_to_fp16(f: np.ndarray) -> np.ndarray:
+    """Returns the binary16 bit patterns (uint16)."""
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    out = np.empty(f.shape, np.uint16)
+    lib().q4o_f32_to_fp16_array(_ptr(f), _ptr(out), f.size)
+    return out
+
+
+# ---------------------------------------------------------------- Q8_0
+
+def quantize_q8_0(x: np.ndarray) -> np.ndarray:
+    """x float32 [..., K] (K % 32 == 0) -> uint8 [..., K/32, 34] canonical Q8_0 blocks."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    K = x.shape[-1]
+    assert K % QK == 0
+    out = np.empty(x.shape[:-1] + (K // QK, Q8_BLOCK_BYTES), np.uint8)
+    lib().q4o_quantize_q8_0(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def q8_split(blocks: np.ndarray):
+    """Canonical Q8_0 blocks [..., nb, 34] -> (d fp16 bits [..., nb], q int8 [..., nb*32])."""
+    blocks = np.ascontiguousarray(blocks)
+    d = blocks[..., 0:2].copy().view(np.uint16)[..., 0]
+    q = blocks[..., 2:].copy().view(np.int8)
+    return d, q.reshape(blocks.shape[:-2] + (-1,))
+
+
+# ---------------------------------------------------------------- Q4_0
+
+def decode_q4_0(w: np.ndarray):
+    """Q4_0 blocks [..., 18] -> (d float32 [...], nibbles uint8 [..., 32])."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    nblk = w.size // Q4_BLOCK_BYTES
+    d = np.empty(nblk, np.float32)
+    nib = np.empty(nblk * QK, np.uint8)
+    lib().q4o_decode_q4_0(_ptr(w), _ptr(d), _ptr(nib), nblk)
+    return d.reshape(w.shape[:-1]), nib.reshape(w.shape[:-1] + (QK,))
+
+
+def block_dot(q4_block: np.ndarray, q8_block: np.ndarray) -> int:
+    a = np.ascontiguousarray(q4_block, dtype=np.uint8)
+    b = np.ascontiguousarray(q8_block, dtype=np.uint8)
+    assert a.size == Q4_BLOCK_BYTES and b.size == Q8_BLOCK_BYTES
+    return int(lib().q4o_block_dot(_ptr(a), _ptr(b)))
+
+
+def block_sums(w: np.ndarray, xq8: np.ndarray, rows: int, cols: int, n: int) -> np.ndarray:
+    """-> int32 [n][rows][cols/32]"""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    xq8 = np.ascontiguousarray(xq8, dtype=np.uint8)
+    assert w.size == rows * (cols // QK) * Q4_BLOCK_BYTES
+    assert xq8.size == n * (cols // QK) * Q8_BLOCK_BYTES
+    s = np.empty((n, rows, cols // QK), np.int32)
+    lib().q4o_block_sums(_ptr(w), _ptr(xq8), rows, cols, n, _ptr(s))
+    return s
+
+
+def gemv(w: np.ndarray, xq8: np.ndarray, rows: int, cols: int, n: int, want_y64: bool = False):
+    """-> (y float32 [n][rows], S float64 [n][rows][, y64 float64 [n][rows]])"""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    xq8 = np.ascontiguousarray(xq8, dtype=np.uint8)
+    assert w.size == rows * (cols // QK) * Q4_BLOCK_BYTES
+    assert xq8.size == n * (cols // QK) * Q8_BLOCK_BYTES
+    y = np.empty((n, rows), np.float32)
+    S = np.empty((n, rows), np.float64)
+    y64 = np.empty((n, rows), np.float64) if want_y64 else None
+    lib().q4o_gemv(_ptr(w), _ptr(xq8), rows, cols, n, _ptr(y), _ptr(S),
+                   _ptr(y64) if want_y64 else None)
+    return (y, S, y64) if want_y64 else (y, S)
+
+
+def gemv_rows(w: np.ndarray, xq8: np.ndarray, cols: int, n: int, row_idx: np.ndarray):
+    """Selected output rows of the full matrix w -> (y [n][len(row_idx)], S [n][len(row_idx)])."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    xq8 = np.ascontiguousarray(xq8, dtype=np.uint8)
+    idx = np.ascontiguousarray(row_idx, dtype=np.int64)
+    rows = w.size // ((cols // QK) * Q4_BLOCK_BYTES)
+    assert idx.size == 0 or (idx.min() >= 0 and idx.max() < rows)
+    y = np.empty((n, idx.size), np.float32)
+    S = np.empty((n, idx.size), np.float64)
+    lib().q4o_gemv_rows(_ptr(w), _ptr(xq8), cols, n, _ptr(idx), idx.size, _ptr(y), _ptr(S))
+    return y, S

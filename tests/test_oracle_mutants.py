@@ -1,0 +1,103 @@
+"""The oracle's pins are strong enough: each plausible mistake planted in a copy
+of the oracle (on the CPU) makes at least one pin fail, and the unmodified copy
+passes them all."""
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import test_oracle_fp16 as t16
+import test_oracle_q4 as t4
+import test_oracle_q8 as t8
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
+                   "q4_oracle.c")
+
+MUTANTS = [
+    ("nibble_halves_swapped",
+     "return j < 16 ? (qs[j] & 0x0f) : (qs[j - 16] >> 4);",
+     "return j < 16 ? (qs[j] >> 4) : (qs[j - 16] & 0x0f);"),
+    ("offset_dropped", "s += (q4_nibble(q4_block, j) - 8) * (int32_t)q[j];",
+     "s += (q4_nibble(q4_block, j)) * (int32_t)q[j];"),
+    ("offset_sign", "s += (q4_nibble(q4_block, j) - 8) * (int32_t)q[j];",
+     "s += (8 - q4_nibble(q4_block, j)) * (int32_t)q[j];"),
+    ("round_half_even", "float r = roundf(v);", "float r = nearbyintf(v);"),
+    ("round_floor_plus_half", "float r = roundf(v);", "float r = floorf(v + 0.5f);"),
+    ("divide_by_fp16_scale", "float v = x[j] / d;",
+     "float v = x[j] / q4o_fp16_to_f32(q4o_f32_to_fp16(d));"),
+    ("multiply_by_reciprocal", "float v = x[j] / d;", "float v = x[j] * (1.0f / d);"),
+    ("scale_from_signed_max", "float a = fabsf(x[j]);", "float a = x[j];"),
+    ("scale_255", "float d = amax / 127.0f;", "float d = amax / 128.0f;"),
+    ("fp16_encode_truncates", "double r = nearbyint(k);", "double r = floor(k);"),
+    ("fp16_encode_ties_away", "double r = nearbyint(k);", "double r = round(k);"),
+    ("fp16_subnormal_decode", "v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+    ("scale_product_drops_dx", "double p = dw * dx;", "double p = dw;"),
+    ("accumulate_sign", "acc += t;", "acc -= t;"),
+    ("scale_big_endian", "return (uint16_t)(p[0] | (p[1] << 8));",
+     "return (uint16_t)(p[1] | (p[0] << 8));"),
+    ("activation_row_ignored",
+     "gemv_one(w + r * nb * Q4_BLOCK_BYTES, xq8 + (int64_t)t * nb * Q8_BLOCK_BYTES, nb,",
+     "gemv_one(w + r * nb * Q4_BLOCK_BYTES, xq8, nb,"),
+    ("last_block_dropped", "for (int64_t b = 0; b < nb; ++b) {\n        const uint8_t* wb",
+     "for (int64_t b = 0; b + 1 < nb; ++b) {\n        const uint8_t* wb"),
+]
+
+
+def _pins(o, b):
+    """Run the oracle's pins; return the names of those that fail."""
+    checks = [("fp16_exhaustive", lambda: t16.test_fp16_decode_exhaustive(o)),
+              ("fp16_ties", lambda: t16.test_fp16_encode_every_tie_and_neighbour(o)),
+              ("fp16_specials", lambda: t16.test_fp16_encode_specials(o)),
+              ("q8_properties", lambda: t8.test_q8_0_properties_random(o)),
+              ("q8_near_ties", lambda: t8.test_q8_0_near_ties(o)),
+              ("sum_fold_brute", lambda: t4.test_block_sums_fold_identity_and_brute_force(o)),
+              ("gemv_golden", lambda: t4.test_gemv_golden_small(o)),
+              ("gemv_zero", lambda: t4.test_gemv_all_eight_nibbles_is_exact_zero(o)),
+              ("gemv_one_hot", lambda: t4.test_gemv_one_hot_activation_closed_form(o)),
+              ("gemv_brute_a", lambda: t4.test_gemv_matches_fp64_bruteforce(o, b, 17, 288, 8)),
+              ("gemv_brute_b", lambda: t4.test_gemv_matches_fp64_bruteforce(o, b, 70, 96, 1))]
+    checks += [(f"q8_golden_{c['name']}", (lambda c=c: t8.test_q8_0_golden_blocks(o, c)))
+               for c in t8.CASES]
+    checks += [(f"q4_golden_{c['name']}", (lambda c=c: t4.test_q4_0_golden_decode(o, c)))
+               for c in t4.Q4_CASES]
+    checks += [(f"sum_golden_{c['name']}", (lambda c=c: t4.test_block_sum_golden(o, c)))
+               for c in t4.SUM_CASES]
+    failed = []
+    with np.errstate(all="ignore"):
+        for name, fn in checks:
+            try:
+                fn()
+            except AssertionError:
+                failed.append(name)
+    return failed
+
+
+def _build_variant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    if old is not None:
+        assert src.count(old) == 1, f"mutation site for {name} not unique"
+        src = src.replace(old, new)
+    c = tmp_path / f"{name}.c"
+    c.write_text(src)
+    so = tmp_path / f"lib{name}.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-o",
+                    str(so), str(c), "-lm"], check=True)
+    return str(so)
+
+
+def test_unmodified_copy_passes_all_pins(oracle, bruteforce, tmp_path):
+    so = _build_variant(tmp_path, "control", None, None)
+    with oracle.using(so):
+        assert _pins(oracle, bruteforce) == []
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(oracle, bruteforce, tmp_path, name, old, new):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc missing")
+    so = _build_variant(tmp_path, name, old, new)
+    with oracle.using(so):
+        failed = _pins(oracle, bruteforce)
+    assert failed, f"mutant {name} survived every pin"
