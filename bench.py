@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark: Q4_0 x Q8_0 weight-streaming GEMV sweep on one MI355X.
+
+A step is one pass of the whole hot path over one decode token's projections:
+one launch quantizes every matrix's fresh fp32 activation to Q8_0, one launch
+streams every Q4_0 matrix once and writes every output.  Weights are synthetic,
+seeded, Qwen2.5-shaped; consecutive steps alternate between seeded copies of the
+weight set so no step finds the previous step's bytes in the 256 MB Infinity
+Cache.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload qwen2.5-1.5b|qwen2.5-7b|lm_head] [--n N]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "Q4_0 GEMV weight-stream GB/s (% of 8 TB/s HBM peak) and implied tok/s at N=1"
+KERNEL_SRC = os.path.join(ROOT, "q4_weight_streaming_amd", "csrc", "q4s_kernels.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def workload_shapes(name: str):
+    from q4_weight_streaming_amd import synth
+    if name == "qwen2.5-1.5b":
+        return synth.qwen25_1p5b(), 1, 2
+    if name == "qwen2.5-7b":
+        return synth.qwen25_7b(), 4, 1
+    if name == "lm_head":
+        return [synth.MatShape("lm_head", 151936, 1536)], 2, 4
+    raise SystemExit(f"unknown workload {name}")
+
+
+def make_copy(shapes, cfg: int, copy: int, n: int, dev, keep_host: bool, act_cfg: int | None = None):
+    """One seeded copy of the weight set with its activations and outputs."""
+    import numpy as np  # noqa: F401
+    import torch
+
+    from q4_weight_streaming_amd import _lib as q
+    from q4_weight_streaming_amd import synth
+    mats, host = [], []
+    for m, s in enumerate(shapes):
+        w = synth.q4_0_weights(s.rows, s.cols, synth.generator(cfg, m, copy, 0))
+        x = synth.activation(n, s.cols, synth.generator(cfg if act_cfg is None else act_cfg, m, copy, 1),
+                             outliers=0 if s.name == "lm_head" and len(shapes) == 1 else 8)
+        wc = torch.from_numpy(w.reshape(-1)).to(dev)
+        wp = q.repack_q4_0(wc, s.rows, s.cols)
+        del wc
+        mats.append({"w_packed": wp, "x": torch.from_numpy(x).to(dev),
+                     "x_q8": torch.empty(q.q8_bytes(n, s.cols), dtype=torch.uint8, device=dev),
+                     "y": torch.empty((n, s.rows), dtype=torch.float32, device=dev),
+                     "rows": s.rows, "cols": s.cols})
+        if keep_host:
+            host.append((w, x))
+    torch.cuda.synchronize()
+    return mats, host
+
+
+def time_steps(run_fns, steps: int, warmup: int, stream):
+    """Average ms per step of run_fns[i % len] over `steps` steps, after `warmup`."""
+    import torch
+    for i in range(warmup):
+        run_fns[i % len(run_fns)]()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        run_fns[i % len(run_fns)]()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def time_kernel(run_fns, steps: int, stream):
+    """Average duration of each launch of run_fns, bracketed by events on its stream."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        run_fns[i % len(run_fns)]()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    d = sorted(a.elapsed_time(b) for a, b in ev)
+    return sum(d) / len(d), d[len(d) // 2], d[0]
+
+
+def traffic_from_profile(workload: str, n: int, launch_bytes: int):
+    """HBM bytes per GEMV launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"sweep_{workload}_n{n}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(host, shapes, n: int, budget_s: float):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+    from oracle import oracle
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    done_bytes, done = 0, 0
+    for (w, x), s in zip(host, shapes):
+        xq = oracle.quantize_q8_0(x)
+        oracle.gemv(w, xq, s.rows, s.cols, n)
+        done_bytes += s.q4_bytes
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(shapes)} matrices of copy 0 ({done_bytes} Q4_0 bytes), quantize + GEMV, "
+                      f"one pass, {dt:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen2.5-1.5b", choices=["qwen2.5-1.5b", "qwen2.5-7b", "lm_head"])
+    ap.add_argument("--n", type=int, default=1, help="activation rows per GEMV (1..8)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify-ratio", action="store_true", help="skip the N=8 / N=1 step-cost ratio")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--profile-only", action="store_true",
+                    help="run a few GEMV-only sweeps plus a 1 GiB copy, for rocprofv3 counter runs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU part; see DESIGN.md for how it would shard)", file=sys.stderr)
+        return 2
+    if not 1 <= args.n <= 8:
+        raise SystemExit("--n must be in 1..8")
+
+    import torch
+
+    from q4_weight_streaming_amd import _lib as q
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    q.lib()
+
+    shapes, cfg, ncopies = workload_shapes(args.workload)
+    n = args.n
+    log(f"generating {ncopies} copies of {args.workload} ({len(shapes)} matrices), n={n}")
+    copies, host0 = [], None
+    for c in range(ncopies):
+        mats, host = make_copy(shapes, cfg, c, n, dev, keep_host=(c == 0 and not args.no_cpu_baseline))
+        copies.append(mats)
+        if c == 0:
+            host0 = host
+        log(f"copy {c} ready")
+    full = [q.Sweep(m, n) for m in copies]                                 # quantize + GEMV
+    gemv = [q.Sweep([{k: v for k, v in mm.items() if k != "x"} for mm in m], n) for m in copies]
+    info = gemv[0].info()
+    weight_bytes = info["weight_bytes"]
+    launch_bytes = info["weight_bytes"] + info["act_bytes"] + info["out_bytes"]
+
+    if args.profile_only:
+        for p in full:
+            p.run()                              # quantized activations in place
+        for i in range(10):
+            gemv[i % ncopies].run()
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        q.bench_copy(src, dst)
+        torch.cuda.synchronize()
+        log(f"profile run done: 10 GEMV sweeps of {launch_bytes} algorithmic bytes, one 1 GiB copy")
+        return 0
+
+    ms = time_steps([p.run for p in full], args.steps, args.warmup, stream)
+    log(f"step {ms * 1e3:.1f} us")
+    k_avg, k_med, k_min = time_kernel([p.run for p in gemv], args.steps, stream)
+    log(f"GEMV launch avg {k_avg * 1e3:.1f} us, median {k_med * 1e3:.1f}, min {k_min * 1e3:.1f}")
+
+    value = weight_bytes / (ms * 1e-3) / 1e9
+    achieved = launch_bytes / (k_avg * 1e-3) / 1e9
+    traffic = traffic_from_profile(args.workload, n, launch_bytes)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload} decode sweep, {len(shapes)} Q4_0 matrices "
+                               f"({weight_bytes} B), N={n}, fresh Q8_0-quantized fp32 activation per "
+                               f"matrix, {ncopies} rotated seeded copies",
+                   "n": n, "matrices": len(shapes), "weight_bytes": weight_bytes, "copies": ncopies,
+                   "launches_per_step": 2, "accumulate": "f32", "gemv_tiles": info["n_tiles"]},
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "tok_s": round(1000.0 / ms, 1) if n == 1 else None,
+        "gemv_only": {"us_avg": round(k_avg * 1e3, 2), "us_median": round(k_med * 1e3, 2),
+                      "us_min": round(k_min * 1e3, 2),
+                      "weight_gb_s": round(weight_bytes / (k_avg * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "k_sweep (GEMV launch of the sweep)", "algorithmic_bytes_per_launch": launch_bytes},
+    }
+
+    if n == 1 and not args.no_verify_ratio:
+        # the same weight copies stepped with 8 activation rows (multi-token verify)
+        n8 = []
+        for c, m in enumerate(copies):
+            mats8 = []
+            for mi, (s, mm) in enumerate(zip(shapes, m)):
+                from q4_weight_streaming_amd import synth
+                x = synth.activation(8, s.cols, synth.generator(3, mi, c, 1))
+                mats8.append({"w_packed": mm["w_packed"], "x": torch.from_numpy(x).to(dev),
+                              "x_q8": torch.empty(q.q8_bytes(8, s.cols), dtype=torch.uint8, device=dev),
+                              "y": torch.empty((8, s.rows), dtype=torch.float32, device=dev),
+                              "rows": s.rows, "cols": s.cols})
+            n8.append(q.Sweep(mats8, 8))
+        ms8 = time_steps([p.run for p in n8], args.steps, args.warmup, stream)
+        out["verify_n8"] = {"ms_per_step": round(ms8, 5), "ratio_to_n1": round(ms8 / ms, 3)}
+        log(f"n=8 step {ms8 * 1e3:.1f} us, ratio {ms8 / ms:.3f}")
+        del n8
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(host0, shapes, n, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

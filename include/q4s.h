@@ -1,0 +1,237 @@
+/*
+ * q4s.h -- C ABI of libq4stream: Q4_0-weight x Q8_0-activation weight-streaming
+ * GEMV / skinny GEMM (1 to 8 activation rows) for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (the "minfer" README on the nano-inference page):
+ *   - weights stay quantized in GPU memory as Q4_0 ("How it works", the
+ *     cuda_infer bullet) and are repacked once at load time into 32-row groups
+ *     so a warp reads one contiguous span ("How it works", the mega.cu bullet;
+ *     milestone M15);
+ *   - the activation is quantized to int8 once per product (milestones M3.5
+ *     and M15) in the Q8_0 block format (34-byte blocks, milestone M14);
+ *   - each output is a sum over 32-wide blocks of an exact integer dot
+ *     s = sum_j (nibble_j - 8) * q_j (milestone M9), scaled by d_w * d_x and
+ *     accumulated in fp32 ("How it works", mega.cu bullet; milestone M16);
+ *   - a step carries up to 8 activation rows that share one pass over the
+ *     weights (mega.cu bullet; milestone M16), with every row's result
+ *     bit-identical to the same row computed alone;
+ *   - a whole decode step's projections stream in one launch instead of one
+ *     launch per matrix (Results paragraph on the roofline; milestone M15).
+ *
+ * Conventions for every entry point:
+ *   - Buffers are device memory owned by the caller.  Nothing here allocates,
+ *     frees or synchronizes device memory, except q4s_sweep_plan_upload, which
+ *     copies the plan's tables into caller-provided device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     call only enqueues work on it; buffers must stay alive until it completes.
+ *   - Arguments are validated before any HIP call; a failed check returns a
+ *     status other than Q4S_OK and enqueues nothing.  q4s_last_error() then
+ *     describes the failure (thread-local).  No C++ exception crosses the ABI.
+ *   - A launch failure reported by the HIP runtime returns Q4S_ERR_HIP; faults
+ *     inside a kernel surface at the caller's next stream synchronization.
+ *   - A pointer may be NULL only when the buffer it names has 0 bytes.
+ *   - Shapes: rows >= 0, cols >= 0 with cols % 32 == 0, n in 0..8, and
+ *     rows, cols < 2^31.  rows == 0 or n == 0 is a no-op; cols == 0 writes
+ *     y = 0 (the empty sum).
+ *
+ * Layouts:
+ *   Canonical Q4_0 (GGUF): [rows][cols/32] blocks of 18 bytes: binary16 scale
+ *     d_w (little-endian), then 16 bytes qs; element j < 16 is qs[j] & 0xF,
+ *     element j >= 16 is qs[j-16] >> 4; weight = (nibble - 8) * d_w.
+ *   Packed Q4_0 (this library, produced by q4s_repack_q4_0): rows padded to a
+ *     multiple of 64 (G = ceil(rows/64) groups), blocks padded to a multiple of
+ *     8 (C = ceil(cols/256) chunks).  Group g, chunk c occupies 9216 bytes at
+ *     offset (g*C + c) * 9216:
+ *       bytes [0, 8192)   : nibbles, [8 blocks][64 rows][16 bytes]; each byte is
+ *                           the canonical qs byte XOR 0x88, i.e. both nibbles
+ *                           hold (nibble - 8) in 4-bit two's complement;
+ *       bytes [8192, 9216): scales, [64 rows][8 blocks] binary16 d_w.
+ *     Padding rows and blocks hold zero bytes (weight 0, scale 0).
+ *   Q8_0 activation (planar): for n rows of cols values,
+ *       bytes [0, n*cols)             : q, int8 [n][cols];
+ *       bytes [n*cols, n*cols*34/32)  : d_x, binary16 [n][cols/32];
+ *     the buffer is q4s_q8_bytes(n, cols) long (rounded up to 16 bytes).
+ *     Per 32-block: d = max|x| / 127 (fp32, correctly rounded); q =
+ *     round-half-away-from-zero(x / d) with the fp32 d as divisor; stored
+ *     d_x = binary16(d) (round to nearest even, subnormals kept).  An
+ *     all-zero block stores d_x = +0, q = 0.  Inputs must be finite with
+ *     |x| < 8e6 (so d_x stays finite).
+ *   Output y: fp32 [n][rows], row-major.
+ *
+ * Numerics: per block the kernel forms the exact integer s, then
+ *   part = fmaf(d_w * d_x, (float)s, part) over the 8 blocks of a 256-column
+ *   chunk (d_w * d_x is exact in fp32), adds the chunk partial to the row
+ *   accumulator in chunk order, and, for long rows split over the 4 waves of a
+ *   workgroup, adds the (up to 4) split accumulators in split order.  The
+ *   partition depends only on (rows, cols), so results are deterministic,
+ *   identical for every n (row t of an n-row call equals the 1-row call bit
+ *   for bit), and identical between q4s_gemv_q4_0 and q4s_sweep_run.
+ *   Against the exact result the error is below 1e-5 * sum_b |d_w d_x s|.
+ */
+#ifndef Q4S_H
+#define Q4S_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4S_ABI_VERSION 1
+#define Q4S_MAX_N 8
+
+typedef enum {
+    Q4S_OK = 0,
+    Q4S_ERR_NULL = 1,      /* a required pointer is NULL                    */
+    Q4S_ERR_SHAPE = 2,     /* rows / cols / n out of range                  */
+    Q4S_ERR_ALIGN = 3,     /* pointer misaligned for its layout             */
+    Q4S_ERR_ALIAS = 4,     /* an output buffer overlaps an input buffer     */
+    Q4S_ERR_PLAN = 5,      /* invalid plan, plan memory or matrix table     */
+    Q4S_ERR_HIP = 6        /* the HIP runtime reported an error             */
+} q4s_status;
+
+/* ---------------------------------------------------------------- general */
+
+/* Q4S_ABI_VERSION of the loaded library. */
+int q4s_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* q4s_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* q4s_last_error(void);
+
+/* --------------------------------------------------------------- sizes */
+
+/* Canonical Q4_0 bytes: rows * cols/32 * 18.  0 for invalid shapes. */
+size_t q4s_q4_0_bytes(int64_t rows, int64_t cols);
+
+/* Packed Q4_0 bytes: ceil(rows/64) * ceil(cols/256) * 9216.  0 if invalid. */
+size_t q4s_packed_bytes(int64_t rows, int64_t cols);
+
+/* Planar Q8_0 bytes for n rows: n * cols * 34 / 32 rounded up to a multiple of
+ * 16 (the GEMV reads scales as whole dwords).  0 if invalid. */
+size_t q4s_q8_bytes(int n, int64_t cols);
+
+/* ----------------------------------------------------------- operations */
+
+/*
+ * Weight repack (load time).  w_q4_0: canonical Q4_0 [rows][cols/32] x 18 B
+ * (2-byte aligned); w_packed: q4s_packed_bytes(rows, cols) bytes (16-byte
+ * aligned), fully overwritten, padding included.  Lossless: the canonical
+ * bytes are recoverable from the packed ones (layout above).
+ * Source: mega.cu bullet of "How it works" and milestone M15 (row-group
+ * packing at load).
+ */
+q4s_status q4s_repack_q4_0(const void* w_q4_0, void* w_packed, int64_t rows, int64_t cols,
+                           void* stream);
+
+/*
+ * Q8_0 activation quantization.  x: fp32 [n][cols] (4-byte aligned);
+ * x_q8: q4s_q8_bytes(n, cols) bytes (16-byte aligned), planar layout above.
+ * Source: milestones M3.5 and M15 (int8 activations, quantized once), M14
+ * (34-byte Q8_0 blocks).
+ */
+q4s_status q4s_quantize_q8_0(const float* x, void* x_q8, int n, int64_t cols, void* stream);
+
+/*
+ * y[t][r] = sum_b d_w[r][b] * d_x[t][b] * s[t][r][b] for t < n, r < rows.
+ * w_packed: packed Q4_0 (16-byte aligned); x_q8: planar Q8_0 of n rows
+ * (16-byte aligned); y: fp32 [n][rows] (4-byte aligned), must not overlap
+ * either input.  n in 0..8.  Needs no workspace.
+ * Source: cuda_infer and mega.cu bullets of "How it works"; milestones M9,
+ * M15, M16.
+ */
+q4s_status q4s_gemv_q4_0(const void* w_packed, const void* x_q8, float* y, int64_t rows,
+                         int64_t cols, int n, void* stream);
+
+/*
+ * Test hook: the exact per-block integer sums s[t][r][b] = sum_j
+ * (nibble_{r,b,j} - 8) * q_{t,b,j}, int32 [n][rows][cols/32], computed by the
+ * same device code as the GEMV.  Source: milestone M9.
+ */
+q4s_status q4s_block_sums(const void* w_packed, const void* x_q8, int32_t* s, int64_t rows,
+                          int64_t cols, int n, void* stream);
+
+/* ---------------------------------------------------- layer-stack sweep */
+
+/*
+ * One matrix of a sweep.  When x is non-NULL, q4s_sweep_run first quantizes
+ * x (fp32 [n][cols]) into x_q8; otherwise x_q8 must already hold the planar
+ * Q8_0 activation.  y: fp32 [n][rows].
+ */
+typedef struct {
+    const void* w_packed;
+    const float* x;
+    void* x_q8;
+    float* y;
+    int64_t rows;
+    int64_t cols;
+} q4s_mat;
+
+typedef struct q4s_plan q4s_plan; /* opaque; host memory only */
+
+typedef struct {
+    int64_t n_mats;
+    int64_t n_tiles;          /* workgroups of the GEMV launch                */
+    int64_t n_quant_blocks;   /* Q8_0 blocks quantized per run (0: none)      */
+    int64_t weight_bytes;     /* canonical Q4_0 bytes of all matrices         */
+    int64_t packed_bytes;     /* packed bytes read by one run                 */
+    int64_t act_bytes;        /* Q8_0 activation bytes read by one run        */
+    int64_t out_bytes;        /* y bytes written by one run                   */
+    int64_t dev_bytes;        /* device memory the plan needs                 */
+} q4s_plan_info;
+
+/*
+ * Build a plan for n activation rows (1..8) over n_mats matrices (the table is
+ * copied; the buffers it names must stay valid for every run).  Every matrix
+ * is checked as in q4s_gemv_q4_0 (a matrix with x is quantized even when
+ * rows == 0).  No y may overlap any w_packed, x_q8 or x of the sweep, and no
+ * x_q8 may overlap any x; several matrices may read one x_q8.  *dev_bytes_needed receives the device memory size
+ * q4s_sweep_plan_upload needs.  Source: Results paragraph on the roofline and
+ * milestone M15 (one persistent launch for every projection of a step).
+ */
+q4s_status q4s_sweep_plan_create(const q4s_mat* mats, int n_mats, int n,
+                                 size_t* dev_bytes_needed, q4s_plan** out);
+
+/*
+ * Copy the plan's tables into dev_mem (16-byte aligned, >= dev_bytes_needed
+ * bytes, owned by the caller and kept alive while the plan is used).  The copy
+ * is enqueued on `stream` from host memory held by the plan.
+ */
+q4s_status q4s_sweep_plan_upload(q4s_plan* plan, void* dev_mem, size_t dev_bytes, void* stream);
+/* (Destroy the plan only after `stream` has completed the upload.) */
+
+/*
+ * One sweep: if any matrix has x, one launch quantizes all of them; then one
+ * launch streams every matrix's weights once and writes every y.  Calls on
+ * one plan must not overlap in time (they share the plan's device tables only
+ * for reading, but write the same y and x_q8 buffers).
+ */
+q4s_status q4s_sweep_run(const q4s_plan* plan, void* stream);
+
+q4s_status q4s_sweep_plan_info(const q4s_plan* plan, q4s_plan_info* info);
+
+void q4s_sweep_plan_destroy(q4s_plan* plan);
+
+/* -------------------------------------------------- measurement helpers */
+
+/*
+ * Streaming-read microbenchmark (the roofline kernel of milestone M15): reads
+ * `bytes` (a multiple of 16) from `buf` (16-byte aligned) with 16-byte loads,
+ * `loads_in_flight` (1, 2, 4 or 8) per thread per iteration, using `n_blocks`
+ * workgroups of 256 threads (0: 2048); writes one word to `sink` (device,
+ * 4 bytes) only if a practically impossible checksum occurs.
+ */
+q4s_status q4s_bench_read(const void* buf, size_t bytes, int loads_in_flight, int n_blocks,
+                          uint32_t* sink, void* stream);
+
+/* Plain 16-byte copy of `bytes` (a multiple of 16) from src to dst. */
+q4s_status q4s_bench_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4S_H */

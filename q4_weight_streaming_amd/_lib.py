@@ -1,0 +1,246 @@
+"""ctypes binding of libq4stream (include/q4s.h): argument marshalling only.
+
+Every computation runs in the HIP library.  PyTorch supplies device memory and
+the current stream; this module only checks tensor placement, passes
+``data_ptr()`` values and the stream handle, and turns status codes into
+exceptions.  If the library is not built the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libq4stream.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "q4s.h")
+MAX_N = 8
+
+_lib = None
+
+
+class Q4SError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn}: {status_string(status)} ({detail})")
+        self.status = status
+
+
+class _Mat(ctypes.Structure):
+    _fields_ = [("w_packed", ctypes.c_void_p), ("x", ctypes.c_void_p), ("x_q8", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_int64) for k in
+                ("n_mats", "n_tiles", "n_quant_blocks", "weight_bytes", "packed_bytes", "act_bytes",
+                 "out_bytes", "dev_bytes")]
+
+    def as_dict(self) -> dict:
+        return {k: int(getattr(self, k)) for k, _ in self._fields_}
+
+
+def lib():
+    """The loaded library; raises if libq4stream.so has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m q4_weight_streaming_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        sig = {
+            "q4s_abi_version": ([], i32),
+            "q4s_status_string": ([i32], ctypes.c_char_p),
+            "q4s_last_error": ([], ctypes.c_char_p),
+            "q4s_q4_0_bytes": ([i64, i64], sz),
+            "q4s_packed_bytes": ([i64, i64], sz),
+            "q4s_q8_bytes": ([i32, i64], sz),
+            "q4s_repack_q4_0": ([p, p, i64, i64, p], i32),
+            "q4s_quantize_q8_0": ([p, p, i32, i64, p], i32),
+            "q4s_gemv_q4_0": ([p, p, p, i64, i64, i32, p], i32),
+            "q4s_block_sums": ([p, p, p, i64, i64, i32, p], i32),
+            "q4s_sweep_plan_create": ([p, i32, i32, ctypes.POINTER(sz), ctypes.POINTER(p)], i32),
+            "q4s_sweep_plan_upload": ([p, p, sz, p], i32),
+            "q4s_sweep_run": ([p, p], i32),
+            "q4s_sweep_plan_info": ([p, ctypes.POINTER(PlanInfo)], i32),
+            "q4s_sweep_plan_destroy": ([p], None),
+            "q4s_bench_read": ([p, sz, i32, i32, p, p], i32),
+            "q4s_bench_copy": ([p, p, sz, p], i32),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        if L.q4s_abi_version() != 1:
+            raise RuntimeError("libq4stream ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/q4s.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4s_[a-z0-9_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib().q4s_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise Q4SError(fn, status, lib().q4s_last_error().decode())
+
+
+def _stream(device: torch.device | None = None) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype | None = None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+# ------------------------------------------------------------------ sizes
+
+def q4_0_bytes(rows: int, cols: int) -> int:
+    return int(lib().q4s_q4_0_bytes(rows, cols))
+
+
+def packed_bytes(rows: int, cols: int) -> int:
+    return int(lib().q4s_packed_bytes(rows, cols))
+
+
+def q8_bytes(n: int, cols: int) -> int:
+    return int(lib().q4s_q8_bytes(n, cols))
+
+
+# ------------------------------------------------------------- operations
+
+def repack_q4_0(w_q4_0: torch.Tensor, rows: int, cols: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Canonical Q4_0 bytes (uint8, rows*cols/32*18) -> packed uint8 tensor."""
+    if w_q4_0.numel() != q4_0_bytes(rows, cols) or w_q4_0.dtype != torch.uint8:
+        raise ValueError("w_q4_0 must be uint8 with rows*cols/32*18 elements")
+    if out is None:
+        out = torch.empty(packed_bytes(rows, cols), dtype=torch.uint8, device=w_q4_0.device)
+    _check("q4s_repack_q4_0", lib().q4s_repack_q4_0(_dev(w_q4_0, "w_q4_0"), _dev(out, "out", torch.uint8),
+                                                     rows, cols, _stream(w_q4_0.device)))
+    return out
+
+
+def quantize_q8_0(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 [n][cols] -> planar Q8_0 bytes (uint8, q8_bytes(n, cols))."""
+    if x.dim() != 2:
+        raise ValueError("x must be [n][cols]")
+    n, cols = x.shape
+    if out is None:
+        out = torch.empty(q8_bytes(n, cols), dtype=torch.uint8, device=x.device)
+    _check("q4s_quantize_q8_0", lib().q4s_quantize_q8_0(_dev(x, "x", torch.float32), _dev(out, "out", torch.uint8),
+                                                         n, cols, _stream(x.device)))
+    return out
+
+
+def q8_views(x_q8: torch.Tensor, n: int, cols: int):
+    """Views of a planar Q8_0 buffer: (q int8 [n][cols], d binary16 bits int16 [n][cols/32])."""
+    q = x_q8[: n * cols].view(torch.int8).view(n, cols)
+    d = x_q8[n * cols: n * cols + n * cols // 16].view(torch.int16).view(n, cols // 32)
+    return q, d
+
+
+def gemv_q4_0(w_packed: torch.Tensor, x_q8: torch.Tensor, rows: int, cols: int, n: int,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """y fp32 [n][rows] = Q4_0 W [rows][cols] x Q8_0 activation rows."""
+    if out is None:
+        out = torch.empty((n, rows), dtype=torch.float32, device=w_packed.device)
+    _check("q4s_gemv_q4_0", lib().q4s_gemv_q4_0(_dev(w_packed, "w_packed", torch.uint8),
+                                                 _dev(x_q8, "x_q8", torch.uint8),
+                                                 _dev(out, "out", torch.float32), rows, cols, n,
+                                                 _stream(w_packed.device)))
+    return out
+
+
+def block_sums(w_packed: torch.Tensor, x_q8: torch.Tensor, rows: int, cols: int, n: int) -> torch.Tensor:
+    """Per-block integer sums, int32 [n][rows][cols/32]."""
+    out = torch.empty((n, rows, cols // 32), dtype=torch.int32, device=w_packed.device)
+    _check("q4s_block_sums", lib().q4s_block_sums(_dev(w_packed, "w_packed", torch.uint8),
+                                                   _dev(x_q8, "x_q8", torch.uint8),
+                                                   _dev(out, "out", torch.int32), rows, cols, n,
+                                                   _stream(w_packed.device)))
+    return out
+
+
+class Sweep:
+    """A layer-stack sweep over many matrices with n activation rows each.
+
+    mats: sequence of dicts with keys w_packed, x_q8, y, rows, cols and optional x
+    (fp32 [n][cols]; when given, each run quantizes it into x_q8 first).
+    """
+
+    def __init__(self, mats, n: int):
+        self.n = n
+        self._keep = list(mats)            # keep tensors alive as long as the plan
+        arr = (_Mat * max(1, len(mats)))()
+        for i, m in enumerate(mats):
+            x = m.get("x")
+            arr[i] = _Mat(_dev(m["w_packed"], "w_packed", torch.uint8) if m["w_packed"].numel() else None,
+                          _dev(x, "x", torch.float32) if x is not None else None,
+                          _dev(m["x_q8"], "x_q8", torch.uint8) if m["x_q8"].numel() else None,
+                          _dev(m["y"], "y", torch.float32) if m["y"].numel() else None,
+                          int(m["rows"]), int(m["cols"]))
+        need = ctypes.c_size_t(0)
+        plan = ctypes.c_void_p(None)
+        _check("q4s_sweep_plan_create", lib().q4s_sweep_plan_create(arr, len(mats), n, ctypes.byref(need),
+                                                                     ctypes.byref(plan)))
+        self._plan = plan
+        dev = mats[0]["y"].device if mats else torch.device("cuda")
+        self.dev_mem = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+        _check("q4s_sweep_plan_upload", lib().q4s_sweep_plan_upload(self._plan, self.dev_mem.data_ptr(),
+                                                                     int(need.value), _stream(dev)))
+        torch.cuda.current_stream(dev).synchronize()
+        self.device = dev
+
+    def info(self) -> dict:
+        inf = PlanInfo()
+        _check("q4s_sweep_plan_info", lib().q4s_sweep_plan_info(self._plan, ctypes.byref(inf)))
+        return inf.as_dict()
+
+    def run(self) -> None:
+        _check("q4s_sweep_run", lib().q4s_sweep_run(self._plan, _stream(self.device)))
+
+    def close(self) -> None:
+        if self._plan:
+            lib().q4s_sweep_plan_destroy(self._plan)
+            self._plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ----------------------------------------------------------- measurement
+
+def bench_read(buf: torch.Tensor, loads_in_flight: int = 4, n_blocks: int = 0,
+               sink: torch.Tensor | None = None) -> None:
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check("q4s_bench_read", lib().q4s_bench_read(_dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                                   loads_in_flight, n_blocks, _dev(sink, "sink"),
+                                                   _stream(buf.device)))
+
+
+def bench_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    _check("q4s_bench_copy", lib().q4s_bench_copy(_dev(src, "src"), _dev(dst, "dst"), nbytes,
+                                                   _stream(src.device)))

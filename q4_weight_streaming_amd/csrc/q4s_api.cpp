@@ -1,0 +1,380 @@
+// C ABI of libq4stream (include/q4s.h): argument validation, the sweep plan
+// (tile table), and kernel launches.  Every check runs before any HIP call.
+#include "q4s.h"
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "q4s_internal.h"
+
+using namespace q4s;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+q4s_status fail(q4s_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+// prepend "matrix i: " to the current error text
+q4s_status prefix_matrix(q4s_status s, int i) {
+    char tmp[sizeof g_err];
+    memcpy(tmp, g_err, sizeof tmp);
+    return fail(s, "matrix %d: %s", i, tmp);
+}
+
+q4s_status ok() {
+    g_err[0] = '\0';
+    return Q4S_OK;
+}
+
+q4s_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(Q4S_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+q4s_status check_shape(int64_t rows, int64_t cols, int n) {
+    if (rows < 0 || rows >= kMaxDim) return fail(Q4S_ERR_SHAPE, "rows=%lld out of [0, 2^31)", (long long)rows);
+    if (cols < 0 || cols >= kMaxDim || cols % 32 != 0)
+        return fail(Q4S_ERR_SHAPE, "cols=%lld must be a multiple of 32 in [0, 2^31)", (long long)cols);
+    if (n < 0 || n > Q4S_MAX_N) return fail(Q4S_ERR_SHAPE, "n=%d out of [0, %d]", n, Q4S_MAX_N);
+    return Q4S_OK;
+}
+
+// pointer p naming `bytes` bytes: may be NULL only when bytes == 0; must be a-aligned
+q4s_status check_ptr(const void* p, size_t bytes, uintptr_t a, const char* name) {
+    if (p == nullptr) {
+        if (bytes == 0) return Q4S_OK;
+        return fail(Q4S_ERR_NULL, "%s is NULL", name);
+    }
+    if (!aligned(p, a)) return fail(Q4S_ERR_ALIGN, "%s must be %u-byte aligned", name, (unsigned)a);
+    return Q4S_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+size_t packed_bytes(int64_t rows, int64_t cols) {
+    return (size_t)(groups_of(rows) * chunks_of(cols)) * kChunkBytes;
+}
+size_t q8_bytes(int n, int64_t cols) {
+    const size_t raw = (size_t)n * (size_t)cols / 32 * 34;
+    return (raw + 15) & ~(size_t)15;
+}
+
+MatDesc make_desc(const void* w, const void* xq8, float* y, int64_t rows, int64_t cols, int n) {
+    MatDesc m;
+    m.w = (const uint8_t*)w;
+    m.xq = (const int8_t*)xq8;
+    m.xd = (const uint16_t*)((const uint8_t*)xq8 + (size_t)n * (size_t)cols);
+    m.y = y;
+    m.rows = (int32_t)rows;
+    m.cols = (int32_t)cols;
+    m.nb = (int32_t)(cols / 32);
+    m.G = (int32_t)groups_of(rows);
+    m.C = (int32_t)chunks_of(cols);
+    m.ks = choose_ksplit(m.C);
+    return m;
+}
+
+// validation shared by the GEMV and each sweep matrix
+q4s_status check_gemv(const void* w, const void* xq8, const float* y, int64_t rows, int64_t cols,
+                      int n) {
+    q4s_status s = check_shape(rows, cols, n);
+    if (s) return s;
+    const bool live = rows > 0 && n > 0;
+    const size_t wb = live ? packed_bytes(rows, cols) : 0;
+    const size_t xb = live ? q8_bytes(n, cols) : 0;
+    const size_t yb = live ? (size_t)n * rows * 4 : 0;
+    if ((s = check_ptr(w, wb, 16, "w_packed"))) return s;
+    if ((s = check_ptr(xq8, xb, 16, "x_q8"))) return s;
+    if ((s = check_ptr(y, yb, 4, "y"))) return s;
+    if (overlap(y, yb, w, wb) || overlap(y, yb, xq8, xb))
+        return fail(Q4S_ERR_ALIAS, "y overlaps an input");
+    return Q4S_OK;
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+
+extern "C" {
+
+int q4s_abi_version(void) { return Q4S_ABI_VERSION; }
+
+const char* q4s_status_string(int s) {
+    switch (s) {
+        case Q4S_OK: return "ok";
+        case Q4S_ERR_NULL: return "null pointer";
+        case Q4S_ERR_SHAPE: return "invalid shape";
+        case Q4S_ERR_ALIGN: return "misaligned pointer";
+        case Q4S_ERR_ALIAS: return "output overlaps input";
+        case Q4S_ERR_PLAN: return "invalid plan";
+        case Q4S_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* q4s_last_error(void) { return g_err; }
+
+size_t q4s_q4_0_bytes(int64_t rows, int64_t cols) {
+    if (check_shape(rows, cols, 1) != Q4S_OK) return 0;
+    return (size_t)rows * (size_t)(cols / 32) * 18;
+}
+
+size_t q4s_packed_bytes(int64_t rows, int64_t cols) {
+    if (check_shape(rows, cols, 1) != Q4S_OK) return 0;
+    return packed_bytes(rows, cols);
+}
+
+size_t q4s_q8_bytes(int n, int64_t cols) {
+    if (check_shape(0, cols, n) != Q4S_OK) return 0;
+    return q8_bytes(n, cols);
+}
+
+q4s_status q4s_repack_q4_0(const void* w_q4_0, void* w_packed, int64_t rows, int64_t cols, void* stream) {
+    q4s_status s = check_shape(rows, cols, 1);
+    if (s) return s;
+    const size_t cb = (size_t)rows * (size_t)(cols / 32) * 18;
+    const size_t pb = packed_bytes(rows, cols);
+    if ((s = check_ptr(w_q4_0, cb, 2, "w_q4_0"))) return s;
+    if ((s = check_ptr(w_packed, pb, 16, "w_packed"))) return s;
+    if (overlap(w_q4_0, cb, w_packed, pb)) return fail(Q4S_ERR_ALIAS, "w_packed overlaps w_q4_0");
+    if (pb == 0) return ok();
+    return hip_status(launch_repack((const uint8_t*)w_q4_0, (uint8_t*)w_packed, rows, cols,
+                                    (hipStream_t)stream), "repack launch");
+}
+
+q4s_status q4s_quantize_q8_0(const float* x, void* x_q8, int n, int64_t cols, void* stream) {
+    q4s_status s = check_shape(0, cols, n);
+    if (s) return s;
+    const size_t xb = (size_t)n * (size_t)cols * 4;
+    const size_t qb = (n > 0 && cols > 0) ? q8_bytes(n, cols) : 0;
+    if ((s = check_ptr(x, xb, 4, "x"))) return s;
+    if ((s = check_ptr(x_q8, qb, 16, "x_q8"))) return s;
+    if (overlap(x, xb, x_q8, qb)) return fail(Q4S_ERR_ALIAS, "x_q8 overlaps x");
+    if (qb == 0) return ok();
+    QuantDesc d;
+    d.x = x;
+    d.q = (int8_t*)x_q8;
+    d.d = (uint16_t*)((uint8_t*)x_q8 + (size_t)n * (size_t)cols);
+    d.blk0 = 0;
+    d.n = n;
+    d.cols = (int32_t)cols;
+    return hip_status(launch_quantize(d, (hipStream_t)stream), "quantize launch");
+}
+
+q4s_status q4s_gemv_q4_0(const void* w_packed, const void* x_q8, float* y, int64_t rows, int64_t cols,
+                         int n, void* stream) {
+    q4s_status s = check_gemv(w_packed, x_q8, y, rows, cols, n);
+    if (s) return s;
+    if (rows == 0 || n == 0) return ok();
+    const MatDesc m = make_desc(w_packed, x_q8, y, rows, cols, n);
+    return hip_status(launch_gemv(m, n, gsets_of(m.G, m.ks), (hipStream_t)stream), "gemv launch");
+}
+
+q4s_status q4s_block_sums(const void* w_packed, const void* x_q8, int32_t* sums, int64_t rows,
+                          int64_t cols, int n, void* stream) {
+    q4s_status s = check_shape(rows, cols, n);
+    if (s) return s;
+    const bool live = rows > 0 && n > 0 && cols > 0;
+    const size_t wb = live ? packed_bytes(rows, cols) : 0;
+    const size_t xb = live ? q8_bytes(n, cols) : 0;
+    const size_t sb = live ? (size_t)n * rows * (cols / 32) * 4 : 0;
+    if ((s = check_ptr(w_packed, wb, 16, "w_packed"))) return s;
+    if ((s = check_ptr(x_q8, xb, 16, "x_q8"))) return s;
+    if ((s = check_ptr(sums, sb, 4, "s"))) return s;
+    if (overlap(sums, sb, w_packed, wb) || overlap(sums, sb, x_q8, xb))
+        return fail(Q4S_ERR_ALIAS, "s overlaps an input");
+    if (!live) return ok();
+    const MatDesc m = make_desc(w_packed, x_q8, nullptr, rows, cols, n);
+    return hip_status(launch_block_sums(m, n, sums, (hipStream_t)stream), "block_sums launch");
+}
+
+// ==================================================================== sweep
+
+struct q4s_plan {
+    int n = 0;
+    std::vector<MatDesc> mats;
+    std::vector<uint32_t> tiles;     // (matrix, group set) pairs, largest tiles first
+    std::vector<QuantDesc> quant;    // matrices with an fp32 activation to quantize
+    int64_t quant_blocks = 0;
+    q4s_plan_info info{};
+    // device image: [MatDesc x n_mats][QuantDesc x n_quant][tiles], 16-byte aligned parts
+    size_t off_mats = 0, off_quant = 0, off_tiles = 0, dev_bytes = 0;
+    std::vector<uint8_t> image;
+    uint8_t* dev = nullptr;
+};
+
+q4s_status q4s_sweep_plan_create(const q4s_mat* mats, int n_mats, int n, size_t* dev_bytes_needed,
+                                 q4s_plan** out) {
+    if (!out || !dev_bytes_needed) return fail(Q4S_ERR_NULL, "out and dev_bytes_needed are required");
+    *out = nullptr;
+    if (n < 1 || n > Q4S_MAX_N) return fail(Q4S_ERR_SHAPE, "n=%d out of [1, %d]", n, Q4S_MAX_N);
+    if (n_mats < 0 || (n_mats > 0 && !mats)) return fail(Q4S_ERR_PLAN, "invalid matrix table");
+    q4s_status s;
+    // per-matrix checks, then the hazards between the two phases of a run:
+    // quantize reads x and writes x_q8; the GEMV reads w_packed and x_q8 and writes y
+    struct Region { const void* p; size_t b; };
+    std::vector<Region> xs, q8s, ws, ys;
+    for (int i = 0; i < n_mats; ++i) {
+        const q4s_mat& a = mats[i];
+        if ((s = check_gemv(a.w_packed, a.x_q8, a.y, a.rows, a.cols, n))) return prefix_matrix(s, i);
+        const bool live = a.rows > 0;
+        size_t xb = live && a.cols > 0 ? q8_bytes(n, a.cols) : 0;
+        if (a.x) {
+            // x is quantized into x_q8 even when rows == 0
+            const size_t fb = (size_t)n * a.cols * 4;
+            xb = a.cols > 0 ? q8_bytes(n, a.cols) : 0;
+            if ((s = check_ptr(a.x, fb, 4, "x"))) return prefix_matrix(s, i);
+            if ((s = check_ptr(a.x_q8, xb, 16, "x_q8"))) return prefix_matrix(s, i);
+            xs.push_back({a.x, fb});
+        }
+        q8s.push_back({a.x_q8, xb});
+        ws.push_back({a.w_packed, live ? packed_bytes(a.rows, a.cols) : 0});
+        ys.push_back({a.y, live ? (size_t)n * a.rows * 4 : 0});
+    }
+    auto any_overlap = [](const std::vector<Region>& A, const std::vector<Region>& B) {
+        for (const Region& a : A)
+            for (const Region& b : B)
+                if (overlap(a.p, a.b, b.p, b.b)) return true;
+        return false;
+    };
+    if (any_overlap(q8s, xs)) return fail(Q4S_ERR_ALIAS, "an x_q8 of the sweep overlaps an x");
+    if (any_overlap(ys, ws) || any_overlap(ys, q8s) || any_overlap(ys, xs))
+        return fail(Q4S_ERR_ALIAS, "a y of the sweep overlaps an input");
+
+    q4s_plan* p = new (std::nothrow) q4s_plan;
+    if (!p) return fail(Q4S_ERR_PLAN, "out of host memory");
+    p->n = n;
+    struct Tile { uint32_t mat, gset; int64_t bytes; };
+    std::vector<Tile> tiles;
+    for (int i = 0; i < n_mats; ++i) {
+        const q4s_mat& a = mats[i];
+        MatDesc m = make_desc(a.w_packed, a.x_q8, a.y, a.rows, a.cols, n);
+        p->mats.push_back(m);
+        p->info.weight_bytes += a.rows * (a.cols / 32) * 18;
+        if (a.x && a.cols > 0) {
+            QuantDesc q;
+            q.x = a.x;
+            q.q = (int8_t*)a.x_q8;
+            q.d = (uint16_t*)((uint8_t*)a.x_q8 + (size_t)n * a.cols);
+            q.blk0 = p->quant_blocks;
+            q.n = n;
+            q.cols = (int32_t)a.cols;
+            p->quant.push_back(q);
+            p->quant_blocks += (int64_t)n * (a.cols / 32);
+        }
+        if (a.rows == 0) continue;
+        p->info.packed_bytes += (int64_t)packed_bytes(a.rows, a.cols);
+        p->info.act_bytes += (int64_t)n * a.cols / 32 * 34;
+        p->info.out_bytes += (int64_t)n * a.rows * 4;
+        const int gpw = kWaves / m.ks;
+        const int64_t ng = gsets_of(m.G, m.ks);
+        for (int64_t gs = 0; gs < ng; ++gs) {
+            const int64_t groups = std::min<int64_t>(gpw, m.G - gs * gpw);
+            tiles.push_back({(uint32_t)i, (uint32_t)gs, groups * m.C * kChunkBytes});
+        }
+    }
+    std::stable_sort(tiles.begin(), tiles.end(), [](const Tile& a, const Tile& b) { return a.bytes > b.bytes; });
+    for (const Tile& t : tiles) {
+        p->tiles.push_back(t.mat);
+        p->tiles.push_back(t.gset);
+    }
+    auto up16 = [](size_t v) { return (v + 15) & ~(size_t)15; };
+    p->off_mats = 0;
+    p->off_quant = up16(p->mats.size() * sizeof(MatDesc));
+    p->off_tiles = p->off_quant + up16(p->quant.size() * sizeof(QuantDesc));
+    p->dev_bytes = std::max<size_t>(16, p->off_tiles + up16(p->tiles.size() * sizeof(uint32_t)));
+    p->image.assign(p->dev_bytes, 0);
+    if (!p->mats.empty()) memcpy(p->image.data() + p->off_mats, p->mats.data(), p->mats.size() * sizeof(MatDesc));
+    if (!p->quant.empty()) memcpy(p->image.data() + p->off_quant, p->quant.data(), p->quant.size() * sizeof(QuantDesc));
+    if (!p->tiles.empty()) memcpy(p->image.data() + p->off_tiles, p->tiles.data(), p->tiles.size() * sizeof(uint32_t));
+    p->info.n_mats = n_mats;
+    p->info.n_tiles = (int64_t)tiles.size();
+    p->info.n_quant_blocks = p->quant_blocks;
+    p->info.dev_bytes = (int64_t)p->dev_bytes;
+    *dev_bytes_needed = p->dev_bytes;
+    *out = p;
+    return ok();
+}
+
+q4s_status q4s_sweep_plan_upload(q4s_plan* p, void* dev_mem, size_t dev_bytes, void* stream) {
+    if (!p) return fail(Q4S_ERR_NULL, "plan is NULL");
+    if (!dev_mem) return fail(Q4S_ERR_NULL, "dev_mem is NULL");
+    if (!aligned(dev_mem, 16)) return fail(Q4S_ERR_ALIGN, "dev_mem must be 16-byte aligned");
+    if (dev_bytes < p->dev_bytes)
+        return fail(Q4S_ERR_PLAN, "dev_mem holds %zu bytes, plan needs %zu", dev_bytes, p->dev_bytes);
+    // the quantize descriptors' block offsets and the tables are position independent;
+    // only the base of the image changes
+    hipError_t e = hipMemcpyAsync(dev_mem, p->image.data(), p->dev_bytes, hipMemcpyHostToDevice,
+                                  (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "plan upload");
+    p->dev = (uint8_t*)dev_mem;
+    return ok();
+}
+
+q4s_status q4s_sweep_run(const q4s_plan* p, void* stream) {
+    if (!p) return fail(Q4S_ERR_NULL, "plan is NULL");
+    if (!p->dev) return fail(Q4S_ERR_PLAN, "plan was not uploaded");
+    hipStream_t st = (hipStream_t)stream;
+    if (!p->quant.empty()) {
+        hipError_t e = launch_quantize_batch((const QuantDesc*)(p->dev + p->off_quant), (int)p->quant.size(),
+                                             p->quant_blocks, st);
+        if (e != hipSuccess) return hip_status(e, "sweep quantize launch");
+    }
+    return hip_status(launch_sweep((const MatDesc*)(p->dev + p->off_mats),
+                                   (const uint32_t*)(p->dev + p->off_tiles), (int64_t)p->tiles.size() / 2,
+                                   p->n, st),
+                      "sweep launch");
+}
+
+q4s_status q4s_sweep_plan_info(const q4s_plan* p, q4s_plan_info* info) {
+    if (!p || !info) return fail(Q4S_ERR_NULL, "plan and info are required");
+    *info = p->info;
+    return ok();
+}
+
+void q4s_sweep_plan_destroy(q4s_plan* p) { delete p; }
+
+// ============================================================= measurement
+
+q4s_status q4s_bench_read(const void* buf, size_t bytes, int loads_in_flight, int n_blocks, uint32_t* sink,
+                          void* stream) {
+    if (bytes % 16) return fail(Q4S_ERR_SHAPE, "bytes must be a multiple of 16");
+    if (loads_in_flight != 1 && loads_in_flight != 2 && loads_in_flight != 4 && loads_in_flight != 8)
+        return fail(Q4S_ERR_SHAPE, "loads_in_flight must be 1, 2, 4 or 8");
+    if (n_blocks < 0 || n_blocks > (1 << 20)) return fail(Q4S_ERR_SHAPE, "n_blocks out of range");
+    q4s_status s;
+    if ((s = check_ptr(buf, bytes, 16, "buf"))) return s;
+    if ((s = check_ptr(sink, bytes ? 4 : 0, 4, "sink"))) return s;
+    return hip_status(launch_bench_read(buf, bytes, loads_in_flight, n_blocks, sink, (hipStream_t)stream),
+                      "bench_read launch");
+}
+
+q4s_status q4s_bench_copy(const void* src, void* dst, size_t bytes, void* stream) {
+    if (bytes % 16) return fail(Q4S_ERR_SHAPE, "bytes must be a multiple of 16");
+    q4s_status s;
+    if ((s = check_ptr(src, bytes, 16, "src"))) return s;
+    if ((s = check_ptr(dst, bytes, 16, "dst"))) return s;
+    if (overlap(src, bytes, dst, bytes)) return fail(Q4S_ERR_ALIAS, "dst overlaps src");
+    return hip_status(launch_bench_copy(src, dst, bytes, (hipStream_t)stream), "bench_copy launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Internal declarations shared by the C-ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace q4s {
+
+// Packed Q4_0 geometry.  A 64-row group is one wavefront (lane = row); a chunk
+// is 8 blocks = 256 columns.  Per (group, chunk): 8192 nibble bytes laid out
+// [block][row][16 B] so one wave-wide 16-byte load reads 1 KB contiguous, then
+// 1024 scale bytes [row][8 x binary16] so one 16-byte load per lane fetches the
+// lane's 8 scales.
+constexpr int kGroupRows = 64;
+constexpr int kChunkBlocks = 8;
+constexpr int kBlockNibBytes = 16;
+constexpr int kChunkNibBytes = kChunkBlocks * kGroupRows * kBlockNibBytes;  // 8192
+constexpr int kChunkBytes = kChunkNibBytes + kGroupRows * kChunkBlocks * 2;   // 9216
+constexpr int kWaves = 4;                 // wavefronts per workgroup
+constexpr int kThreads = kWaves * 64;     // workgroup size
+constexpr int kMaxN = 8;                  // activation rows per call
+
+// One matrix as the GEMV kernels see it.  A workgroup tile ("group set") is
+// kWaves / ks row groups; the ks waves of one group split its chunks into ks
+// contiguous ranges [s*C/ks, (s+1)*C/ks) and add their accumulators in split
+// order through LDS.
+struct MatDesc {
+    const uint8_t* w;     // packed Q4_0
+    const int8_t* xq;     // Q8_0 q, int8 [n][cols]
+    const uint16_t* xd;   // Q8_0 d_x, binary16 [n][nb]
+    float* y;             // fp32 [n][rows]
+    int32_t rows, cols;
+    int32_t nb, G, C, ks; // blocks per row, row groups, chunks, K splits (1, 2 or 4)
+};
+
+// One activation of a batched Q8_0 quantization.
+struct QuantDesc {
+    const float* x;       // fp32 [n][cols]
+    int8_t* q;            // [n][cols]
+    uint16_t* d;          // [n][nb]
+    int64_t blk0;         // first global block index of this activation
+    int32_t n, cols;
+};
+
+// K split chosen from the chunk count alone (so every n and every entry point
+// uses the same partition of a given shape).
+inline int choose_ksplit(int64_t C) { return C <= 8 ? 1 : (C <= 16 ? 2 : 4); }
+inline int64_t groups_of(int64_t rows) { return (rows + kGroupRows - 1) / kGroupRows; }
+inline int64_t chunks_of(int64_t cols) { return (cols / 32 + kChunkBlocks - 1) / kChunkBlocks; }
+inline int64_t gsets_of(int64_t G, int ks) {
+    int gpw = kWaves / ks;
+    return (G + gpw - 1) / gpw;
+}
+
+// Kernel launchers (q4s_kernels.hip).  Each returns the launch status.
+hipError_t launch_repack(const uint8_t* w, uint8_t* packed, int64_t rows, int64_t cols,
+                         hipStream_t st);
+hipError_t launch_quantize(const QuantDesc& d, hipStream_t st);
+hipError_t launch_quantize_batch(const QuantDesc* dev_descs, int n_descs, int64_t total_blocks,
+                                 hipStream_t st);
+hipError_t launch_gemv(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st);
+hipError_t launch_sweep(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles,
+                        int n, hipStream_t st);
+hipError_t launch_block_sums(const MatDesc& m, int n, int32_t* s, hipStream_t st);
+hipError_t launch_bench_read(const void* buf, size_t bytes, int lif, int n_blocks,
+                             uint32_t* sink, hipStream_t st);
+hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
+
+}  // namespace q4s

@@ -1,0 +1,124 @@
+"""The C-ABI library: it loads, exports every function include/q4s.h declares,
+and rejects bad arguments before touching the GPU (no device needed here)."""
+import ctypes
+
+import pytest
+
+from q4_weight_streaming_amd import _lib as q
+
+FAKE = 0x7F0000000000  # a 256-byte aligned address that is never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def L():
+    return q.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = q.header_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.q4s_abi_version() == 1
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert q.status_string(s)
+    assert q.status_string(99) == "unknown status"
+
+
+def test_sizes():
+    assert q.q4_0_bytes(151936, 1536) == 131_272_704
+    assert q.packed_bytes(1536, 1536) == 1_327_104          # no padding at config shapes
+    assert q.packed_bytes(151936, 1536) == 131_272_704
+    assert q.packed_bytes(1536, 8960) == 1536 * 280 * 18
+    assert q.packed_bytes(65, 288) == 2 * 2 * 9216         # 2 groups x 2 chunks, padded
+    assert q.packed_bytes(1, 32) == 9216
+    assert q.packed_bytes(0, 1536) == 0 and q.packed_bytes(10, 0) == 0
+    assert q.q8_bytes(1, 1536) == 1632
+    assert q.q8_bytes(8, 8960) == 8 * 8960 * 34 // 32
+    assert q.q8_bytes(1, 32) == 48                         # 34 rounded up to 16
+    assert q.packed_bytes(3, 33) == 0 and q.q8_bytes(9, 32) == 0 and q.q4_0_bytes(-1, 32) == 0
+
+
+def _err(L):
+    return L.q4s_last_error().decode()
+
+
+def test_gemv_validation(L):
+    g = L.q4s_gemv_q4_0
+    assert g(FAKE, FAKE, FAKE + (1 << 30), 64, 33, 1, None) == 2        # cols % 32
+    assert "cols" in _err(L)
+    assert g(FAKE, FAKE, FAKE + (1 << 30), 64, 64, 9, None) == 2        # n > 8
+    assert g(FAKE, FAKE, FAKE + (1 << 30), -1, 64, 1, None) == 2
+    assert g(None, FAKE, FAKE + (1 << 30), 64, 64, 1, None) == 1        # null weights
+    assert g(FAKE + 8, FAKE, FAKE + (1 << 30), 64, 64, 1, None) == 3    # misaligned
+    assert g(FAKE, FAKE + 4, FAKE + (1 << 30), 64, 64, 1, None) == 3
+    assert g(FAKE, FAKE + (1 << 20), FAKE + 64, 64, 64, 1, None) == 4   # y inside w
+    assert "overlap" in _err(L)
+    assert g(None, None, None, 0, 64, 1, None) == 0                     # rows == 0: no-op
+    assert g(None, None, None, 64, 64, 0, None) == 0                    # n == 0: no-op
+    assert _err(L) == ""
+
+
+def test_other_entry_points_validate(L):
+    assert L.q4s_repack_q4_0(FAKE + 1, FAKE + (1 << 30), 64, 64, None) == 3   # 2-byte alignment
+    assert L.q4s_repack_q4_0(FAKE, FAKE, 64, 64, None) == 4                     # in place
+    assert L.q4s_repack_q4_0(None, None, 0, 64, None) == 0
+    assert L.q4s_quantize_q8_0(FAKE, FAKE + 8, 1, 64, None) == 3
+    assert L.q4s_quantize_q8_0(FAKE, FAKE, 1, 64, None) == 4
+    assert L.q4s_quantize_q8_0(None, FAKE, 1, 64, None) == 1
+    assert L.q4s_quantize_q8_0(FAKE, FAKE + (1 << 30), 1, 48, None) == 2
+    assert L.q4s_block_sums(FAKE, FAKE + (1 << 28), FAKE + 2, 64, 64, 1, None) == 3
+    assert L.q4s_bench_read(FAKE, 24, 4, 0, FAKE + (1 << 30), None) == 2
+    assert L.q4s_bench_read(FAKE, 32, 3, 0, FAKE + (1 << 30), None) == 2
+    assert L.q4s_bench_copy(FAKE, FAKE + 16, 64, None) == 4
+    assert L.q4s_sweep_run(None, None) == 1
+
+
+def _plan(L, mats, n):
+    arr = (q._Mat * len(mats))(*[q._Mat(*m) for m in mats])
+    need = ctypes.c_size_t(0)
+    plan = ctypes.c_void_p(None)
+    st = L.q4s_sweep_plan_create(arr, len(mats), n, ctypes.byref(need), ctypes.byref(plan))
+    return st, plan, need.value
+
+
+def test_sweep_plan_host_side(L):
+    from q4_weight_streaming_amd import synth
+    shapes = synth.qwen25_1p5b()
+    mats, base = [], FAKE
+    for s in shapes:                                      # disjoint fake regions per buffer
+        w = base; base += (q.packed_bytes(s.rows, s.cols) + 4095) // 4096 * 4096
+        x = base; base += (q.q8_bytes(1, s.cols) + 4095) // 4096 * 4096
+        y = base; base += (4 * s.rows + 4095) // 4096 * 4096
+        mats.append((w, None, x, y, s.rows, s.cols))
+    st, plan, need = _plan(L, mats, 1)
+    assert st == 0, _err(L)
+    info = q.PlanInfo()
+    assert L.q4s_sweep_plan_info(plan, ctypes.byref(info)) == 0
+    d = info.as_dict()
+    assert d["n_mats"] == 197
+    assert d["weight_bytes"] == 868_257_792 == d["packed_bytes"]
+    # group sets: q,o 6; k,v 1; gate,up 35; down 24 (4-way K split) per layer; lm_head 594
+    assert d["n_tiles"] == 28 * (6 + 1 + 1 + 6 + 35 + 35 + 24) + 594
+    assert d["n_quant_blocks"] == 0 and d["dev_bytes"] == need
+    assert d["out_bytes"] == 4 * sum(s.rows for s in shapes)
+    L.q4s_sweep_plan_destroy(plan)
+    # an output aliasing another matrix's input is rejected
+    bad = list(mats)
+    bad[1] = (mats[1][0], None, mats[1][2], mats[0][0], mats[1][4], mats[1][5])
+    st, plan, _ = _plan(L, bad, 1)
+    assert st == 4 and not plan.value
+    st, plan, _ = _plan(L, mats[:3], 9)
+    assert st == 2
+    st, plan, _ = _plan(L, [(FAKE, None, FAKE + 8, FAKE + (1 << 30), 64, 64)], 1)
+    assert st == 3 and "matrix 0" in _err(L)
+
+
+def test_library_refuses_when_missing(monkeypatch, tmp_path):
+    monkeypatch.setattr(q, "_lib", None)
+    monkeypatch.setattr(q, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        q.lib()

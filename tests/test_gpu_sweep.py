@@ -1,0 +1,142 @@
+"""GPU parity of the layer-stack sweep at the full workload sizes, in the same
+launch configuration the benchmark times (one plan, quantize + GEMV launches).
+
+  * Qwen2.5-1.5B-shaped set (197 matrices, 868 MB), N=1: every output against
+    the oracle; the sweep equals the standalone GEMV bit for bit.
+  * the same set at N=8 (multi-token verify): each row equals the N=1 sweep of
+    that activation bit for bit; sampled outputs against the oracle.
+  * lm_head alone (151936 x 1536): every output against the oracle.
+  * Qwen2.5-7B-shaped set (3.98 GB), N=1 and N=8: sampled outputs per matrix.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import assert_within, dev, packed_weights, require_gpu, to_dev
+from q4_weight_streaming_amd import _lib as q
+from q4_weight_streaming_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _stack(cfg, shapes, n, act_cfg=None, keep_host=True):
+    """Generate, upload and repack a weight stack; returns host weights, device tensors."""
+    host_w, host_x, mats = [], [], []
+    for m, s in enumerate(shapes):
+        w = synth.q4_0_weights(s.rows, s.cols, synth.generator(cfg, m, 0, 0))
+        x = synth.activation(n, s.cols, synth.generator(cfg if act_cfg is None else act_cfg, m, 0, 1))
+        wp = packed_weights(w, s.rows, s.cols)
+        mats.append({"w_packed": wp, "x": to_dev(x),
+                     "x_q8": torch.empty(q.q8_bytes(n, s.cols), dtype=torch.uint8, device=dev()),
+                     "y": torch.empty((n, s.rows), dtype=torch.float32, device=dev()),
+                     "rows": s.rows, "cols": s.cols})
+        if keep_host:
+            host_w.append(w)
+        host_x.append(x)
+    torch.cuda.synchronize()
+    return host_w, host_x, mats
+
+
+@pytest.fixture(scope="module")
+def qwen15():
+    require_gpu()
+    return _stack(1, synth.qwen25_1p5b(), 1)
+
+
+def test_sweep_small_mixed_equals_standalone(oracle):
+    require_gpu()
+    shapes = [synth.MatShape("a", 257, 1536), synth.MatShape("b", 64, 8960), synth.MatShape("c", 1, 32),
+              synth.MatShape("d", 130, 4128), synth.MatShape("e", 0, 64), synth.MatShape("f", 90, 0)]
+    for n in (1, 4, 8):
+        _, hx, mats = _stack(77, shapes, n)
+        sw = q.Sweep(mats, n)
+        sw.run()
+        torch.cuda.synchronize()
+        for m, x in zip(mats, hx):
+            xq = q.quantize_q8_0(to_dev(x))
+            assert torch.equal(xq, m["x_q8"])
+            y = q.gemv_q4_0(m["w_packed"], xq, m["rows"], m["cols"], n)
+            assert torch.equal(y, m["y"])
+        assert (mats[5]["y"] == 0).all()
+
+
+def test_qwen15_n1_full_parity(oracle, qwen15):
+    hw, hx, mats = qwen15
+    sw = q.Sweep(mats, 1)
+    info = sw.info()
+    assert info["weight_bytes"] == 868_257_792
+    for m in mats:
+        m["y"].fill_(float("nan"))
+    sw.run()
+    sw.run()                                    # repeated runs give the same bytes
+    torch.cuda.synchronize()
+    worst = 0.0
+    for i, (w, x, m) in enumerate(zip(hw, hx, mats)):
+        y_ref, S = oracle.gemv(w, oracle.quantize_q8_0(x), m["rows"], m["cols"], 1)
+        worst = max(worst, assert_within(m["y"].cpu().numpy(), y_ref, S, what=f"matrix {i}"))
+    print(f"worst |y - y_ref| / S = {worst:.3e}")
+    # sweep == standalone GEMV, bit for bit
+    for i in (0, 1, 4, 6, 196):
+        m = mats[i]
+        y = q.gemv_q4_0(m["w_packed"], m["x_q8"], m["rows"], m["cols"], 1)
+        assert torch.equal(y, m["y"])
+
+
+def test_qwen15_n8_verify(oracle, qwen15):
+    hw, _, mats1 = qwen15
+    shapes = synth.qwen25_1p5b()
+    n = 8
+    mats8, hx8 = [], []
+    for mi, (s, m1) in enumerate(zip(shapes, mats1)):
+        x = synth.activation(n, s.cols, synth.generator(3, mi, 0, 1))
+        hx8.append(x)
+        mats8.append({"w_packed": m1["w_packed"], "x": to_dev(x),
+                      "x_q8": torch.empty(q.q8_bytes(n, s.cols), dtype=torch.uint8, device=dev()),
+                      "y": torch.empty((n, s.rows), dtype=torch.float32, device=dev()),
+                      "rows": s.rows, "cols": s.cols})
+    q.Sweep(mats8, n).run()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for i in range(0, 197, 3):
+        s = shapes[i]
+        idx = np.unique(np.concatenate([rng.integers(0, s.rows, 48), [0, s.rows - 1]]))
+        y_ref, S = oracle.gemv_rows(hw[i], oracle.quantize_q8_0(hx8[i]), s.cols, n, idx)
+        assert_within(mats8[i]["y"].cpu().numpy()[:, idx], y_ref, S, what=f"matrix {i}")
+    # each row of the 8-row sweep equals the 1-row sweep of that activation
+    for t in (0, 5):
+        mats_t = [{"w_packed": m["w_packed"], "x": m["x"][t:t + 1].contiguous(),
+                   "x_q8": torch.empty(q.q8_bytes(1, m["cols"]), dtype=torch.uint8, device=dev()),
+                   "y": torch.empty((1, m["rows"]), dtype=torch.float32, device=dev()),
+                   "rows": m["rows"], "cols": m["cols"]} for m in mats8]
+        q.Sweep(mats_t, 1).run()
+        torch.cuda.synchronize()
+        for m8, mt in zip(mats8, mats_t):
+            assert torch.equal(m8["y"][t], mt["y"][0])
+
+
+def test_lm_head_full_parity(oracle):
+    require_gpu()
+    rows, cols = 151936, 1536
+    w = synth.q4_0_weights(rows, cols, synth.generator(2, 0, 0, 0))
+    x = synth.activation(1, cols, synth.generator(2, 0, 0, 1), outliers=0)
+    y = q.gemv_q4_0(packed_weights(w, rows, cols), q.quantize_q8_0(to_dev(x)), rows, cols, 1)
+    y_ref, S = oracle.gemv(w, oracle.quantize_q8_0(x), rows, cols, 1)
+    assert_within(y.cpu().numpy(), y_ref, S, what="lm_head")
+
+
+@pytest.mark.parametrize("n", [1, 8])
+def test_qwen7b_sampled_parity(oracle, n):
+    require_gpu()
+    shapes = synth.qwen25_7b()
+    hw, hx, mats = _stack(4, shapes, n)
+    sw = q.Sweep(mats, n)
+    assert sw.info()["weight_bytes"] == 3_977_035_776
+    sw.run()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(n)
+    for i, s in enumerate(shapes):
+        idx = np.unique(np.concatenate([rng.integers(0, s.rows, 32), [0, s.rows - 1]]))
+        y_ref, S = oracle.gemv_rows(hw[i], oracle.quantize_q8_0(hx[i]), s.cols, n, idx)
+        assert_within(mats[i]["y"].cpu().numpy()[:, idx], y_ref, S, what=f"7B matrix {i}")
+    del mats
+    torch.cuda.empty_cache()
