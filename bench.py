@@ -116,23 +116,31 @@ def traffic_from_profile(workload: str, n: int, launch_bytes: int):
 
 
 def cpu_baseline(host, shapes, n: int, budget_s: float):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+    """The CPU oracle, as it stands, on a bounded sample of the same workload: whole
+    passes (quantize + GEMV of every matrix of copy 0) repeated until `budget_s`
+    seconds have been spent, or matrices of one pass if a pass alone exceeds it."""
     from oracle import oracle
     oracle.build(force=False)
     threads = oracle.max_threads()
     t0 = time.perf_counter()
-    done_bytes, done = 0, 0
-    for (w, x), s in zip(host, shapes):
-        xq = oracle.quantize_q8_0(x)
-        oracle.gemv(w, xq, s.rows, s.cols, n)
-        done_bytes += s.q4_bytes
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
+    done_bytes, done, passes = 0, 0, 0
+    while True:
+        for (w, x), s in zip(host, shapes):
+            xq = oracle.quantize_q8_0(x)
+            oracle.gemv(w, xq, s.rows, s.cols, n)
+            done_bytes += s.q4_bytes
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        else:
+            passes += 1
+            if time.perf_counter() - t0 < budget_s:
+                continue
+        break
     dt = time.perf_counter() - t0
     return {"value": round(done_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {len(shapes)} matrices of copy 0 ({done_bytes} Q4_0 bytes), quantize + GEMV, "
-                      f"one pass, {dt:.2f} s"}
+            "sample": f"{done} matrix products ({passes} whole passes over the {len(shapes)} matrices of copy 0, "
+                      f"{done_bytes} Q4_0 bytes), quantize + GEMV, {dt:.1f} s"}
 
 
 def main() -> int:
@@ -144,7 +152,7 @@ def main() -> int:
     ap.add_argument("--n", type=int, default=1, help="activation rows per GEMV (1..8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify-ratio", action="store_true", help="skip the N=8 / N=1 step-cost ratio")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--profile-only", action="store_true",
                     help="run a few GEMV-only sweeps plus a 1 GiB copy, for rocprofv3 counter runs")
     args = ap.parse_args()

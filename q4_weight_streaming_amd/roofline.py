@@ -1,0 +1,68 @@
+"""Achievable HBM read bandwidth on this GPU: the streaming-read microbenchmark.
+
+One launch reads a buffer far larger than the 256 MB Infinity Cache with
+16-byte loads, L loads in flight per thread, over a range of grid sizes; the
+best rate is the practical ceiling the GEMV is compared with (the roofline
+method of the minfer README, milestone M15: one launch over a large buffer,
+several 16-byte loads in flight per thread).  A plain copy is timed as well.
+
+  python -m q4_weight_streaming_amd.roofline [--gib 4] [--reps 5]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gib", type=float, default=4.0)
+    ap.add_argument("--reps", type=int, default=5)
+    args = ap.parse_args()
+
+    import torch
+
+    from q4_weight_streaming_amd import _lib as q
+    dev = torch.device("cuda:0")
+    nbytes = int(args.gib * (1 << 30)) // 16 * 16
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(args.reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    rows = []
+    for lif in (1, 2, 4, 8):
+        for blocks in (256, 512, 1024, 2048, 4096, 8192, 16384):
+            t = timed(lambda: q.bench_read(buf, lif, blocks, sink))
+            rows.append({"loads_in_flight": lif, "workgroups": blocks, "gb_s": round(nbytes / t / 1e9, 1)})
+            print(f"read L={lif} wg={blocks:6d}: {nbytes / t / 1e9:8.1f} GB/s", file=sys.stderr, flush=True)
+    half = nbytes // 2 // 16 * 16
+    src, dst = buf[:half], buf[half:2 * half]
+    t = timed(lambda: q.bench_copy(src, dst))
+    copy = round(2 * half / t / 1e9, 1)
+    print(f"copy: {copy} GB/s (read + write)", file=sys.stderr)
+    best = max(rows, key=lambda r: r["gb_s"])
+    print(json.dumps({"buffer_bytes": nbytes, "best_read": best, "copy_gb_s": copy, "sweep": rows}))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

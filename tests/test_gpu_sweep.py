@@ -54,7 +54,8 @@ def test_sweep_small_mixed_equals_standalone(oracle):
         torch.cuda.synchronize()
         for m, x in zip(mats, hx):
             xq = q.quantize_q8_0(to_dev(x))
-            assert torch.equal(xq, m["x_q8"])
+            used = n * m["cols"] * 34 // 32                  # bytes past this are padding
+            assert torch.equal(xq[:used], m["x_q8"][:used])
             y = q.gemv_q4_0(m["w_packed"], xq, m["rows"], m["cols"], n)
             assert torch.equal(y, m["y"])
         assert (mats[5]["y"] == 0).all()
