@@ -153,6 +153,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify-ratio", action="store_true", help="skip the N=8 / N=1 step-cost ratio")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--verify-n", default="8", help="comma list of row counts for the t(N)/t(1) ratios")
     ap.add_argument("--profile-only", action="store_true",
                     help="run a few GEMV-only sweeps plus a 1 GiB copy, for rocprofv3 counter runs")
     args = ap.parse_args()
@@ -237,22 +238,25 @@ def main() -> int:
     }
 
     if n == 1 and not args.no_verify_ratio:
-        # the same weight copies stepped with 8 activation rows (multi-token verify)
-        n8 = []
-        for c, m in enumerate(copies):
-            mats8 = []
-            for mi, (s, mm) in enumerate(zip(shapes, m)):
-                from q4_weight_streaming_amd import synth
-                x = synth.activation(8, s.cols, synth.generator(3, mi, c, 1))
-                mats8.append({"w_packed": mm["w_packed"], "x": torch.from_numpy(x).to(dev),
-                              "x_q8": torch.empty(q.q8_bytes(8, s.cols), dtype=torch.uint8, device=dev),
-                              "y": torch.empty((8, s.rows), dtype=torch.float32, device=dev),
-                              "rows": s.rows, "cols": s.cols})
-            n8.append(q.Sweep(mats8, 8))
-        ms8 = time_steps([p.run for p in n8], args.steps, args.warmup, stream)
-        out["verify_n8"] = {"ms_per_step": round(ms8, 5), "ratio_to_n1": round(ms8 / ms, 3)}
-        log(f"n=8 step {ms8 * 1e3:.1f} us, ratio {ms8 / ms:.3f}")
-        del n8
+        # the same weight copies stepped with several activation rows (multi-token verify)
+        from q4_weight_streaming_amd import synth
+        verify = {}
+        for nv in sorted({int(v) for v in args.verify_n.split(",") if v}):
+            plans = []
+            for c, m in enumerate(copies):
+                mats_v = []
+                for mi, (s, mm) in enumerate(zip(shapes, m)):
+                    x = synth.activation(nv, s.cols, synth.generator(3, mi, c, 1))
+                    mats_v.append({"w_packed": mm["w_packed"], "x": torch.from_numpy(x).to(dev),
+                                   "x_q8": torch.empty(q.q8_bytes(nv, s.cols), dtype=torch.uint8, device=dev),
+                                   "y": torch.empty((nv, s.rows), dtype=torch.float32, device=dev),
+                                   "rows": s.rows, "cols": s.cols})
+                plans.append(q.Sweep(mats_v, nv))
+            msv = time_steps([p.run for p in plans], args.steps, args.warmup, stream)
+            verify[f"n{nv}"] = {"ms_per_step": round(msv, 5), "ratio_to_n1": round(msv / ms, 3)}
+            log(f"n={nv} step {msv * 1e3:.1f} us, ratio {msv / ms:.3f}")
+            del plans
+        out["verify"] = verify
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(host0, shapes, n, args.cpu_budget)

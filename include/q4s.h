@@ -47,10 +47,12 @@
  *                           hold (nibble - 8) in 4-bit two's complement;
  *       bytes [8192, 9216): scales, [64 rows][8 blocks] binary16 d_w.
  *     Padding rows and blocks hold zero bytes (weight 0, scale 0).
- *   Q8_0 activation (planar): for n rows of cols values,
+ *   Q8_0 activation (planar): for n rows of cols values, with
+ *   D = cols/32 rounded up to a multiple of 8,
  *       bytes [0, n*cols)             : q, int8 [n][cols];
- *       bytes [n*cols, n*cols*34/32)  : d_x, binary16 [n][cols/32];
- *     the buffer is q4s_q8_bytes(n, cols) long (rounded up to 16 bytes).
+ *       bytes [n*cols, n*cols + 2*n*D): d_x, binary16 [n][D] (entries past
+ *                                       cols/32 are padding, never read);
+ *     at cols % 256 == 0 this is the dense n*cols*34/32 bytes.
  *     Per 32-block: d = max|x| / 127 (fp32, correctly rounded); q =
  *     round-half-away-from-zero(x / d) with the fp32 d as divisor; stored
  *     d_x = binary16(d) (round to nearest even, subnormals kept).  An
@@ -110,8 +112,9 @@ size_t q4s_q4_0_bytes(int64_t rows, int64_t cols);
 /* Packed Q4_0 bytes: ceil(rows/64) * ceil(cols/256) * 9216.  0 if invalid. */
 size_t q4s_packed_bytes(int64_t rows, int64_t cols);
 
-/* Planar Q8_0 bytes for n rows: n * cols * 34 / 32 rounded up to a multiple of
- * 16 (the GEMV reads scales as whole dwords).  0 if invalid. */
+/* Planar Q8_0 bytes for n rows: n*cols + 2*n*D, D = ceil(cols/256)*8 (the d_x
+ * rows are padded to 8 entries so every 8-block chunk of scales is one aligned
+ * 16-byte load).  0 if invalid. */
 size_t q4s_q8_bytes(int n, int64_t cols);
 
 /* ----------------------------------------------------------- operations */

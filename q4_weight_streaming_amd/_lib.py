@@ -150,8 +150,9 @@ def quantize_q8_0(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Ten
 
 def q8_views(x_q8: torch.Tensor, n: int, cols: int):
     """Views of a planar Q8_0 buffer: (q int8 [n][cols], d binary16 bits int16 [n][cols/32])."""
+    stride = (cols // 32 + 7) // 8 * 8
     q = x_q8[: n * cols].view(torch.int8).view(n, cols)
-    d = x_q8[n * cols: n * cols + n * cols // 16].view(torch.int16).view(n, cols // 32)
+    d = x_q8[n * cols: n * cols + 2 * n * stride].view(torch.int16).view(n, stride)[:, : cols // 32]
     return q, d
 
 

@@ -22,6 +22,7 @@ HIP_FLAGS = [
     "-fPIC",
     "-ffp-contract=off",                                   # one fixed fp32 expression per block
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",  # no v_pk_*_f32
+    "-mllvm", "-amdgpu-mfma-vgpr-form",                    # MFMA results in VGPRs, no accvgpr reads
     "-Wall",
 ]
 

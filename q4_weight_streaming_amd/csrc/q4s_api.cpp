@@ -73,9 +73,9 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 size_t packed_bytes(int64_t rows, int64_t cols) {
     return (size_t)(groups_of(rows) * chunks_of(cols)) * kChunkBytes;
 }
+// planar Q8_0: q [n][cols], then d_x [n][dstride] (rows padded to 8 entries)
 size_t q8_bytes(int n, int64_t cols) {
-    const size_t raw = (size_t)n * (size_t)cols / 32 * 34;
-    return (raw + 15) & ~(size_t)15;
+    return (size_t)n * (size_t)cols + (size_t)n * (size_t)dstride_of(cols) * 2;
 }
 
 MatDesc make_desc(const void* w, const void* xq8, float* y, int64_t rows, int64_t cols, int n) {
@@ -90,6 +90,8 @@ MatDesc make_desc(const void* w, const void* xq8, float* y, int64_t rows, int64_
     m.G = (int32_t)groups_of(rows);
     m.C = (int32_t)chunks_of(cols);
     m.ks = choose_ksplit(m.C);
+    m.dstride = (int32_t)dstride_of(cols);
+    m.pad_ = 0;
     return m;
 }
 
@@ -177,6 +179,8 @@ q4s_status q4s_quantize_q8_0(const float* x, void* x_q8, int n, int64_t cols, vo
     d.blk0 = 0;
     d.n = n;
     d.cols = (int32_t)cols;
+    d.dstride = (int32_t)dstride_of(cols);
+    d.pad_ = 0;
     return hip_status(launch_quantize(d, (hipStream_t)stream), "quantize launch");
 }
 
@@ -214,10 +218,11 @@ struct q4s_plan {
     std::vector<MatDesc> mats;
     std::vector<uint32_t> tiles;     // (matrix, group set) pairs, largest tiles first
     std::vector<QuantDesc> quant;    // matrices with an fp32 activation to quantize
+    std::vector<uint32_t> qtiles;    // (activation, first block) pairs, kQuantTileBlocks blocks each
     int64_t quant_blocks = 0;
     q4s_plan_info info{};
-    // device image: [MatDesc x n_mats][QuantDesc x n_quant][tiles], 16-byte aligned parts
-    size_t off_mats = 0, off_quant = 0, off_tiles = 0, dev_bytes = 0;
+    // device image: [MatDesc x n_mats][QuantDesc x n_quant][tiles][quantize tiles], 16-byte aligned parts
+    size_t off_mats = 0, off_quant = 0, off_tiles = 0, off_qtiles = 0, dev_bytes = 0;
     std::vector<uint8_t> image;
     uint8_t* dev = nullptr;
 };
@@ -278,8 +283,15 @@ q4s_status q4s_sweep_plan_create(const q4s_mat* mats, int n_mats, int n, size_t*
             q.blk0 = p->quant_blocks;
             q.n = n;
             q.cols = (int32_t)a.cols;
+            q.dstride = (int32_t)dstride_of(a.cols);
+            q.pad_ = 0;
+            const int64_t nblk = (int64_t)n * (a.cols / 32);
+            for (int64_t b = 0; b < nblk; b += kQuantTileBlocks) {
+                p->qtiles.push_back((uint32_t)p->quant.size());
+                p->qtiles.push_back((uint32_t)b);
+            }
             p->quant.push_back(q);
-            p->quant_blocks += (int64_t)n * (a.cols / 32);
+            p->quant_blocks += nblk;
         }
         if (a.rows == 0) continue;
         p->info.packed_bytes += (int64_t)packed_bytes(a.rows, a.cols);
@@ -301,11 +313,14 @@ q4s_status q4s_sweep_plan_create(const q4s_mat* mats, int n_mats, int n, size_t*
     p->off_mats = 0;
     p->off_quant = up16(p->mats.size() * sizeof(MatDesc));
     p->off_tiles = p->off_quant + up16(p->quant.size() * sizeof(QuantDesc));
-    p->dev_bytes = std::max<size_t>(16, p->off_tiles + up16(p->tiles.size() * sizeof(uint32_t)));
+    p->off_qtiles = p->off_tiles + up16(p->tiles.size() * sizeof(uint32_t));
+    p->dev_bytes = std::max<size_t>(16, p->off_qtiles + up16(p->qtiles.size() * sizeof(uint32_t)));
     p->image.assign(p->dev_bytes, 0);
     if (!p->mats.empty()) memcpy(p->image.data() + p->off_mats, p->mats.data(), p->mats.size() * sizeof(MatDesc));
     if (!p->quant.empty()) memcpy(p->image.data() + p->off_quant, p->quant.data(), p->quant.size() * sizeof(QuantDesc));
     if (!p->tiles.empty()) memcpy(p->image.data() + p->off_tiles, p->tiles.data(), p->tiles.size() * sizeof(uint32_t));
+    if (!p->qtiles.empty())
+        memcpy(p->image.data() + p->off_qtiles, p->qtiles.data(), p->qtiles.size() * sizeof(uint32_t));
     p->info.n_mats = n_mats;
     p->info.n_tiles = (int64_t)tiles.size();
     p->info.n_quant_blocks = p->quant_blocks;
@@ -335,8 +350,9 @@ q4s_status q4s_sweep_run(const q4s_plan* p, void* stream) {
     if (!p->dev) return fail(Q4S_ERR_PLAN, "plan was not uploaded");
     hipStream_t st = (hipStream_t)stream;
     if (!p->quant.empty()) {
-        hipError_t e = launch_quantize_batch((const QuantDesc*)(p->dev + p->off_quant), (int)p->quant.size(),
-                                             p->quant_blocks, st);
+        hipError_t e = launch_quantize_batch((const QuantDesc*)(p->dev + p->off_quant),
+                                             (const uint32_t*)(p->dev + p->off_qtiles),
+                                             (int64_t)p->qtiles.size() / 2, st);
         if (e != hipSuccess) return hip_status(e, "sweep quantize launch");
     }
     return hip_status(launch_sweep((const MatDesc*)(p->dev + p->off_mats),

@@ -29,24 +29,29 @@ constexpr int kMaxN = 8;                  // activation rows per call
 struct MatDesc {
     const uint8_t* w;     // packed Q4_0
     const int8_t* xq;     // Q8_0 q, int8 [n][cols]
-    const uint16_t* xd;   // Q8_0 d_x, binary16 [n][nb]
+    const uint16_t* xd;   // Q8_0 d_x, binary16 [n][dstride]
     float* y;             // fp32 [n][rows]
     int32_t rows, cols;
     int32_t nb, G, C, ks; // blocks per row, row groups, chunks, K splits (1, 2 or 4)
+    int32_t dstride;      // d_x row stride: nb rounded up to a multiple of 8
+    int32_t pad_;
 };
 
 // One activation of a batched Q8_0 quantization.
 struct QuantDesc {
     const float* x;       // fp32 [n][cols]
     int8_t* q;            // [n][cols]
-    uint16_t* d;          // [n][nb]
+    uint16_t* d;          // [n][dstride]
     int64_t blk0;         // first global block index of this activation
     int32_t n, cols;
+    int32_t dstride;      // nb rounded up to a multiple of 8
+    int32_t pad_;
 };
 
 // K split chosen from the chunk count alone (so every n and every entry point
 // uses the same partition of a given shape).
 inline int choose_ksplit(int64_t C) { return C <= 8 ? 1 : (C <= 16 ? 2 : 4); }
+inline int64_t dstride_of(int64_t cols) { return (cols / 32 + 7) / 8 * 8; }
 inline int64_t groups_of(int64_t rows) { return (rows + kGroupRows - 1) / kGroupRows; }
 inline int64_t chunks_of(int64_t cols) { return (cols / 32 + kChunkBlocks - 1) / kChunkBlocks; }
 inline int64_t gsets_of(int64_t G, int ks) {
@@ -58,7 +63,8 @@ inline int64_t gsets_of(int64_t G, int ks) {
 hipError_t launch_repack(const uint8_t* w, uint8_t* packed, int64_t rows, int64_t cols,
                          hipStream_t st);
 hipError_t launch_quantize(const QuantDesc& d, hipStream_t st);
-hipError_t launch_quantize_batch(const QuantDesc* dev_descs, int n_descs, int64_t total_blocks,
+constexpr int kQuantTileBlocks = 32;   // Q8_0 blocks per workgroup of the batched quantizer
+hipError_t launch_quantize_batch(const QuantDesc* dev_descs, const uint32_t* dev_tiles, int64_t n_tiles,
                                  hipStream_t st);
 hipError_t launch_gemv(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st);
 hipError_t launch_sweep(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles,

@@ -32,6 +32,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef u32x8 u32x8_a4 __attribute__((aligned(4)));
 #define Q4S_CONST __attribute__((address_space(4)))
+#define Q4S_GLOBAL __attribute__((address_space(1)))
+
+// Pointers taken from a descriptor table are generic to the compiler; casting
+// them to the global address space keeps the streaming loads global_load_*
+// (a flat load would also count against the scalar-load wait counter).
+template <class T>
+__device__ __forceinline__ const Q4S_GLOBAL T* gp(const void* p) { return (const Q4S_GLOBAL T*)p; }
+template <class T>
+__device__ __forceinline__ Q4S_GLOBAL T* gwr(void* p) { return (Q4S_GLOBAL T*)p; }
 
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -47,8 +56,8 @@ struct Chunk {
 __device__ __forceinline__ void load_chunk(Chunk& ch, const uint8_t* p) {
 #pragma unroll
     for (int b = 0; b < kChunkBlocks; ++b)
-        ch.nib[b] = __builtin_nontemporal_load((const u32x4*)(p + b * (kGroupRows * kBlockNibBytes)));
-    ch.scale = __builtin_nontemporal_load((const u32x4*)(p + kChunkNibBytes));
+        ch.nib[b] = __builtin_nontemporal_load(gp<u32x4>(p + b * (kGroupRows * kBlockNibBytes)));
+    ch.scale = __builtin_nontemporal_load(gp<u32x4>(p + kChunkNibBytes));
 }
 
 // 32 int8 activation values of one block, wave-uniform -> SGPRs.
@@ -56,8 +65,8 @@ __device__ __forceinline__ u32x8 act_q(const int8_t* xq, int64_t off) {
     return *(const Q4S_CONST u32x8_a4*)(xq + off);
 }
 
-// binary16 activation scale idx, wave-uniform (dword scalar load; the Q8_0
-// buffer size is rounded up to 16 bytes so the containing dword is in bounds).
+// binary16 activation scale idx, wave-uniform (dword scalar load; d_x rows are
+// padded to a multiple of 8 entries, so the containing dword is in bounds).
 __device__ __forceinline__ float act_d(const uint16_t* xd, int64_t idx) {
     const uint32_t v = *(const Q4S_CONST uint32_t*)(xd + (idx & ~(int64_t)1));
     const uint16_t h = (idx & 1) ? (uint16_t)(v >> 16) : (uint16_t)(v & 0xffffu);
@@ -103,11 +112,14 @@ __device__ __forceinline__ int block_dot16(const Unpacked& u, const u32x8& q) {
 // Adds chunk `c` (held in ch) of the lane's row into acc[0..N).  The per-block
 // term is fmaf(d_w/16 * d_x, (float)(16 s), part): the product of the two
 // scales is exact, so this equals fmaf(d_w * d_x, (float)s, part) bit for bit.
+// Within a chunk blocks 0-3 and blocks 4-7 form two chains that are added at
+// the end; the MFMA path (two blocks per instruction) forms exactly the same
+// chains.
 template <int N>
 __device__ __forceinline__ void chunk_fma(const MatDesc& m, int c, const Chunk& ch, float (&acc)[N]) {
-    float part[N];
+    float pe[N], po[N];
 #pragma unroll
-    for (int t = 0; t < N; ++t) part[t] = 0.0f;
+    for (int t = 0; t < N; ++t) pe[t] = po[t] = 0.0f;
 #pragma unroll
     for (int b = 0; b < kChunkBlocks; ++b) {
         // padding blocks of the last chunk have zero nibbles and scale; read a
@@ -120,12 +132,13 @@ __device__ __forceinline__ void chunk_fma(const MatDesc& m, int c, const Chunk& 
         for (int t = 0; t < N; ++t) {
             const u32x8 q = act_q(m.xq, (int64_t)t * m.cols + (int64_t)blk * 32);
             const int s16 = block_dot16(u, q);
-            const float dx = act_d(m.xd, (int64_t)t * m.nb + blk);
-            part[t] = fmaf(dw16 * dx, (float)s16, part[t]);
+            const float dx = act_d(m.xd, (int64_t)t * m.dstride + blk);
+            float& p = (b < kChunkBlocks / 2) ? pe[t] : po[t];
+            p = fmaf(dw16 * dx, (float)s16, p);
         }
     }
 #pragma unroll
-    for (int t = 0; t < N; ++t) acc[t] += part[t];
+    for (int t = 0; t < N; ++t) acc[t] += pe[t] + po[t];
 }
 
 // One wave streams chunks [c0, c1) of row group g; lane = row.  Two chunks are
@@ -151,6 +164,195 @@ __device__ __forceinline__ void wave_task(const MatDesc& m, int g, int c0, int c
     }
 }
 
+// ---------------------------------------------------------------- MFMA path (n >= 2)
+//
+// For 2..8 activation rows the per-block dots run on the matrix cores with
+// v_mfma_i32_16x16x64_i8, two Q4_0 blocks per instruction (blocks p and p+4
+// of a chunk, p = 0..3): D = A x B with
+//   A (16 x 64): rows 0-7 = token slots 0-7 of block p, rows 8-15 = token
+//      slots 0-7 of block p+4; a row is non-zero only in its block's K half
+//      (lane groups 0-1 carry block p, lane groups 2-3 block p+4);
+//   B (64 x 16): 16 rows of the wave's 64-row group, K half 0 = block p,
+//      K half 1 = block p+4;
+// so D[slot][row] for slots 0-7 is block p's exact integer sum and slots 8-15
+// block p+4's.  In D, lane (lg, j) = (lane/16, lane%16) holds row j and slots
+// 4*lg + r: lanes 0-31 accumulate blocks 0-3 of a chunk, lanes 32-63 blocks
+// 4-7, and the two chains are added at the end of the chunk, exactly as in
+// the 1-row path, so each row's result is bit-identical to the 1-row call.
+// Token slots >= n read a valid activation row and are never stored.
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 4x4 dword transpose across the four 16-lane groups: on entry lane (m, j)
+// holds v[0..3]; on exit lane (g, j) holds in v[m] what lane (m, j) held in v[g].
+__device__ __forceinline__ void xpose4x4(uint32_t (&v)[4]) {
+    auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+    v[0] = a[0];
+    v[2] = a[1];
+    auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+    v[1] = b[0];
+    v[3] = b[1];
+    auto c = __builtin_amdgcn_permlane16_swap(v[0], v[1], false, false);
+    v[0] = c[0];
+    v[1] = c[1];
+    auto d = __builtin_amdgcn_permlane16_swap(v[2], v[3], false, false);
+    v[2] = d[0];
+    v[3] = d[1];
+}
+
+// Per-lane activation data of one chunk.  a[p]: the A operand of block pair
+// (p, p+4): 16 bytes, q[8k..8k+7] and q[16+8k..16+8k+7] (k = lg & 1) of the
+// lane's token and block, or zero where the lane's row lies outside its K
+// half; dx[r]: the binary16 scales of token slot 4*(lg&1) + r for the four
+// blocks 4*(lg>>1) .. 4*(lg>>1)+3 of the chunk that the lane accumulates.
+struct ActChunk {
+    u32x4 a[kChunkBlocks / 2];
+    u32x2 dx[4];
+};
+
+template <int N>
+__device__ __forceinline__ void load_act(ActChunk& a, const MatDesc& m, int c) {
+    const int lane = threadIdx.x & 63;
+    const int lg = lane >> 4, i = lane & 15;
+    const int h = lg >> 1;
+    const bool active = h == (i >> 3);
+    const uint8_t* xa = (const uint8_t*)m.xq + (int64_t)min(i & 7, N - 1) * m.cols + 8 * (lg & 1);
+#pragma unroll
+    for (int p = 0; p < kChunkBlocks / 2; ++p) {
+        const int blk = min(c * kChunkBlocks + p + 4 * h, m.nb - 1);
+        const u32x2 lo = *gp<u32x2>(xa + (int64_t)blk * 32);
+        const u32x2 hi = *gp<u32x2>(xa + (int64_t)blk * 32 + 16);
+        const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        a.a[p] = active ? v : z;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = min(4 * (lg & 1) + r, N - 1);
+        // d_x rows are padded to a multiple of 8 entries (zero past the last
+        // block), so this aligned 8-byte load stays inside row t
+        a.dx[r] = *gp<u32x2>(m.xd + (int64_t)t * m.dstride + c * kChunkBlocks + 4 * h);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void chunk_mfma(Chunk& ch, const ActChunk& a, float (&acc)[16], u32x4* lds_sc) {
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15, h = lane >> 5;
+    // the scales of rows 16*mt + j for the lane's four blocks, exchanged
+    // through the wave's own LDS slot
+    lds_sc[lane] = ch.scale;
+    u32x2 sc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) sc[mt] = *((const u32x2*)&lds_sc[16 * mt + j] + h);
+    float part[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) part[k] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kChunkBlocks / 2; ++p) {
+        // B operands: lane (g, j) gets dwords 2(g&1), 2(g&1)+1 of block p + 4(g>>1)
+        // of row 16*mt + j, for the 4 row tiles mt
+        uint32_t e[4] = {ch.nib[p][0], ch.nib[p][2], ch.nib[p + 4][0], ch.nib[p + 4][2]};
+        uint32_t o[4] = {ch.nib[p][1], ch.nib[p][3], ch.nib[p + 4][1], ch.nib[p + 4][3]};
+        xpose4x4(e);
+        xpose4x4(o);
+        const i32x4 aop = (i32x4)a.a[p];
+        const i32x4 zero = {0, 0, 0, 0};
+        i32x4 d[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const i32x4 bop = {(int)((e[mt] << 4) & 0xF0F0F0F0u), (int)((o[mt] << 4) & 0xF0F0F0F0u),
+                               (int)(e[mt] & 0xF0F0F0F0u), (int)(o[mt] & 0xF0F0F0F0u)};
+            d[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop, bop, zero, 0, 0, 0);
+        }
+        float dx16[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dx16[r] = ((p & 1) ? half_hi(a.dx[r][p >> 1]) : half_lo(a.dx[r][p >> 1])) * 0.0625f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const float dw = (p & 1) ? half_hi(sc[mt][p >> 1]) : half_lo(sc[mt][p >> 1]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                part[mt * 4 + r] = fmaf(dw * dx16[r], (float)d[mt][r], part[mt * 4 + r]);
+        }
+    }
+    // chains of blocks 0-3 live in lanes 0-31, of blocks 4-7 in lanes 32-63
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[k]), __float_as_uint(part[k]), false, false);
+        acc[k] += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+}
+
+// acc[mt*4 + r] = y[token 4*(lg&1) + r][row g*64 + 16*mt + j]
+template <int N>
+__device__ __forceinline__ void wave_task_mfma(const MatDesc& m, int g, int c0, int c1, float (&acc)[16],
+                                               u32x4* lds_sc) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
+    if (g >= m.G || c0 >= c1) return;
+    const uint8_t* wp = m.w + ((size_t)g * m.C + c0) * kChunkBytes + lane * kBlockNibBytes;
+    Chunk wa, wb;
+    ActChunk aa, ab;
+    load_chunk(wa, wp);
+    load_act<N>(aa, m, c0);
+    for (int c = c0; c < c1; c += 2) {
+        const bool has_b = c + 1 < c1;
+        if (has_b) {
+            load_chunk(wb, wp + kChunkBytes);
+            load_act<N>(ab, m, c + 1);
+        }
+        chunk_mfma<N>(wa, aa, acc, lds_sc);
+        if (!has_b) break;
+        if (c + 2 < c1) {
+            load_chunk(wa, wp + 2 * kChunkBytes);
+            load_act<N>(aa, m, c + 2);
+        }
+        chunk_mfma<N>(wb, ab, acc, lds_sc);
+        wp += 2 * kChunkBytes;
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void run_tile_mfma(const MatDesc& m, int64_t gset, float* red, u32x4* lds_sc) {
+    const int wave = wave_uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int lg = lane >> 4, j = lane & 15;
+    const int ks = m.ks;
+    const int gpw = kWaves / ks;
+    const int64_t g = gset * gpw + wave / ks;
+    const int s = wave % ks;
+    const int c0 = (int)((int64_t)s * m.C / ks);
+    const int c1 = (int)((int64_t)(s + 1) * m.C / ks);
+    float acc[16];
+    wave_task_mfma<N>(m, (int)g, c0, c1, acc, lds_sc + wave * 64);
+    if (ks > 1) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) red[(wave * 16 + k) * 64 + lane] = acc[k];
+        __syncthreads();
+        if (s != 0) return;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            float v = red[(wave * 16 + k) * 64 + lane];
+            for (int q = 1; q < ks; ++q) v += red[((wave + q) * 16 + k) * 64 + lane];
+            acc[k] = v;
+        }
+    }
+    if (g >= m.G || lg >= 2) return;  // lanes 32-63 hold the same sums as lanes 0-31
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int64_t row = g * kGroupRows + 16 * mt + j;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tok = 4 * lg + r;
+            if (tok < N && row < m.rows) gwr<float>(m.y)[(int64_t)tok * m.rows + row] = acc[mt * 4 + r];
+        }
+    }
+}
+
 // One workgroup tile: kWaves / ks row groups, ks waves per group.
 template <int N>
 __device__ __forceinline__ void run_tile(const MatDesc& m, int64_t gset, float* red) {
@@ -168,7 +370,7 @@ __device__ __forceinline__ void run_tile(const MatDesc& m, int64_t gset, float* 
     if (ks == 1) {
         if (g < m.G && row < m.rows) {
 #pragma unroll
-            for (int t = 0; t < N; ++t) m.y[(int64_t)t * m.rows + row] = acc[t];
+            for (int t = 0; t < N; ++t) gwr<float>(m.y)[(int64_t)t * m.rows + row] = acc[t];
         }
         return;
     }
@@ -180,15 +382,31 @@ __device__ __forceinline__ void run_tile(const MatDesc& m, int64_t gset, float* 
         for (int t = 0; t < N; ++t) {
             float v = red[(wave * N + t) * 64 + lane];
             for (int j = 1; j < ks; ++j) v += red[((wave + j) * N + t) * 64 + lane];
-            m.y[(int64_t)t * m.rows + row] = v;
+            gwr<float>(m.y)[(int64_t)t * m.rows + row] = v;
         }
     }
 }
 
+// Per-workgroup LDS of the GEMV kernels: the split reduction buffer and, for
+// the MFMA path, one 1 KB scale-exchange slot per wave.
+template <int N>
+struct TileLds {
+    float red[kWaves * (N == 1 ? 1 : 16) * 64];
+    u32x4 sc[N == 1 ? 1 : kWaves * 64];
+};
+
+template <int N>
+__device__ __forceinline__ void run_any(const MatDesc& m, int64_t gset, TileLds<N>& l) {
+    if constexpr (N == 1)
+        run_tile<1>(m, gset, l.red);
+    else
+        run_tile_mfma<N>(m, gset, l.red, l.sc);
+}
+
 template <int N>
 __global__ __launch_bounds__(kThreads) void k_gemv(MatDesc m) {
-    __shared__ float red[kWaves * N * 64];
-    run_tile<N>(m, blockIdx.x, red);
+    __shared__ TileLds<N> l;
+    run_any<N>(m, blockIdx.x, l);
 }
 
 // The sweep: workgroup i takes tile i = (matrix, group set) of a table sorted
@@ -197,11 +415,11 @@ __global__ __launch_bounds__(kThreads) void k_gemv(MatDesc m) {
 template <int N>
 __global__ __launch_bounds__(kThreads) void k_sweep(const MatDesc* __restrict__ mats,
                                                     const uint32_t* __restrict__ tiles) {
-    __shared__ float red[kWaves * N * 64];
+    __shared__ TileLds<N> l;
     const uint32_t mi = tiles[2 * (size_t)blockIdx.x];
     const uint32_t gs = tiles[2 * (size_t)blockIdx.x + 1];
     const MatDesc m = mats[mi];
-    run_tile<N>(m, gs, red);
+    run_any<N>(m, gs, l);
 }
 
 // Test hook: the exact per-block sums, from the same loads, unpack and dot.
@@ -282,7 +500,10 @@ __device__ __forceinline__ void quant_local(const QuantDesc& qd, int64_t lb) {
     const int64_t t = lb / nb;
     const int64_t b = lb - t * nb;
     const int64_t off = t * qd.cols + b * 32;
-    quant_block(qd.x + off, qd.q + off, qd.d + t * nb + b);
+    quant_block(qd.x + off, qd.q + off, qd.d + t * qd.dstride + b);
+    // the half-wave of a row's last block zeroes the row's padding entries
+    const int l = threadIdx.x & 31;
+    if (b == nb - 1 && l < qd.dstride - nb) qd.d[t * qd.dstride + nb + l] = 0;
 }
 
 __global__ __launch_bounds__(256) void k_quantize(QuantDesc qd, int64_t total_blocks) {
@@ -291,17 +512,19 @@ __global__ __launch_bounds__(256) void k_quantize(QuantDesc qd, int64_t total_bl
     quant_local(qd, gb);
 }
 
-__global__ __launch_bounds__(256) void k_quantize_batch(const QuantDesc* __restrict__ descs, int n_descs,
-                                                        int64_t total_blocks) {
-    const int64_t gb = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 5;
-    if (gb >= total_blocks) return;
-    int lo = 0, hi = n_descs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (descs[mid].blk0 <= gb) lo = mid; else hi = mid - 1;
-    }
-    const QuantDesc qd = descs[lo];
-    quant_local(qd, gb - qd.blk0);
+// Batched quantization for the sweep: workgroup i takes tile i = (activation,
+// first block) of a host-built table and quantizes up to kQuantTileBlocks
+// consecutive blocks of that activation (each 32-lane half-wave takes every
+// 8th block), so no thread searches for its activation.
+__global__ __launch_bounds__(256) void k_quantize_batch(const QuantDesc* __restrict__ descs,
+                                                        const uint32_t* __restrict__ tiles) {
+    const uint32_t di = tiles[2 * (size_t)blockIdx.x];
+    const uint32_t b0 = tiles[2 * (size_t)blockIdx.x + 1];
+    const QuantDesc qd = descs[di];
+    const int64_t total = (int64_t)qd.n * (qd.cols / 32);
+    const int64_t end = min((int64_t)b0 + kQuantTileBlocks, total);
+    for (int64_t lb = (int64_t)b0 + (threadIdx.x >> 5); lb < end; lb += 8)  // uniform per half-wave
+        quant_local(qd, lb);
 }
 
 // ---------------------------------------------------------------- measurement
@@ -352,12 +575,10 @@ hipError_t launch_quantize(const QuantDesc& d, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_batch(const QuantDesc* dev_descs, int n_descs, int64_t total_blocks,
+hipError_t launch_quantize_batch(const QuantDesc* dev_descs, const uint32_t* dev_tiles, int64_t n_tiles,
                                  hipStream_t st) {
-    if (total_blocks == 0 || n_descs == 0) return hipSuccess;
-    const int64_t grid = (total_blocks * 32 + 255) / 256;
-    hipLaunchKernelGGL(k_quantize_batch, dim3((unsigned)grid), dim3(256), 0, st, dev_descs, n_descs,
-                       total_blocks);
+    if (n_tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_quantize_batch, dim3((unsigned)n_tiles), dim3(256), 0, st, dev_descs, dev_tiles);
     return hipGetLastError();
 }
 

@@ -32,8 +32,9 @@ def q8_canonical(x_q8: torch.Tensor, n: int, cols: int) -> np.ndarray:
     """Planar Q8_0 buffer -> canonical 34-byte blocks [n][cols/32][34] (byte moves only)."""
     b = x_q8.cpu().numpy()
     nb = cols // 32
+    stride = (nb + 7) // 8 * 8                                    # d_x rows padded to 8 entries
     qv = b[: n * cols].reshape(n, nb, 32)
-    dv = b[n * cols: n * cols + 2 * n * nb].reshape(n, nb, 2)
+    dv = b[n * cols: n * cols + 2 * n * stride].reshape(n, stride, 2)[:, :nb]
     return np.concatenate([dv, qv], axis=2)
 
 

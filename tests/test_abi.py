@@ -36,9 +36,10 @@ def test_sizes():
     assert q.packed_bytes(65, 288) == 2 * 2 * 9216         # 2 groups x 2 chunks, padded
     assert q.packed_bytes(1, 32) == 9216
     assert q.packed_bytes(0, 1536) == 0 and q.packed_bytes(10, 0) == 0
-    assert q.q8_bytes(1, 1536) == 1632
+    assert q.q8_bytes(1, 1536) == 1632                     # dense Q8_0 at cols % 256 == 0
     assert q.q8_bytes(8, 8960) == 8 * 8960 * 34 // 32
-    assert q.q8_bytes(1, 32) == 48                         # 34 rounded up to 16
+    assert q.q8_bytes(1, 32) == 32 + 16                    # d_x row padded to 8 entries
+    assert q.q8_bytes(3, 288) == 3 * 288 + 3 * 16 * 2
     assert q.packed_bytes(3, 33) == 0 and q.q8_bytes(9, 32) == 0 and q.q4_0_bytes(-1, 32) == 0
 
 
