@@ -109,17 +109,19 @@ __device__ __forceinline__ int block_dot16(const Unpacked& u, const u32x8& q) {
 
 // ---------------------------------------------------------------- GEMV core
 
-// Adds chunk `c` (held in ch) of the lane's row into acc[0..N).  The per-block
-// term is fmaf(d_w/16 * d_x, (float)(16 s), part): the product of the two
-// scales is exact, so this equals fmaf(d_w * d_x, (float)s, part) bit for bit.
-// Within a chunk blocks 0-3 and blocks 4-7 form two chains that are added at
-// the end; the MFMA path (two blocks per instruction) forms exactly the same
-// chains.
+// Summation order shared by every path.  A wave task streams chunks [c0, c1)
+// of one row group.  Within a segment of up to kSegChunks chunks, blocks 0-3
+// of every chunk form chain A and blocks 4-7 chain B, each one fmaf per block
+// in chunk order; at the end of the segment the task accumulator takes
+// acc += (A + B).  The per-block term is fmaf(d_w/16 * d_x, (float)(16 s), .):
+// the product of the two scales is exact, so it equals fmaf(d_w * d_x,
+// (float)s, .) bit for bit.  The MFMA path forms exactly these chains.
+constexpr int kSegChunks = 16;
+
+// Adds chunk `c` (held in ch) of the lane's row into the chains pa / pb.
 template <int N>
-__device__ __forceinline__ void chunk_fma(const MatDesc& m, int c, const Chunk& ch, float (&acc)[N]) {
-    float pe[N], po[N];
-#pragma unroll
-    for (int t = 0; t < N; ++t) pe[t] = po[t] = 0.0f;
+__device__ __forceinline__ void chunk_fma(const MatDesc& m, int c, const Chunk& ch, float (&pa)[N],
+                                          float (&pb)[N]) {
 #pragma unroll
     for (int b = 0; b < kChunkBlocks; ++b) {
         // padding blocks of the last chunk have zero nibbles and scale; read a
@@ -133,12 +135,10 @@ __device__ __forceinline__ void chunk_fma(const MatDesc& m, int c, const Chunk& 
             const u32x8 q = act_q(m.xq, (int64_t)t * m.cols + (int64_t)blk * 32);
             const int s16 = block_dot16(u, q);
             const float dx = act_d(m.xd, (int64_t)t * m.dstride + blk);
-            float& p = (b < kChunkBlocks / 2) ? pe[t] : po[t];
+            float& p = (b < kChunkBlocks / 2) ? pa[t] : pb[t];
             p = fmaf(dw16 * dx, (float)s16, p);
         }
     }
-#pragma unroll
-    for (int t = 0; t < N; ++t) acc[t] += pe[t] + po[t];
 }
 
 // One wave streams chunks [c0, c1) of row group g; lane = row.  Two chunks are
@@ -147,19 +147,31 @@ __device__ __forceinline__ void chunk_fma(const MatDesc& m, int c, const Chunk& 
 template <int N>
 __device__ __forceinline__ void wave_task(const MatDesc& m, int g, int c0, int c1, float (&acc)[N]) {
     const int lane = threadIdx.x & 63;
+    float pa[N], pb[N];
 #pragma unroll
-    for (int t = 0; t < N; ++t) acc[t] = 0.0f;
+    for (int t = 0; t < N; ++t) acc[t] = pa[t] = pb[t] = 0.0f;
     if (g >= m.G || c0 >= c1) return;
     const uint8_t* wp = m.w + ((size_t)g * m.C + c0) * kChunkBytes + lane * kBlockNibBytes;
+    auto seg_end = [&](int c) {  // after chunk c: close the segment if it ends here
+        if (c + 1 == c1 || (c + 1 - c0) % kSegChunks == 0) {
+#pragma unroll
+            for (int t = 0; t < N; ++t) {
+                acc[t] += pa[t] + pb[t];
+                pa[t] = pb[t] = 0.0f;
+            }
+        }
+    };
     Chunk a, b;
     load_chunk(a, wp);
     for (int c = c0; c < c1; c += 2) {
         const bool has_b = c + 1 < c1;
         if (has_b) load_chunk(b, wp + kChunkBytes);
-        chunk_fma<N>(m, c, a, acc);
+        chunk_fma<N>(m, c, a, pa, pb);
+        seg_end(c);
         if (!has_b) break;
         if (c + 2 < c1) load_chunk(a, wp + 2 * kChunkBytes);
-        chunk_fma<N>(m, c + 1, b, acc);
+        chunk_fma<N>(m, c + 1, b, pa, pb);
+        seg_end(c + 1);
         wp += 2 * kChunkBytes;
     }
 }
@@ -176,13 +188,19 @@ __device__ __forceinline__ void wave_task(const MatDesc& m, int g, int c0, int c
 //      K half 1 = block p+4;
 // so D[slot][row] for slots 0-7 is block p's exact integer sum and slots 8-15
 // block p+4's.  In D, lane (lg, j) = (lane/16, lane%16) holds row j and slots
-// 4*lg + r: lanes 0-31 accumulate blocks 0-3 of a chunk, lanes 32-63 blocks
-// 4-7, and the two chains are added at the end of the chunk, exactly as in
-// the 1-row path, so each row's result is bit-identical to the 1-row call.
-// Token slots >= n read a valid activation row and are never stored.
+// 4*lg + r: lanes 0-31 run chain A (blocks 0-3), lanes 32-63 chain B (blocks
+// 4-7), and the chains are combined per segment exactly as in the 1-row path,
+// so each row's result is bit-identical to the 1-row call.  Token slots >= n
+// repeat row n-1 and are never stored.
+//
+// Each chunk's activation is staged through the wave's own LDS slice: two
+// coalesced 16-byte loads per lane bring the 8 tokens x 256 bytes, which are
+// written in A-operand order; the d_x and d_w scales are converted to fp32
+// once per chunk on the way in.
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // 4x4 dword transpose across the four 16-lane groups: on entry lane (m, j)
 // holds v[0..3]; on exit lane (g, j) holds in v[m] what lane (m, j) held in v[g].
@@ -201,54 +219,74 @@ __device__ __forceinline__ void xpose4x4(uint32_t (&v)[4]) {
     v[3] = d[1];
 }
 
-// Per-lane activation data of one chunk.  a[p]: the A operand of block pair
-// (p, p+4): 16 bytes, q[8k..8k+7] and q[16+8k..16+8k+7] (k = lg & 1) of the
-// lane's token and block, or zero where the lane's row lies outside its K
-// half; dx[r]: the binary16 scales of token slot 4*(lg&1) + r for the four
-// blocks 4*(lg>>1) .. 4*(lg>>1)+3 of the chunk that the lane accumulates.
-struct ActChunk {
-    u32x4 a[kChunkBlocks / 2];
-    u32x2 dx[4];
+// A wave's LDS slice.  q: per (token t, block b, K half h) 16 bytes at
+// ((t*8 + b)*2 + h)*16: q[8h..8h+7] then q[16+8h..16+8h+7]; then 16 zero bytes
+// (the A operand of lanes outside their K half).  dx: d_x/16 [token][block]
+// fp32.  dw: d_w [row][block] fp32 of the wave's 64 rows.
+struct WaveLds {
+    u32x4 q[8 * kChunkBlocks * 2 + 1];        // 16-byte slots; the last one stays zero
+    f32x4 dx[8 * kChunkBlocks / 4];
+    f32x4 dw[kGroupRows * kChunkBlocks / 4];
+};
+constexpr int kZeroSlot = 8 * kChunkBlocks * 2;
+
+// The raw activation data of one chunk as loaded: lane (r4, j) holds bytes
+// 16*(j&1) .. +15 of block j>>1 for tokens r4 and 4 + r4 (r4 = lane/16), and
+// the binary16 d_x of token lane/8, block lane%8.
+struct ActRaw {
+    u32x4 q0, q1;
+    uint32_t dxh;
 };
 
 template <int N>
-__device__ __forceinline__ void load_act(ActChunk& a, const MatDesc& m, int c) {
+__device__ __forceinline__ void load_act(ActRaw& a, const MatDesc& m, int c) {
     const int lane = threadIdx.x & 63;
-    const int lg = lane >> 4, i = lane & 15;
-    const int h = lg >> 1;
-    const bool active = h == (i >> 3);
-    const uint8_t* xa = (const uint8_t*)m.xq + (int64_t)min(i & 7, N - 1) * m.cols + 8 * (lg & 1);
+    const int j = lane & 15;
+    const int blk = min(c * kChunkBlocks + (j >> 1), m.nb - 1);  // valid block for padding pieces
+    const int64_t off = (int64_t)blk * 32 + (j & 1) * 16;
+    a.q0 = *gp<u32x4>(m.xq + (int64_t)min(lane >> 4, N - 1) * m.cols + off);
+    a.q1 = *gp<u32x4>(m.xq + (int64_t)min(4 + (lane >> 4), N - 1) * m.cols + off);
+    // d_x rows are padded to a multiple of 8 entries (zero past the last block)
+    a.dxh = *gp<uint16_t>(m.xd + (int64_t)min(lane >> 3, N - 1) * m.dstride + c * kChunkBlocks + (lane & 7));
+}
+
+__device__ __forceinline__ void stage_act(const ActRaw& a, WaveLds& L) {
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15, b = j >> 1, e = j & 1;
 #pragma unroll
-    for (int p = 0; p < kChunkBlocks / 2; ++p) {
-        const int blk = min(c * kChunkBlocks + p + 4 * h, m.nb - 1);
-        const u32x2 lo = *gp<u32x2>(xa + (int64_t)blk * 32);
-        const u32x2 hi = *gp<u32x2>(xa + (int64_t)blk * 32 + 16);
-        const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        a.a[p] = active ? v : z;
+    for (int k = 0; k < 2; ++k) {
+        const int t = (lane >> 4) + 4 * k;
+        const u32x4 v = k ? a.q1 : a.q0;
+        u32x2* s0 = (u32x2*)&L.q[(t * 8 + b) * 2 + 0];
+        u32x2* s1 = (u32x2*)&L.q[(t * 8 + b) * 2 + 1];
+        s0[e] = (u32x2){v[0], v[1]};
+        s1[e] = (u32x2){v[2], v[3]};
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int t = min(4 * (lg & 1) + r, N - 1);
-        // d_x rows are padded to a multiple of 8 entries (zero past the last
-        // block), so this aligned 8-byte load stays inside row t
-        a.dx[r] = *gp<u32x2>(m.xd + (int64_t)t * m.dstride + c * kChunkBlocks + 4 * h);
-    }
+    ((float*)L.dx)[lane] = __half2float(__ushort_as_half((uint16_t)a.dxh)) * 0.0625f;
 }
 
 template <int N>
-__device__ __forceinline__ void chunk_mfma(Chunk& ch, const ActChunk& a, float (&acc)[16], u32x4* lds_sc) {
+__device__ __forceinline__ void chunk_mfma(Chunk& ch, const ActRaw& ar, float (&part)[16], WaveLds& L) {
     const int lane = threadIdx.x & 63;
-    const int j = lane & 15, h = lane >> 5;
-    // the scales of rows 16*mt + j for the lane's four blocks, exchanged
-    // through the wave's own LDS slot
-    lds_sc[lane] = ch.scale;
-    u32x2 sc[4];
+    const int lg = lane >> 4, j = lane & 15, h = lane >> 5;
+    // stage: the activation, and the lane's own row scales as fp32
+    stage_act(ar, L);
+    {
+        f32x4 lo = {half_lo(ch.scale[0]), half_hi(ch.scale[0]), half_lo(ch.scale[1]), half_hi(ch.scale[1])};
+        f32x4 hi = {half_lo(ch.scale[2]), half_hi(ch.scale[2]), half_lo(ch.scale[3]), half_hi(ch.scale[3])};
+        L.dw[2 * lane] = lo;
+        L.dw[2 * lane + 1] = hi;
+    }
+    // the lane's scales: d_w of rows 16*mt + j and d_x/16 of token slots
+    // 4*(lg&1) + r, both for its blocks 4h .. 4h+3
+    f32x4 dw[4], dx[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) sc[mt] = *((const u32x2*)&lds_sc[16 * mt + j] + h);
-    float part[16];
+    for (int mt = 0; mt < 4; ++mt) dw[mt] = L.dw[2 * (16 * mt + j) + h];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) part[k] = 0.0f;
+    for (int r = 0; r < 4; ++r) dx[r] = L.dx[2 * (4 * (lg & 1) + r) + h];
+    const bool active = h == (j >> 3);
+    const int abase = active ? ((j & 7) * 8 + 4 * h) * 2 + (lg & 1) : kZeroSlot;
+    const int astep = active ? 2 : 0;
 #pragma unroll
     for (int p = 0; p < kChunkBlocks / 2; ++p) {
         // B operands: lane (g, j) gets dwords 2(g&1), 2(g&1)+1 of block p + 4(g>>1)
@@ -257,7 +295,7 @@ __device__ __forceinline__ void chunk_mfma(Chunk& ch, const ActChunk& a, float (
         uint32_t o[4] = {ch.nib[p][1], ch.nib[p][3], ch.nib[p + 4][1], ch.nib[p + 4][3]};
         xpose4x4(e);
         xpose4x4(o);
-        const i32x4 aop = (i32x4)a.a[p];
+        const i32x4 aop = (i32x4)L.q[abase + p * astep];
         const i32x4 zero = {0, 0, 0, 0};
         i32x4 d[4];
 #pragma unroll
@@ -266,37 +304,40 @@ __device__ __forceinline__ void chunk_mfma(Chunk& ch, const ActChunk& a, float (
                                (int)(e[mt] & 0xF0F0F0F0u), (int)(o[mt] & 0xF0F0F0F0u)};
             d[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop, bop, zero, 0, 0, 0);
         }
-        float dx16[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            dx16[r] = ((p & 1) ? half_hi(a.dx[r][p >> 1]) : half_lo(a.dx[r][p >> 1])) * 0.0625f;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const float dw = (p & 1) ? half_hi(sc[mt][p >> 1]) : half_lo(sc[mt][p >> 1]);
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                part[mt * 4 + r] = fmaf(dw * dx16[r], (float)d[mt][r], part[mt * 4 + r]);
-        }
-    }
-    // chains of blocks 0-3 live in lanes 0-31, of blocks 4-7 in lanes 32-63
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[k]), __float_as_uint(part[k]), false, false);
-        acc[k] += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                part[mt * 4 + r] = fmaf(dw[mt][p] * dx[r][p], (float)d[mt][r], part[mt * 4 + r]);
     }
 }
 
-// acc[mt*4 + r] = y[token 4*(lg&1) + r][row g*64 + 16*mt + j]
+// acc[mt*4 + r] = y[token 4*(lg&1) + r][row g*64 + 16*mt + j] (lanes 0-31; lanes
+// 32-63 hold the same values)
 template <int N>
 __device__ __forceinline__ void wave_task_mfma(const MatDesc& m, int g, int c0, int c1, float (&acc)[16],
-                                               u32x4* lds_sc) {
+                                               WaveLds& L) {
     const int lane = threadIdx.x & 63;
+    float part[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
+    for (int k = 0; k < 16; ++k) acc[k] = part[k] = 0.0f;
     if (g >= m.G || c0 >= c1) return;
+    if (lane == 0) L.q[kZeroSlot] = (u32x4){0u, 0u, 0u, 0u};
     const uint8_t* wp = m.w + ((size_t)g * m.C + c0) * kChunkBytes + lane * kBlockNibBytes;
+    auto seg_end = [&](int c) {  // after chunk c: close the segment if it ends here
+        if (c + 1 == c1 || (c + 1 - c0) % kSegChunks == 0) {
+            // chain A lives in lanes 0-31, chain B in lanes 32-63
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[k]), __float_as_uint(part[k]),
+                                                           false, false);
+                acc[k] += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                part[k] = 0.0f;
+            }
+        }
+    };
     Chunk wa, wb;
-    ActChunk aa, ab;
+    ActRaw aa, ab;
     load_chunk(wa, wp);
     load_act<N>(aa, m, c0);
     for (int c = c0; c < c1; c += 2) {
@@ -305,19 +346,21 @@ __device__ __forceinline__ void wave_task_mfma(const MatDesc& m, int g, int c0, 
             load_chunk(wb, wp + kChunkBytes);
             load_act<N>(ab, m, c + 1);
         }
-        chunk_mfma<N>(wa, aa, acc, lds_sc);
+        chunk_mfma<N>(wa, aa, part, L);
+        seg_end(c);
         if (!has_b) break;
         if (c + 2 < c1) {
             load_chunk(wa, wp + 2 * kChunkBytes);
             load_act<N>(aa, m, c + 2);
         }
-        chunk_mfma<N>(wb, ab, acc, lds_sc);
+        chunk_mfma<N>(wb, ab, part, L);
+        seg_end(c + 1);
         wp += 2 * kChunkBytes;
     }
 }
 
 template <int N>
-__device__ __forceinline__ void run_tile_mfma(const MatDesc& m, int64_t gset, float* red, u32x4* lds_sc) {
+__device__ __forceinline__ void run_tile_mfma(const MatDesc& m, int64_t gset, float* red, WaveLds* wl) {
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int lg = lane >> 4, j = lane & 15;
@@ -328,7 +371,7 @@ __device__ __forceinline__ void run_tile_mfma(const MatDesc& m, int64_t gset, fl
     const int c0 = (int)((int64_t)s * m.C / ks);
     const int c1 = (int)((int64_t)(s + 1) * m.C / ks);
     float acc[16];
-    wave_task_mfma<N>(m, (int)g, c0, c1, acc, lds_sc + wave * 64);
+    wave_task_mfma<N>(m, (int)g, c0, c1, acc, wl[wave]);
     if (ks > 1) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) red[(wave * 16 + k) * 64 + lane] = acc[k];
@@ -392,7 +435,7 @@ __device__ __forceinline__ void run_tile(const MatDesc& m, int64_t gset, float* 
 template <int N>
 struct TileLds {
     float red[kWaves * (N == 1 ? 1 : 16) * 64];
-    u32x4 sc[N == 1 ? 1 : kWaves * 64];
+    WaveLds wl[N == 1 ? 1 : kWaves];
 };
 
 template <int N>
@@ -400,11 +443,12 @@ __device__ __forceinline__ void run_any(const MatDesc& m, int64_t gset, TileLds<
     if constexpr (N == 1)
         run_tile<1>(m, gset, l.red);
     else
-        run_tile_mfma<N>(m, gset, l.red, l.sc);
+        run_tile_mfma<N>(m, gset, l.red, l.wl);
 }
 
+// The MFMA kernels (n >= 2) are held to 2 waves per SIMD (<= 256 registers).
 template <int N>
-__global__ __launch_bounds__(kThreads) void k_gemv(MatDesc m) {
+__global__ __launch_bounds__(kThreads, N == 1 ? 1 : 2) void k_gemv(MatDesc m) {
     __shared__ TileLds<N> l;
     run_any<N>(m, blockIdx.x, l);
 }
@@ -413,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(MatDesc m) {
 // by tile size, largest first, so the hardware dispatcher's in-order
 // assignment to free slots is a longest-first list schedule.
 template <int N>
-__global__ __launch_bounds__(kThreads) void k_sweep(const MatDesc* __restrict__ mats,
+__global__ __launch_bounds__(kThreads, N == 1 ? 1 : 2) void k_sweep(const MatDesc* __restrict__ mats,
                                                     const uint32_t* __restrict__ tiles) {
     __shared__ TileLds<N> l;
     const uint32_t mi = tiles[2 * (size_t)blockIdx.x];
