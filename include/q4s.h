@@ -131,7 +131,7 @@ q4s_status q4s_repack_q4_0(const void* w_q4_0, void* w_packed, int64_t rows, int
                            void* stream);
 
 /*
- * Q8_0 activation quantization.  x: fp32 [n][cols] (4-byte aligned);
+ * Q8_0 activation quantization.  x: fp32 [n][cols] (16-byte aligned);
  * x_q8: q4s_q8_bytes(n, cols) bytes (16-byte aligned), planar layout above.
  * Source: milestones M3.5 and M15 (int8 activations, quantized once), M14
  * (34-byte Q8_0 blocks).
@@ -161,8 +161,8 @@ q4s_status q4s_block_sums(const void* w_packed, const void* x_q8, int32_t* s, in
 
 /*
  * One matrix of a sweep.  When x is non-NULL, q4s_sweep_run first quantizes
- * x (fp32 [n][cols]) into x_q8; otherwise x_q8 must already hold the planar
- * Q8_0 activation.  y: fp32 [n][rows].
+ * x (fp32 [n][cols], 16-byte aligned) into x_q8; otherwise x_q8 must already
+ * hold the planar Q8_0 activation.  y: fp32 [n][rows].
  */
 typedef struct {
     const void* w_packed;

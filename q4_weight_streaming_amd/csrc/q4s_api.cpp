@@ -168,7 +168,7 @@ q4s_status q4s_quantize_q8_0(const float* x, void* x_q8, int n, int64_t cols, vo
     if (s) return s;
     const size_t xb = (size_t)n * (size_t)cols * 4;
     const size_t qb = (n > 0 && cols > 0) ? q8_bytes(n, cols) : 0;
-    if ((s = check_ptr(x, xb, 4, "x"))) return s;
+    if ((s = check_ptr(x, xb, 16, "x"))) return s;
     if ((s = check_ptr(x_q8, qb, 16, "x_q8"))) return s;
     if (overlap(x, xb, x_q8, qb)) return fail(Q4S_ERR_ALIAS, "x_q8 overlaps x");
     if (qb == 0) return ok();
@@ -247,7 +247,7 @@ q4s_status q4s_sweep_plan_create(const q4s_mat* mats, int n_mats, int n, size_t*
             // x is quantized into x_q8 even when rows == 0
             const size_t fb = (size_t)n * a.cols * 4;
             xb = a.cols > 0 ? q8_bytes(n, a.cols) : 0;
-            if ((s = check_ptr(a.x, fb, 4, "x"))) return prefix_matrix(s, i);
+            if ((s = check_ptr(a.x, fb, 16, "x"))) return prefix_matrix(s, i);
             if ((s = check_ptr(a.x_q8, xb, 16, "x_q8"))) return prefix_matrix(s, i);
             xs.push_back({a.x, fb});
         }

@@ -523,52 +523,57 @@ __global__ __launch_bounds__(256) void k_repack(const uint8_t* __restrict__ w, u
 
 // ---------------------------------------------------------------- quantize
 
-// 32 consecutive lanes quantize one block: d = max|x| / 127 (correctly rounded
-// fp32 division), q = roundf(x / d) (half away from zero), d_x = binary16(d)
-// rounded to nearest even.  All-zero blocks give d = 0, q = 0.
-__device__ __forceinline__ void quant_block(const float* x, int8_t* q, uint16_t* d) {
-    const int l = threadIdx.x & 31;
-    const float v = x[l];
-    float a = fabsf(v);
+// 8 consecutive lanes quantize one block, 4 values each: d = max|x| / 127
+// (correctly rounded fp32 division), q = roundf(x / d) (half away from zero),
+// d_x = binary16(d) rounded to nearest even.  All-zero blocks give d = 0, q = 0.
+// `valid` is uniform over the 8 lanes of a block.
+__device__ __forceinline__ void quant_block8(const float* x, int8_t* q, uint16_t* d, bool valid) {
+    const int o = threadIdx.x & 7;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (valid) v = *gp<f32x4>(x + 4 * o);
+    float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 #pragma unroll
-    for (int off = 16; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 32));
+    for (int off = 1; off < 8; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 8));
+    if (!valid) return;
     const float dd = a / 127.0f;
-    int qi = 0;
-    if (a != 0.0f) qi = (int)roundf(v / dd);
-    q[l] = (int8_t)qi;
-    if (l == 0) *d = __half_as_ushort(__float2half_rn(dd));
+    uint32_t packed = 0;
+    if (a != 0.0f) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) packed |= ((uint32_t)(uint8_t)(int8_t)(int)roundf(v[k] / dd)) << (8 * k);
+    }
+    *gwr<uint32_t>(q + 4 * o) = packed;
+    if (o == 0) *gwr<uint16_t>(d) = __half_as_ushort(__float2half_rn(dd));
 }
 
-__device__ __forceinline__ void quant_local(const QuantDesc& qd, int64_t lb) {
+// Block lb (row-major over [n][nb]) of one activation; the lanes of a row's
+// last block also zero the row's padding entries of d_x.
+__device__ __forceinline__ void quant_local(const QuantDesc& qd, int64_t lb, bool valid) {
     const int nb = qd.cols / 32;
-    const int64_t t = lb / nb;
-    const int64_t b = lb - t * nb;
+    const int64_t t = valid ? lb / nb : 0;
+    const int64_t b = valid ? lb - t * nb : 0;
     const int64_t off = t * qd.cols + b * 32;
-    quant_block(qd.x + off, qd.q + off, qd.d + t * qd.dstride + b);
-    // the half-wave of a row's last block zeroes the row's padding entries
-    const int l = threadIdx.x & 31;
-    if (b == nb - 1 && l < qd.dstride - nb) qd.d[t * qd.dstride + nb + l] = 0;
+    quant_block8(qd.x + off, qd.q + off, qd.d + t * qd.dstride + b, valid);
+    const int o = threadIdx.x & 7;
+    if (valid && b == nb - 1 && o < qd.dstride - nb) gwr<uint16_t>(qd.d)[t * qd.dstride + nb + o] = 0;
 }
 
+// Standalone quantization: 32 blocks per 256-thread workgroup.
 __global__ __launch_bounds__(256) void k_quantize(QuantDesc qd, int64_t total_blocks) {
-    const int64_t gb = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 5;
-    if (gb >= total_blocks) return;  // uniform per 32-lane half
-    quant_local(qd, gb);
+    const int64_t lb = (int64_t)blockIdx.x * kQuantTileBlocks + (threadIdx.x >> 3);
+    quant_local(qd, lb, lb < total_blocks);
 }
 
 // Batched quantization for the sweep: workgroup i takes tile i = (activation,
 // first block) of a host-built table and quantizes up to kQuantTileBlocks
-// consecutive blocks of that activation (each 32-lane half-wave takes every
-// 8th block), so no thread searches for its activation.
+// consecutive blocks of that activation, one block per 8 lanes.
 __global__ __launch_bounds__(256) void k_quantize_batch(const QuantDesc* __restrict__ descs,
                                                         const uint32_t* __restrict__ tiles) {
     const uint32_t di = tiles[2 * (size_t)blockIdx.x];
     const uint32_t b0 = tiles[2 * (size_t)blockIdx.x + 1];
     const QuantDesc qd = descs[di];
     const int64_t total = (int64_t)qd.n * (qd.cols / 32);
-    const int64_t end = min((int64_t)b0 + kQuantTileBlocks, total);
-    for (int64_t lb = (int64_t)b0 + (threadIdx.x >> 5); lb < end; lb += 8)  // uniform per half-wave
-        quant_local(qd, lb);
+    const int64_t lb = (int64_t)b0 + (threadIdx.x >> 3);
+    quant_local(qd, lb, lb < total);
 }
 
 // ---------------------------------------------------------------- measurement
@@ -614,7 +619,7 @@ hipError_t launch_repack(const uint8_t* w, uint8_t* packed, int64_t rows, int64_
 hipError_t launch_quantize(const QuantDesc& d, hipStream_t st) {
     const int64_t total = (int64_t)d.n * (d.cols / 32);
     if (total == 0) return hipSuccess;
-    const int64_t grid = (total * 32 + 255) / 256;
+    const int64_t grid = (total + kQuantTileBlocks - 1) / kQuantTileBlocks;
     hipLaunchKernelGGL(k_quantize, dim3((unsigned)grid), dim3(256), 0, st, d, total);
     return hipGetLastError();
 }

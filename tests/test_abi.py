@@ -70,6 +70,7 @@ def test_other_entry_points_validate(L):
     assert L.q4s_quantize_q8_0(FAKE, FAKE + 8, 1, 64, None) == 3
     assert L.q4s_quantize_q8_0(FAKE, FAKE, 1, 64, None) == 4
     assert L.q4s_quantize_q8_0(None, FAKE, 1, 64, None) == 1
+    assert L.q4s_quantize_q8_0(FAKE + 4, FAKE + (1 << 30), 1, 64, None) == 3   # x needs 16 bytes
     assert L.q4s_quantize_q8_0(FAKE, FAKE + (1 << 30), 1, 48, None) == 2
     assert L.q4s_block_sums(FAKE, FAKE + (1 << 28), FAKE + 2, 64, 64, 1, None) == 3
     assert L.q4s_bench_read(FAKE, 24, 4, 0, FAKE + (1 << 30), None) == 2
