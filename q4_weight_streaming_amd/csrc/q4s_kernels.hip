@@ -161,18 +161,29 @@ __device__ __forceinline__ void wave_task(const MatDesc& m, int g, int c0, int c
             }
         }
     };
+    // The steady-state body prefetches unconditionally so that every path
+    // reaching a chunk's use has the same loads outstanding (a conditional
+    // prefetch makes the compiler wait for all loads, the prefetch included).
     Chunk a, b;
     load_chunk(a, wp);
-    for (int c = c0; c < c1; c += 2) {
-        const bool has_b = c + 1 < c1;
-        if (has_b) load_chunk(b, wp + kChunkBytes);
+    int c = c0;
+    for (; c + 2 < c1; c += 2, wp += 2 * kChunkBytes) {
+        load_chunk(b, wp + kChunkBytes);
         chunk_fma<N>(m, c, a, pa, pb);
         seg_end(c);
-        if (!has_b) break;
-        if (c + 2 < c1) load_chunk(a, wp + 2 * kChunkBytes);
+        load_chunk(a, wp + 2 * kChunkBytes);
         chunk_fma<N>(m, c + 1, b, pa, pb);
         seg_end(c + 1);
-        wp += 2 * kChunkBytes;
+    }
+    if (c + 1 < c1) {  // two chunks left
+        load_chunk(b, wp + kChunkBytes);
+        chunk_fma<N>(m, c, a, pa, pb);
+        seg_end(c);
+        chunk_fma<N>(m, c + 1, b, pa, pb);
+        seg_end(c + 1);
+    } else {           // one chunk left
+        chunk_fma<N>(m, c, a, pa, pb);
+        seg_end(c);
     }
 }
 
@@ -336,26 +347,32 @@ __device__ __forceinline__ void wave_task_mfma(const MatDesc& m, int g, int c0, 
             }
         }
     };
+    // unconditional prefetch in the steady state, as in the 1-row path
     Chunk wa, wb;
     ActRaw aa, ab;
     load_chunk(wa, wp);
     load_act<N>(aa, m, c0);
-    for (int c = c0; c < c1; c += 2) {
-        const bool has_b = c + 1 < c1;
-        if (has_b) {
-            load_chunk(wb, wp + kChunkBytes);
-            load_act<N>(ab, m, c + 1);
-        }
+    int c = c0;
+    for (; c + 2 < c1; c += 2, wp += 2 * kChunkBytes) {
+        load_chunk(wb, wp + kChunkBytes);
+        load_act<N>(ab, m, c + 1);
         chunk_mfma<N>(wa, aa, part, L);
         seg_end(c);
-        if (!has_b) break;
-        if (c + 2 < c1) {
-            load_chunk(wa, wp + 2 * kChunkBytes);
-            load_act<N>(aa, m, c + 2);
-        }
+        load_chunk(wa, wp + 2 * kChunkBytes);
+        load_act<N>(aa, m, c + 2);
         chunk_mfma<N>(wb, ab, part, L);
         seg_end(c + 1);
-        wp += 2 * kChunkBytes;
+    }
+    if (c + 1 < c1) {
+        load_chunk(wb, wp + kChunkBytes);
+        load_act<N>(ab, m, c + 1);
+        chunk_mfma<N>(wa, aa, part, L);
+        seg_end(c);
+        chunk_mfma<N>(wb, ab, part, L);
+        seg_end(c + 1);
+    } else {
+        chunk_mfma<N>(wa, aa, part, L);
+        seg_end(c);
     }
 }
 
