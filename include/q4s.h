@@ -60,15 +60,19 @@
  *     |x| < 8e6 (so d_x stays finite).
  *   Output y: fp32 [n][rows], row-major.
  *
- * Numerics: per block the kernel forms the exact integer s, then
- *   part = fmaf(d_w * d_x, (float)s, part) over the 8 blocks of a 256-column
- *   chunk (d_w * d_x is exact in fp32), adds the chunk partial to the row
- *   accumulator in chunk order, and, for long rows split over the 4 waves of a
- *   workgroup, adds the (up to 4) split accumulators in split order.  The
- *   partition depends only on (rows, cols), so results are deterministic,
- *   identical for every n (row t of an n-row call equals the 1-row call bit
- *   for bit), and identical between q4s_gemv_q4_0 and q4s_sweep_run.
- *   Against the exact result the error is below 1e-5 * sum_b |d_w d_x s|.
+ * Numerics: per block the kernel forms the exact integer s and the term
+ *   fmaf(d_w * d_x, (float)s, chain) (d_w * d_x is exact in fp32).  A wave
+ *   streams a contiguous range of 256-column chunks of 64 rows; within each
+ *   segment of up to 16 chunks, blocks 0-3 of every chunk form chain A and
+ *   blocks 4-7 chain B (in chunk order), and the row accumulator takes
+ *   acc += (A + B) at the end of the segment.  Rows longer than 2048 columns
+ *   are split over 2 or 4 waves of a workgroup, whose accumulators are added
+ *   in split order.  The partition depends only on (rows, cols), so results
+ *   are deterministic, identical for every n (row t of an n-row call equals
+ *   the 1-row call bit for bit), and identical between q4s_gemv_q4_0 and
+ *   q4s_sweep_run.  The rounding error is at most
+ *   (64 + ceil(c/16) + 4) * 2^-24 * sum_b |d_w d_x s|, c = chunks per wave,
+ *   i.e. below 1e-5 * sum_b |d_w d_x s| for rows up to 2^20 columns.
  */
 #ifndef Q4S_H
 #define Q4S_H
