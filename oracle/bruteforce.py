@@ -36,6 +36,16 @@ def dequant_q8_0(xq8: np.ndarray, n: int, cols: int) -> np.ndarray:
     return (q * d[:, :, None]).reshape(n, cols)
 
 
+def dequant_q8_0_weights(w: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """Q8_0 weight blocks [rows][cols/32][34] -> fp64 [rows][cols]."""
+    return dequant_q8_0(w, rows, cols)
+
+
+def q8w_gemv64(w: np.ndarray, xq8: np.ndarray, rows: int, cols: int, n: int) -> np.ndarray:
+    """fp64 y [n][rows] of a Q8_0-weight GEMV by dequantize-then-matmul."""
+    return dequant_q8_0(xq8, n, cols) @ dequant_q8_0_weights(w, rows, cols).T
+
+
 def gemv64(w: np.ndarray, xq8: np.ndarray, rows: int, cols: int, n: int) -> np.ndarray:
     """fp64 y [n][rows] by dequantize-then-matmul."""
     W = dequant_q4_0(w, rows, cols)

@@ -59,6 +59,12 @@ def _bind(path: str):
     L.q4o_block_sums.argtypes = [p, p, i64, i64, ctypes.c_int, p]
     L.q4o_gemv.argtypes = [p, p, i64, i64, ctypes.c_int, p, p, p]
     L.q4o_gemv_rows.argtypes = [p, p, i64, ctypes.c_int, p, i64, p, p]
+    L.q4o_q8w_block_dot.argtypes = [p, p]
+    L.q4o_q8w_block_dot.restype = ctypes.c_int32
+    L.q4o_q8w_block_sums.argtypes = [p, p, i64, i64, ctypes.c_int, p]
+    L.q4o_q8w_gemv.argtypes = [p, p, i64, i64, ctypes.c_int, p, p, p]
+    L.q4o_requant_block_q8_0_to_q4_0.argtypes = [p, p]
+    L.q4o_requant_q8_0_to_q4_0.argtypes = [p, p, i64]
     L.q4o_set_threads.argtypes = [ctypes.c_int]
     L.q4o_max_threads.restype = ctypes.c_int
     return L
@@ -200,3 +206,47 @@ def gemv_rows(w: np.ndarray, xq8: np.ndarray, cols: int, n: int, row_idx: np.nda
     S = np.empty((n, idx.size), np.float64)
     lib().q4o_gemv_rows(_ptr(w), _ptr(xq8), cols, n, _ptr(idx), idx.size, _ptr(y), _ptr(S))
     return y, S
+
+
+# ---------------------------------------------------------------- Q8_0 weights
+
+def q8w_block_dot(w_block: np.ndarray, x_block: np.ndarray) -> int:
+    a = np.ascontiguousarray(w_block, dtype=np.uint8)
+    b = np.ascontiguousarray(x_block, dtype=np.uint8)
+    assert a.size == Q8_BLOCK_BYTES and b.size == Q8_BLOCK_BYTES
+    return int(lib().q4o_q8w_block_dot(_ptr(a), _ptr(b)))
+
+
+def q8w_block_sums(w: np.ndarray, xq8: np.ndarray, rows: int, cols: int, n: int) -> np.ndarray:
+    """Q8_0 weights [rows][cols/32][34] x Q8_0 activations -> int32 [n][rows][cols/32]"""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    xq8 = np.ascontiguousarray(xq8, dtype=np.uint8)
+    assert w.size == rows * (cols // QK) * Q8_BLOCK_BYTES
+    assert xq8.size == n * (cols // QK) * Q8_BLOCK_BYTES
+    s = np.empty((n, rows, cols // QK), np.int32)
+    lib().q4o_q8w_block_sums(_ptr(w), _ptr(xq8), rows, cols, n, _ptr(s))
+    return s
+
+
+def q8w_gemv(w: np.ndarray, xq8: np.ndarray, rows: int, cols: int, n: int, want_y64: bool = False):
+    """Q8_0-weight GEMV -> (y float32 [n][rows], S float64 [n][rows][, y64])"""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    xq8 = np.ascontiguousarray(xq8, dtype=np.uint8)
+    assert w.size == rows * (cols // QK) * Q8_BLOCK_BYTES
+    assert xq8.size == n * (cols // QK) * Q8_BLOCK_BYTES
+    y = np.empty((n, rows), np.float32)
+    S = np.empty((n, rows), np.float64)
+    y64 = np.empty((n, rows), np.float64) if want_y64 else None
+    lib().q4o_q8w_gemv(_ptr(w), _ptr(xq8), rows, cols, n, _ptr(y), _ptr(S),
+                       _ptr(y64) if want_y64 else None)
+    return (y, S, y64) if want_y64 else (y, S)
+
+
+def requant_q8_0_to_q4_0(w_q8: np.ndarray) -> np.ndarray:
+    """Q8_0 blocks [..., 34] -> Q4_0 blocks [..., 18] (load-time requantization)."""
+    a = np.ascontiguousarray(w_q8, dtype=np.uint8)
+    assert a.shape[-1] == Q8_BLOCK_BYTES
+    nblk = a.size // Q8_BLOCK_BYTES
+    out = np.empty(a.shape[:-1] + (Q4_BLOCK_BYTES,), np.uint8)
+    lib().q4o_requant_q8_0_to_q4_0(_ptr(a), _ptr(out), nblk)
+    return out

@@ -15,6 +15,10 @@
  *     lm_head 248 MB at 151936 x 1536), which fix 18 B and 34 B blocks.
  *   - "How it works", src/mega.cu bullet and M16: per-block integer sums,
  *     accumulated through one float expression.
+ *   - Milestones M6 and M14, and the gemv_q8_dp4a bullet of "How it works":
+ *     the lm_head stored as Q8_0 weights (34 B blocks of 32 int8 values and a
+ *     binary16 scale), multiplied by the same int8 activations.
+ *   - Milestones M14 and M18: 8-bit heads requantized to Q4_0 at load.
  *
  * Block formats (GGUF convention, where the pages leave the byte order open):
  *   Q4_0 (18 B / 32 weights): fp16 scale d (little-endian), then 16 bytes qs.
@@ -24,6 +28,8 @@
  *        d = max|x| / 127 (fp32, correctly rounded), q = round-half-away(x / d)
  *        with the fp32 d as the divisor; stored d = fp16(d), round to nearest
  *        even, subnormals kept.  An all-zero block stores d = +0 and q = 0.
+ *
+ * Q8_0-weight GEMV: as below with s = sum_j w_j * q_j (int8 weights, no offset).
  *
  * GEMV definition (exact up to the final rounding):
  *   s[n][r][b] = sum_j (nibble_{r,b,j} - 8) * q_{n,b,j}          (int32, literal)
@@ -260,6 +266,107 @@ void q4o_gemv_rows(const uint8_t* w, const uint8_t* xq8, int64_t cols, int n,
             gemv_one(w + row_idx[i] * nb * Q4_BLOCK_BYTES, xq8 + (int64_t)t * nb * Q8_BLOCK_BYTES,
                      nb, y ? y + o : 0, 0, scale ? scale + o : 0);
         }
+}
+
+/* ------------------------------------------------------------------ */
+/* Q8_0 weights (the 8-bit lm_head of milestones M6 and M14).           */
+/* ------------------------------------------------------------------ */
+
+/* s = sum_j w_j * q_j over two Q8_0 blocks (weight block, activation block). */
+int32_t q4o_q8w_block_dot(const uint8_t* w_block, const uint8_t* x_block)
+{
+    const int8_t* w = (const int8_t*)(w_block + 2);
+    const int8_t* q = (const int8_t*)(x_block + 2);
+    int32_t s = 0;
+    for (int j = 0; j < QK; ++j)
+        s += (int32_t)w[j] * (int32_t)q[j];
+    return s;
+}
+
+/* w: [rows][cols/32] Q8_0 weight blocks; xq8: [n][cols/32] Q8_0 blocks; s: [n][rows][cols/32] */
+void q4o_q8w_block_sums(const uint8_t* w, const uint8_t* xq8, int64_t rows, int64_t cols, int n,
+                        int32_t* s)
+{
+    int64_t nb = cols / QK;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int t = 0; t < n; ++t)
+            for (int64_t b = 0; b < nb; ++b)
+                s[((int64_t)t * rows + r) * nb + b] =
+                    q4o_q8w_block_dot(w + (r * nb + b) * Q8_BLOCK_BYTES,
+                                      xq8 + ((int64_t)t * nb + b) * Q8_BLOCK_BYTES);
+}
+
+/* y, scale, y64: [n][rows]; y = fp32(sum_b (d_w d_x) s), summed in fp64 */
+void q4o_q8w_gemv(const uint8_t* w, const uint8_t* xq8, int64_t rows, int64_t cols, int n, float* y,
+                  double* scale, double* y64)
+{
+    int64_t nb = cols / QK;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int t = 0; t < n; ++t) {
+            double acc = 0.0, sabs = 0.0;
+            for (int64_t b = 0; b < nb; ++b) {
+                const uint8_t* wb = w + (r * nb + b) * Q8_BLOCK_BYTES;
+                const uint8_t* xb = xq8 + ((int64_t)t * nb + b) * Q8_BLOCK_BYTES;
+                double p = (double)q4o_fp16_to_f32(load_u16_le(wb)) *
+                           (double)q4o_fp16_to_f32(load_u16_le(xb));
+                double tv = p * (double)q4o_q8w_block_dot(wb, xb); /* exact: <= 42 bits */
+                acc += tv;
+                sabs += fabs(tv);
+            }
+            int64_t o = (int64_t)t * rows + r;
+            if (y)
+                y[o] = (float)acc;
+            if (y64)
+                y64[o] = acc;
+            if (scale)
+                scale[o] = sabs;
+        }
+}
+
+/* ------------------------------------------------------------------ */
+/* Q8_0 -> Q4_0 requantization at load (milestones M14 and M18).        */
+/* The pages name the conversion but not the Q4_0 rounding rule; this   */
+/* takes the GGUF reference rule for the format: the element of largest */
+/* magnitude (first one on ties) maps to nibble 0, d = that value / -8, */
+/* nibble = min(15, trunc(x / d + 8.5)) with x / d formed as x * (1/d), */
+/* all in fp32, and the stored scale is fp16(d).                        */
+/* ------------------------------------------------------------------ */
+
+void q4o_requant_block_q8_0_to_q4_0(const uint8_t* q8_block, uint8_t* q4_block)
+{
+    float d8 = q4o_fp16_to_f32(load_u16_le(q8_block));
+    const int8_t* q = (const int8_t*)(q8_block + 2);
+    float x[QK];
+    for (int j = 0; j < QK; ++j)
+        x[j] = (float)q[j] * d8; /* exact: 8-bit times 11-bit significand */
+    float amax = 0.0f, vmax = 0.0f;
+    for (int j = 0; j < QK; ++j) {
+        if (fabsf(x[j]) > amax) {
+            amax = fabsf(x[j]);
+            vmax = x[j];
+        }
+    }
+    float d = vmax / -8.0f;
+    float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+    store_u16_le(q4_block, q4o_f32_to_fp16(d));
+    int nib[QK];
+    for (int j = 0; j < QK; ++j) {
+        float v = x[j] * id + 8.5f; /* two roundings: the product, then the sum */
+        int n = (int)v;             /* truncation toward zero; v >= 0 here */
+        nib[j] = n > 15 ? 15 : n;
+    }
+    for (int j = 0; j < 16; ++j)
+        q4_block[2 + j] = (uint8_t)(nib[j] | (nib[j + 16] << 4));
+}
+
+/* w_q8: [rows][cols/32] Q8_0 blocks -> w_q4: [rows][cols/32] Q4_0 blocks */
+void q4o_requant_q8_0_to_q4_0(const uint8_t* w_q8, uint8_t* w_q4, int64_t n_blocks)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < n_blocks; ++b)
+        q4o_requant_block_q8_0_to_q4_0(w_q8 + b * Q8_BLOCK_BYTES, w_q4 + b * Q4_BLOCK_BYTES);
 }
 
 void q4o_set_threads(int nthreads)

@@ -39,6 +39,20 @@ def q4_0_weights(rows: int, cols: int, rng: np.random.Generator) -> np.ndarray:
     return out.reshape(rows, nb, Q4_BLOCK_BYTES)
 
 
+def q8_0_weights(rows: int, cols: int, rng: np.random.Generator) -> np.ndarray:
+    """uint8 [rows][cols/32][34]: fp16 scale (little-endian) then 32 int8 values uniform in
+    -127..127 (the range a Q8_0 quantizer produces); the scale as for Q4_0 weights."""
+    assert cols % 32 == 0
+    nb = cols // 32
+    nblk = rows * nb
+    d = (np.abs(rng.normal(0.0, 0.02, size=nblk)) / 8.0).astype("<f2")
+    qs = rng.integers(-127, 128, size=(nblk, 32), dtype=np.int8)
+    out = np.empty((nblk, 34), np.uint8)
+    out[:, 0:2] = d.view(np.uint8).reshape(nblk, 2)
+    out[:, 2:] = qs.view(np.uint8)
+    return out.reshape(rows, nb, 34)
+
+
 def activation(n: int, cols: int, rng: np.random.Generator, outliers: int = 8,
                factor: float = 20.0) -> np.ndarray:
     """fp32 [n][cols] ~ N(0,1), with `outliers` shared channels scaled by `factor`."""

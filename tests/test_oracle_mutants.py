@@ -11,6 +11,7 @@ import pytest
 import test_oracle_fp16 as t16
 import test_oracle_q4 as t4
 import test_oracle_q8 as t8
+import test_oracle_q8w as t8w
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
                    "q4_oracle.c")
@@ -42,6 +43,20 @@ MUTANTS = [
      "gemv_one(w + r * nb * Q4_BLOCK_BYTES, xq8, nb,"),
     ("last_block_dropped", "for (int64_t b = 0; b < nb; ++b) {\n        const uint8_t* wb",
      "for (int64_t b = 0; b + 1 < nb; ++b) {\n        const uint8_t* wb"),
+    ("q8w_weights_unsigned", "const int8_t* w = (const int8_t*)(w_block + 2);",
+     "const uint8_t* w = (const uint8_t*)(w_block + 2);"),
+    ("q8w_scale_drops_dx", "*\n                           (double)q4o_fp16_to_f32(load_u16_le(xb));",
+     "*\n                           1.0;"),
+    ("q8w_token_ignored",
+     "const uint8_t* xb = xq8 + ((int64_t)t * nb + b) * Q8_BLOCK_BYTES;\n                double p",
+     "const uint8_t* xb = xq8 + ((int64_t)0 * nb + b) * Q8_BLOCK_BYTES;\n                double p"),
+    ("requant_last_tie_wins", "if (fabsf(x[j]) > amax) {", "if (fabsf(x[j]) >= amax) {"),
+    ("requant_unsigned_max", "float d = vmax / -8.0f;", "float d = amax / 8.0f;"),
+    ("requant_exact_division", "float v = x[j] * id + 8.5f;", "float v = x[j] / d + 8.5f;"),
+    ("requant_round_plus_8", "float v = x[j] * id + 8.5f;", "float v = x[j] * id + 8.0f;"),
+    ("requant_no_clamp", "nib[j] = n > 15 ? 15 : n;", "nib[j] = n & 15;"),
+    ("requant_halves_swapped", "(uint8_t)(nib[j] | (nib[j + 16] << 4));",
+     "(uint8_t)(nib[j + 16] | (nib[j] << 4));"),
 ]
 
 
@@ -57,13 +72,21 @@ def _pins(o, b):
               ("gemv_zero", lambda: t4.test_gemv_all_eight_nibbles_is_exact_zero(o)),
               ("gemv_one_hot", lambda: t4.test_gemv_one_hot_activation_closed_form(o)),
               ("gemv_brute_a", lambda: t4.test_gemv_matches_fp64_bruteforce(o, b, 17, 288, 8)),
-              ("gemv_brute_b", lambda: t4.test_gemv_matches_fp64_bruteforce(o, b, 70, 96, 1))]
+              ("gemv_brute_b", lambda: t4.test_gemv_matches_fp64_bruteforce(o, b, 70, 96, 1)),
+              ("q8w_golden", lambda: t8w.test_q8w_gemv_golden(o)),
+              ("q8w_sums_brute", lambda: t8w.test_q8w_block_sums_brute_force(o)),
+              ("q8w_brute", lambda: t8w.test_q8w_gemv_matches_fp64_bruteforce(o, b, 17, 288, 8)),
+              ("q8w_unit", lambda: t8w.test_q8w_gemv_unit_weights_closed_form(o)),
+              ("requant_round_trip", lambda: t8w.test_requant_round_trips_q4_0_blocks(o)),
+              ("requant_nearest", lambda: t8w.test_requant_rounds_to_nearest_level(o))]
     checks += [(f"q8_golden_{c['name']}", (lambda c=c: t8.test_q8_0_golden_blocks(o, c)))
                for c in t8.CASES]
     checks += [(f"q4_golden_{c['name']}", (lambda c=c: t4.test_q4_0_golden_decode(o, c)))
                for c in t4.Q4_CASES]
     checks += [(f"sum_golden_{c['name']}", (lambda c=c: t4.test_block_sum_golden(o, c)))
                for c in t4.SUM_CASES]
+    checks += [(f"requant_golden_{c['name']}", (lambda c=c: t8w.test_requant_golden(o, c)))
+               for c in t8w.RQ_CASES]
     failed = []
     with np.errstate(all="ignore"):
         for name, fn in checks:
