@@ -25,7 +25,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "Q4_0 GEMV weight-stream GB/s (% of 8 TB/s HBM peak) and implied tok/s at N=1"
-KERNEL_SRC = os.path.join(ROOT, "q4_weight_streaming_amd", "csrc", "q4s_kernels.hip")
+# the sources the sweep kernel is compiled from (a PMC summary applies only to these)
+KERNEL_SRCS = [os.path.join(ROOT, "q4_weight_streaming_amd", "csrc", f)
+               for f in ("q4s_kernels.hip", "q4s_device.h", "q4s_internal.h")]
 
 
 def log(msg: str) -> None:
@@ -33,7 +35,10 @@ def log(msg: str) -> None:
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def workload_shapes(name: str):

@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define Q4S_ABI_VERSION 1
+#define Q4S_ABI_VERSION 2
 #define Q4S_MAX_N 8
 
 typedef enum {
@@ -160,6 +160,75 @@ q4s_status q4s_gemv_q4_0(const void* w_packed, const void* x_q8, float* y, int64
  */
 q4s_status q4s_block_sums(const void* w_packed, const void* x_q8, int32_t* s, int64_t rows,
                           int64_t cols, int n, void* stream);
+
+/* ------------------------------------------------------ Q8_0 weights */
+
+/*
+ * The 8-bit output head (milestone M6 of the "minfer" README: Q8_0 weights in
+ * a linear layout for a coalesced int8 GEMV, the gemv_q8_dp4a bullet of "How
+ * it works"), and its load-time requantization to Q4_0 (milestones M14, M18).
+ *
+ * Canonical Q8_0 weights (GGUF): [rows][cols/32] blocks of 34 bytes: binary16
+ *   scale d_w (little-endian), then 32 int8 values w_j; weight = w_j * d_w.
+ * Packed Q8_0 (produced by q4s_repack_q8_0): the Q4_0 groups and chunks
+ *   (G = ceil(rows/64), C = ceil(cols/256)); group g, chunk c occupies 17408
+ *   bytes at offset (g*C + c) * 17408, as two pieces of 8704 bytes (blocks
+ *   0-3, then 4-7 of the chunk), each:
+ *     bytes [0, 8192)   : int8 values, [4 blocks][2 halves][64 rows][16 bytes]
+ *                         (half h holds elements 16h .. 16h+15);
+ *     bytes [8192, 8704): scales, [64 rows][4 blocks] binary16 d_w.
+ *   Padding rows and blocks hold zero bytes.
+ * Numerics as for Q4_0 with s = sum_j w_j * q_j, except that chain A takes
+ *   the even blocks of each chunk and chain B the odd ones; the same
+ *   determinism, n-invariance and error bound hold.
+ */
+
+/* Canonical Q8_0 bytes: rows * cols/32 * 34.  0 for invalid shapes. */
+size_t q4s_q8_0_bytes(int64_t rows, int64_t cols);
+
+/* Packed Q8_0 bytes: ceil(rows/64) * ceil(cols/256) * 17408.  0 if invalid. */
+size_t q4s_packed_q8_0_bytes(int64_t rows, int64_t cols);
+
+/*
+ * Weight repack (load time).  w_q8_0: canonical Q8_0 (2-byte aligned);
+ * w_packed: q4s_packed_q8_0_bytes(rows, cols) bytes (16-byte aligned), fully
+ * overwritten, padding included.  Lossless.  Source: milestone M6 (linear
+ * layout for coalescing) and M15 (row-group packing at load).
+ */
+q4s_status q4s_repack_q8_0(const void* w_q8_0, void* w_packed, int64_t rows, int64_t cols,
+                           void* stream);
+
+/*
+ * y[t][r] = sum_b d_w[r][b] * d_x[t][b] * sum_j w_{r,b,j} q_{t,b,j} for t < n,
+ * r < rows.  w_packed: packed Q8_0 (16-byte aligned); x_q8: planar Q8_0
+ * activation of n rows (16-byte aligned); y: fp32 [n][rows], must not overlap
+ * either input.  n in 0..8.  Needs no workspace.  Source: milestone M6 and the
+ * gemv_q8_dp4a bullet of "How it works".
+ */
+q4s_status q4s_gemv_q8_0(const void* w_packed, const void* x_q8, float* y, int64_t rows,
+                         int64_t cols, int n, void* stream);
+
+/*
+ * Test hook: exact per-block sums s[t][r][b] = sum_j w_{r,b,j} * q_{t,b,j},
+ * int32 [n][rows][cols/32], from the same device code as q4s_gemv_q8_0.
+ */
+q4s_status q4s_block_sums_q8_0(const void* w_packed, const void* x_q8, int32_t* s, int64_t rows,
+                               int64_t cols, int n, void* stream);
+
+/*
+ * Load-time requantization of canonical Q8_0 weights to canonical Q4_0 (then
+ * q4s_repack_q4_0).  w_q8_0: rows * cols/32 blocks of 34 bytes (2-byte
+ * aligned); w_q4_0: q4s_q4_0_bytes(rows, cols) bytes (2-byte aligned), must
+ * not overlap the input.  Per block, in fp32 (the pages name the conversion,
+ * not its rounding; this is the GGUF reference rule for Q4_0):
+ * x_j = w_j * d_w; vmax = the x_j of largest magnitude, the first on ties;
+ * d = vmax / -8; id = 1/d (0 when d == 0); nibble_j = min(15,
+ * trunc(x_j * id + 8.5)); stored scale binary16(d), nearest even (a zero
+ * block stores -0).  Blocks with a non-finite scale give unspecified bytes.
+ * Source: milestones M14 and M18.
+ */
+q4s_status q4s_requant_q8_0_to_q4_0(const void* w_q8_0, void* w_q4_0, int64_t rows, int64_t cols,
+                                    void* stream);
 
 /* ---------------------------------------------------- layer-stack sweep */
 

@@ -61,6 +61,12 @@ def lib():
             "q4s_quantize_q8_0": ([p, p, i32, i64, p], i32),
             "q4s_gemv_q4_0": ([p, p, p, i64, i64, i32, p], i32),
             "q4s_block_sums": ([p, p, p, i64, i64, i32, p], i32),
+            "q4s_q8_0_bytes": ([i64, i64], sz),
+            "q4s_packed_q8_0_bytes": ([i64, i64], sz),
+            "q4s_repack_q8_0": ([p, p, i64, i64, p], i32),
+            "q4s_gemv_q8_0": ([p, p, p, i64, i64, i32, p], i32),
+            "q4s_block_sums_q8_0": ([p, p, p, i64, i64, i32, p], i32),
+            "q4s_requant_q8_0_to_q4_0": ([p, p, i64, i64, p], i32),
             "q4s_sweep_plan_create": ([p, i32, i32, ctypes.POINTER(sz), ctypes.POINTER(p)], i32),
             "q4s_sweep_plan_upload": ([p, p, sz, p], i32),
             "q4s_sweep_run": ([p, p], i32),
@@ -73,7 +79,7 @@ def lib():
             f = getattr(L, name)
             f.argtypes = args
             f.restype = res
-        if L.q4s_abi_version() != 1:
+        if L.q4s_abi_version() != 2:
             raise RuntimeError("libq4stream ABI version mismatch")
         _lib = L
     return _lib
@@ -175,6 +181,62 @@ def block_sums(w_packed: torch.Tensor, x_q8: torch.Tensor, rows: int, cols: int,
                                                    _dev(x_q8, "x_q8", torch.uint8),
                                                    _dev(out, "out", torch.int32), rows, cols, n,
                                                    _stream(w_packed.device)))
+    return out
+
+
+# ------------------------------------------------------------ Q8_0 weights
+
+def q8_0_bytes(rows: int, cols: int) -> int:
+    return int(lib().q4s_q8_0_bytes(rows, cols))
+
+
+def packed_q8_0_bytes(rows: int, cols: int) -> int:
+    return int(lib().q4s_packed_q8_0_bytes(rows, cols))
+
+
+def repack_q8_0(w_q8_0: torch.Tensor, rows: int, cols: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Canonical Q8_0 weight bytes (uint8, rows*cols/32*34) -> packed uint8 tensor."""
+    if w_q8_0.numel() != q8_0_bytes(rows, cols) or w_q8_0.dtype != torch.uint8:
+        raise ValueError("w_q8_0 must be uint8 with rows*cols/32*34 elements")
+    if out is None:
+        out = torch.empty(packed_q8_0_bytes(rows, cols), dtype=torch.uint8, device=w_q8_0.device)
+    _check("q4s_repack_q8_0", lib().q4s_repack_q8_0(_dev(w_q8_0, "w_q8_0"), _dev(out, "out", torch.uint8),
+                                                     rows, cols, _stream(w_q8_0.device)))
+    return out
+
+
+def gemv_q8_0(w_packed: torch.Tensor, x_q8: torch.Tensor, rows: int, cols: int, n: int,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """y fp32 [n][rows] = Q8_0 W [rows][cols] x Q8_0 activation rows."""
+    if out is None:
+        out = torch.empty((n, rows), dtype=torch.float32, device=w_packed.device)
+    _check("q4s_gemv_q8_0", lib().q4s_gemv_q8_0(_dev(w_packed, "w_packed", torch.uint8),
+                                                 _dev(x_q8, "x_q8", torch.uint8),
+                                                 _dev(out, "out", torch.float32), rows, cols, n,
+                                                 _stream(w_packed.device)))
+    return out
+
+
+def block_sums_q8_0(w_packed: torch.Tensor, x_q8: torch.Tensor, rows: int, cols: int, n: int) -> torch.Tensor:
+    """Per-block integer sums of the Q8_0-weight product, int32 [n][rows][cols/32]."""
+    out = torch.empty((n, rows, cols // 32), dtype=torch.int32, device=w_packed.device)
+    _check("q4s_block_sums_q8_0", lib().q4s_block_sums_q8_0(_dev(w_packed, "w_packed", torch.uint8),
+                                                             _dev(x_q8, "x_q8", torch.uint8),
+                                                             _dev(out, "out", torch.int32), rows, cols, n,
+                                                             _stream(w_packed.device)))
+    return out
+
+
+def requant_q8_0_to_q4_0(w_q8_0: torch.Tensor, rows: int, cols: int,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """Canonical Q8_0 weight bytes -> canonical Q4_0 bytes (uint8, rows*cols/32*18)."""
+    if w_q8_0.numel() != q8_0_bytes(rows, cols) or w_q8_0.dtype != torch.uint8:
+        raise ValueError("w_q8_0 must be uint8 with rows*cols/32*34 elements")
+    if out is None:
+        out = torch.empty(q4_0_bytes(rows, cols), dtype=torch.uint8, device=w_q8_0.device)
+    _check("q4s_requant_q8_0_to_q4_0",
+           lib().q4s_requant_q8_0_to_q4_0(_dev(w_q8_0, "w_q8_0"), _dev(out, "out", torch.uint8), rows, cols,
+                                          _stream(w_q8_0.device)))
     return out
 
 

@@ -73,6 +73,9 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 size_t packed_bytes(int64_t rows, int64_t cols) {
     return (size_t)(groups_of(rows) * chunks_of(cols)) * kChunkBytes;
 }
+size_t packed_q8_bytes(int64_t rows, int64_t cols) {
+    return (size_t)(groups_of(rows) * chunks_of(cols)) * kQ8ChunkBytes;
+}
 // planar Q8_0: q [n][cols], then d_x [n][dstride] (rows padded to 8 entries)
 size_t q8_bytes(int n, int64_t cols) {
     return (size_t)n * (size_t)cols + (size_t)n * (size_t)dstride_of(cols) * 2;
@@ -95,13 +98,13 @@ MatDesc make_desc(const void* w, const void* xq8, float* y, int64_t rows, int64_
     return m;
 }
 
-// validation shared by the GEMV and each sweep matrix
+// validation shared by the GEMVs and each sweep matrix
 q4s_status check_gemv(const void* w, const void* xq8, const float* y, int64_t rows, int64_t cols,
-                      int n) {
+                      int n, bool q8w = false) {
     q4s_status s = check_shape(rows, cols, n);
     if (s) return s;
     const bool live = rows > 0 && n > 0;
-    const size_t wb = live ? packed_bytes(rows, cols) : 0;
+    const size_t wb = live ? (q8w ? packed_q8_bytes(rows, cols) : packed_bytes(rows, cols)) : 0;
     const size_t xb = live ? q8_bytes(n, cols) : 0;
     const size_t yb = live ? (size_t)n * rows * 4 : 0;
     if ((s = check_ptr(w, wb, 16, "w_packed"))) return s;
@@ -193,12 +196,16 @@ q4s_status q4s_gemv_q4_0(const void* w_packed, const void* x_q8, float* y, int64
     return hip_status(launch_gemv(m, n, gsets_of(m.G, m.ks), (hipStream_t)stream), "gemv launch");
 }
 
-q4s_status q4s_block_sums(const void* w_packed, const void* x_q8, int32_t* sums, int64_t rows,
-                          int64_t cols, int n, void* stream) {
+}  // extern "C"
+
+namespace {
+
+q4s_status block_sums_any(const void* w_packed, const void* x_q8, int32_t* sums, int64_t rows, int64_t cols,
+                          int n, void* stream, bool q8w) {
     q4s_status s = check_shape(rows, cols, n);
     if (s) return s;
     const bool live = rows > 0 && n > 0 && cols > 0;
-    const size_t wb = live ? packed_bytes(rows, cols) : 0;
+    const size_t wb = live ? (q8w ? packed_q8_bytes(rows, cols) : packed_bytes(rows, cols)) : 0;
     const size_t xb = live ? q8_bytes(n, cols) : 0;
     const size_t sb = live ? (size_t)n * rows * (cols / 32) * 4 : 0;
     if ((s = check_ptr(w_packed, wb, 16, "w_packed"))) return s;
@@ -208,7 +215,71 @@ q4s_status q4s_block_sums(const void* w_packed, const void* x_q8, int32_t* sums,
         return fail(Q4S_ERR_ALIAS, "s overlaps an input");
     if (!live) return ok();
     const MatDesc m = make_desc(w_packed, x_q8, nullptr, rows, cols, n);
-    return hip_status(launch_block_sums(m, n, sums, (hipStream_t)stream), "block_sums launch");
+    return hip_status(q8w ? launch_block_sums_q8_0(m, n, sums, (hipStream_t)stream)
+                          : launch_block_sums(m, n, sums, (hipStream_t)stream),
+                      "block_sums launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+q4s_status q4s_block_sums(const void* w_packed, const void* x_q8, int32_t* sums, int64_t rows,
+                          int64_t cols, int n, void* stream) {
+    return block_sums_any(w_packed, x_q8, sums, rows, cols, n, stream, false);
+}
+
+// ============================================================= Q8_0 weights
+
+size_t q4s_q8_0_bytes(int64_t rows, int64_t cols) {
+    if (check_shape(rows, cols, 1) != Q4S_OK) return 0;
+    return (size_t)rows * (size_t)(cols / 32) * 34;
+}
+
+size_t q4s_packed_q8_0_bytes(int64_t rows, int64_t cols) {
+    if (check_shape(rows, cols, 1) != Q4S_OK) return 0;
+    return packed_q8_bytes(rows, cols);
+}
+
+q4s_status q4s_repack_q8_0(const void* w_q8_0, void* w_packed, int64_t rows, int64_t cols, void* stream) {
+    q4s_status s = check_shape(rows, cols, 1);
+    if (s) return s;
+    const size_t cb = (size_t)rows * (size_t)(cols / 32) * 34;
+    const size_t pb = packed_q8_bytes(rows, cols);
+    if ((s = check_ptr(w_q8_0, cb, 2, "w_q8_0"))) return s;
+    if ((s = check_ptr(w_packed, pb, 16, "w_packed"))) return s;
+    if (overlap(w_q8_0, cb, w_packed, pb)) return fail(Q4S_ERR_ALIAS, "w_packed overlaps w_q8_0");
+    if (pb == 0) return ok();
+    return hip_status(launch_repack_q8_0((const uint8_t*)w_q8_0, (uint8_t*)w_packed, rows, cols,
+                                         (hipStream_t)stream), "repack launch");
+}
+
+q4s_status q4s_gemv_q8_0(const void* w_packed, const void* x_q8, float* y, int64_t rows, int64_t cols,
+                         int n, void* stream) {
+    q4s_status s = check_gemv(w_packed, x_q8, y, rows, cols, n, true);
+    if (s) return s;
+    if (rows == 0 || n == 0) return ok();
+    const MatDesc m = make_desc(w_packed, x_q8, y, rows, cols, n);
+    return hip_status(launch_gemv_q8_0(m, n, gsets_of(m.G, m.ks), (hipStream_t)stream), "gemv launch");
+}
+
+q4s_status q4s_block_sums_q8_0(const void* w_packed, const void* x_q8, int32_t* sums, int64_t rows,
+                               int64_t cols, int n, void* stream) {
+    return block_sums_any(w_packed, x_q8, sums, rows, cols, n, stream, true);
+}
+
+q4s_status q4s_requant_q8_0_to_q4_0(const void* w_q8_0, void* w_q4_0, int64_t rows, int64_t cols,
+                                    void* stream) {
+    q4s_status s = check_shape(rows, cols, 1);
+    if (s) return s;
+    const int64_t nblk = rows * (cols / 32);
+    const size_t b8 = (size_t)nblk * 34, b4 = (size_t)nblk * 18;
+    if ((s = check_ptr(w_q8_0, b8, 2, "w_q8_0"))) return s;
+    if ((s = check_ptr(w_q4_0, b4, 2, "w_q4_0"))) return s;
+    if (overlap(w_q8_0, b8, w_q4_0, b4)) return fail(Q4S_ERR_ALIAS, "w_q4_0 overlaps w_q8_0");
+    if (nblk == 0) return ok();
+    return hip_status(launch_requant_q8_0_to_q4_0((const uint8_t*)w_q8_0, (uint8_t*)w_q4_0, nblk,
+                                                  (hipStream_t)stream), "requant launch");
 }
 
 // ==================================================================== sweep

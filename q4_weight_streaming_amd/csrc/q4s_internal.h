@@ -22,6 +22,16 @@ constexpr int kWaves = 4;                 // wavefronts per workgroup
 constexpr int kThreads = kWaves * 64;     // workgroup size
 constexpr int kMaxN = 8;                  // activation rows per call
 
+// Packed Q8_0 geometry.  Same 64-row groups and 8-block chunks; a chunk is
+// stored as two pieces of 4 blocks.  Per piece: the int8 values
+// [block][half][row][16 B] (8192 B; one wave-wide 16-byte load reads 1 KB
+// contiguous), then the scales [row][4 x binary16] (512 B; one 8-byte load per
+// lane).
+constexpr int kQ8PieceBlocks = 4;
+constexpr int kQ8PieceQBytes = kQ8PieceBlocks * 2 * kGroupRows * 16;             // 8192
+constexpr int kQ8PieceBytes = kQ8PieceQBytes + kGroupRows * kQ8PieceBlocks * 2;  // 8704
+constexpr int kQ8ChunkBytes = 2 * kQ8PieceBytes;                                // 17408
+
 // One matrix as the GEMV kernels see it.  A workgroup tile ("group set") is
 // kWaves / ks row groups; the ks waves of one group split its chunks into ks
 // contiguous ranges [s*C/ks, (s+1)*C/ks) and add their accumulators in split
@@ -70,6 +80,12 @@ hipError_t launch_gemv(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st)
 hipError_t launch_sweep(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles,
                         int n, hipStream_t st);
 hipError_t launch_block_sums(const MatDesc& m, int n, int32_t* s, hipStream_t st);
+// Q8_0 weights (q4s_q8w.hip).
+hipError_t launch_repack_q8_0(const uint8_t* w, uint8_t* packed, int64_t rows, int64_t cols,
+                              hipStream_t st);
+hipError_t launch_gemv_q8_0(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st);
+hipError_t launch_block_sums_q8_0(const MatDesc& m, int n, int32_t* s, hipStream_t st);
+hipError_t launch_requant_q8_0_to_q4_0(const uint8_t* w8, uint8_t* w4, int64_t n_blocks, hipStream_t st);
 hipError_t launch_bench_read(const void* buf, size_t bytes, int lif, int n_blocks,
                              uint32_t* sink, hipStream_t st);
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t st);

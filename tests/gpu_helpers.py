@@ -71,3 +71,17 @@ def assert_within(y_gpu: np.ndarray, y_ref: np.ndarray, S: np.ndarray, rel: floa
         raise AssertionError(f"{what}: {bad.sum()} outputs off, first at {tuple(i)}: gpu={y_gpu[tuple(i)]!r} "
                              f"ref={y_ref[tuple(i)]!r} S={S[tuple(i)]!r}")
     return float((err / np.where(S > 0, S, 1)).max()) if err.size else 0.0
+
+
+def unpack_packed_q8(packed: np.ndarray, rows: int, cols: int):
+    """Inverse of the documented packed Q8_0 layout -> (canonical [rows][cols/32][34], padding is zero)."""
+    nb = cols // 32
+    G, C = -(-rows // 64), -(-nb // 8)
+    p = packed.reshape(G, C, 2, 8704)
+    qv = p[..., :8192].reshape(G, C, 2, 4, 2, 64, 16)             # [g][c][piece][blk][half][row][16]
+    sc = p[..., 8192:].reshape(G, C, 2, 64, 4, 2)                   # [g][c][piece][row][blk][2]
+    qv = qv.transpose(0, 5, 1, 2, 3, 4, 6).reshape(G * 64, C * 8, 32)
+    sc = sc.transpose(0, 3, 1, 2, 4, 5).reshape(G * 64, C * 8, 2)
+    full = np.concatenate([sc, qv], axis=2)
+    pad_zero = bool((full[rows:] == 0).all() and (full[:, nb:] == 0).all())
+    return np.ascontiguousarray(full[:rows, :nb]), pad_zero

@@ -16,10 +16,10 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = q.header_functions()
-    assert len(names) >= 17
+    assert len(names) >= 23
     for n in names:
         assert hasattr(L, n), n
-    assert L.q4s_abi_version() == 1
+    assert L.q4s_abi_version() == 2
 
 
 def test_status_strings(L):
@@ -41,6 +41,12 @@ def test_sizes():
     assert q.q8_bytes(1, 32) == 32 + 16                    # d_x row padded to 8 entries
     assert q.q8_bytes(3, 288) == 3 * 288 + 3 * 16 * 2
     assert q.packed_bytes(3, 33) == 0 and q.q8_bytes(9, 32) == 0 and q.q4_0_bytes(-1, 32) == 0
+    # Q8_0 weights: the 8-bit lm_head of milestone M14 is 248 MB at 151936 x 1536
+    assert q.q8_0_bytes(151936, 1536) == 247_959_552
+    assert q.packed_q8_0_bytes(151936, 1536) == 247_959_552   # no padding at config shapes
+    assert q.packed_q8_0_bytes(65, 288) == 2 * 2 * 17408
+    assert q.packed_q8_0_bytes(1, 32) == 17408
+    assert q.packed_q8_0_bytes(0, 64) == 0 and q.q8_0_bytes(3, 33) == 0
 
 
 def _err(L):
@@ -77,6 +83,19 @@ def test_other_entry_points_validate(L):
     assert L.q4s_bench_read(FAKE, 32, 3, 0, FAKE + (1 << 30), None) == 2
     assert L.q4s_bench_copy(FAKE, FAKE + 16, 64, None) == 4
     assert L.q4s_sweep_run(None, None) == 1
+    # Q8_0 weights
+    g = L.q4s_gemv_q8_0
+    assert g(FAKE, FAKE, FAKE + (1 << 30), 64, 33, 1, None) == 2
+    assert g(FAKE + 8, FAKE, FAKE + (1 << 30), 64, 64, 1, None) == 3
+    assert g(FAKE, FAKE + (1 << 20), FAKE + 17408 - 4, 64, 64, 1, None) == 4   # y overlaps packed Q8_0
+    assert g(None, None, None, 0, 64, 1, None) == 0
+    assert L.q4s_repack_q8_0(FAKE + 1, FAKE + (1 << 30), 64, 64, None) == 3
+    assert L.q4s_repack_q8_0(FAKE, FAKE, 64, 64, None) == 4
+    assert L.q4s_block_sums_q8_0(FAKE, FAKE + (1 << 28), FAKE + 2, 64, 64, 1, None) == 3
+    assert L.q4s_requant_q8_0_to_q4_0(FAKE, FAKE + 1, 64, 64, None) == 3
+    assert L.q4s_requant_q8_0_to_q4_0(FAKE, FAKE + 64, 64, 64, None) == 4
+    assert L.q4s_requant_q8_0_to_q4_0(None, FAKE, 64, 64, None) == 1
+    assert L.q4s_requant_q8_0_to_q4_0(None, None, 0, 64, None) == 0
 
 
 def _plan(L, mats, n):
