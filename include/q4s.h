@@ -252,6 +252,7 @@ typedef struct {
     int64_t n_mats;
     int64_t n_tiles;          /* workgroups of the GEMV launch                */
     int64_t n_quant_blocks;   /* Q8_0 blocks quantized per run (0: none)      */
+    int64_t fused_quantize;   /* 1: quantized inside the GEMV launch          */
     int64_t weight_bytes;     /* canonical Q4_0 bytes of all matrices         */
     int64_t packed_bytes;     /* packed bytes read by one run                 */
     int64_t act_bytes;        /* Q8_0 activation bytes read by one run        */
@@ -281,9 +282,14 @@ q4s_status q4s_sweep_plan_upload(q4s_plan* plan, void* dev_mem, size_t dev_bytes
 
 /*
  * One sweep: if any matrix has x, one launch quantizes all of them; then one
- * launch streams every matrix's weights once and writes every y.  Calls on
- * one plan must not overlap in time (they share the plan's device tables only
- * for reading, but write the same y and x_q8 buffers).
+ * launch streams every matrix's weights once and writes every y.  When n == 1
+ * and every matrix has x and rows > 0, there is a single launch instead (the
+ * mega kernel of milestone M15 quantizes the activation inside its one kernel):
+ * each wave quantizes the activation blocks of the chunks it streams, x_q8
+ * still receives the Q8_0 bytes, and the results are bit-identical to the
+ * two-launch form.  Calls on one plan must not overlap in
+ * time (they share the plan's device tables only for reading, but write the
+ * same y and x_q8 buffers).
  */
 q4s_status q4s_sweep_run(const q4s_plan* plan, void* stream);
 

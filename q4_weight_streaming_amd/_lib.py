@@ -34,7 +34,7 @@ class _Mat(ctypes.Structure):
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [(k, ctypes.c_int64) for k in
-                ("n_mats", "n_tiles", "n_quant_blocks", "weight_bytes", "packed_bytes", "act_bytes",
+                ("n_mats", "n_tiles", "n_quant_blocks", "fused_quantize", "weight_bytes", "packed_bytes", "act_bytes",
                  "out_bytes", "dev_bytes")]
 
     def as_dict(self) -> dict:

@@ -95,6 +95,7 @@ MatDesc make_desc(const void* w, const void* xq8, float* y, int64_t rows, int64_
     m.ks = choose_ksplit(m.C);
     m.dstride = (int32_t)dstride_of(cols);
     m.pad_ = 0;
+    m.x = nullptr;
     return m;
 }
 
@@ -291,6 +292,7 @@ struct q4s_plan {
     std::vector<QuantDesc> quant;    // matrices with an fp32 activation to quantize
     std::vector<uint32_t> qtiles;    // (activation, first block) pairs, kQuantTileBlocks blocks each
     int64_t quant_blocks = 0;
+    bool fused = false;              // n == 1, every matrix quantized by the GEMV launch itself
     q4s_plan_info info{};
     // device image: [MatDesc x n_mats][QuantDesc x n_quant][tiles][quantize tiles], 16-byte aligned parts
     size_t off_mats = 0, off_quant = 0, off_tiles = 0, off_qtiles = 0, dev_bytes = 0;
@@ -339,14 +341,24 @@ q4s_status q4s_sweep_plan_create(const q4s_mat* mats, int n_mats, int n, size_t*
     q4s_plan* p = new (std::nothrow) q4s_plan;
     if (!p) return fail(Q4S_ERR_PLAN, "out of host memory");
     p->n = n;
+    // One activation row, every matrix live and given as fp32: the GEMV waves
+    // quantize the activation themselves (no separate quantize launch).
+    p->fused = n == 1 && n_mats > 0;
+    for (int i = 0; i < n_mats && p->fused; ++i) {
+        const q4s_mat& a = mats[i];
+        if (!a.x || a.rows == 0 || a.cols == 0) p->fused = false;
+    }
     struct Tile { uint32_t mat, gset; int64_t bytes; };
     std::vector<Tile> tiles;
     for (int i = 0; i < n_mats; ++i) {
         const q4s_mat& a = mats[i];
         MatDesc m = make_desc(a.w_packed, a.x_q8, a.y, a.rows, a.cols, n);
+        if (p->fused) m.x = a.x;
         p->mats.push_back(m);
         p->info.weight_bytes += a.rows * (a.cols / 32) * 18;
-        if (a.x && a.cols > 0) {
+        if (p->fused) {
+            p->info.n_quant_blocks += a.cols / 32;
+        } else if (a.x && a.cols > 0) {
             QuantDesc q;
             q.x = a.x;
             q.q = (int8_t*)a.x_q8;
@@ -394,7 +406,8 @@ q4s_status q4s_sweep_plan_create(const q4s_mat* mats, int n_mats, int n, size_t*
         memcpy(p->image.data() + p->off_qtiles, p->qtiles.data(), p->qtiles.size() * sizeof(uint32_t));
     p->info.n_mats = n_mats;
     p->info.n_tiles = (int64_t)tiles.size();
-    p->info.n_quant_blocks = p->quant_blocks;
+    if (!p->fused) p->info.n_quant_blocks = p->quant_blocks;
+    p->info.fused_quantize = p->fused ? 1 : 0;
     p->info.dev_bytes = (int64_t)p->dev_bytes;
     *dev_bytes_needed = p->dev_bytes;
     *out = p;
@@ -420,6 +433,11 @@ q4s_status q4s_sweep_run(const q4s_plan* p, void* stream) {
     if (!p) return fail(Q4S_ERR_NULL, "plan is NULL");
     if (!p->dev) return fail(Q4S_ERR_PLAN, "plan was not uploaded");
     hipStream_t st = (hipStream_t)stream;
+    if (p->fused)
+        return hip_status(launch_sweep_fused((const MatDesc*)(p->dev + p->off_mats),
+                                             (const uint32_t*)(p->dev + p->off_tiles), (int64_t)p->tiles.size() / 2,
+                                             st),
+                          "sweep launch");
     if (!p->quant.empty()) {
         hipError_t e = launch_quantize_batch((const QuantDesc*)(p->dev + p->off_quant),
                                              (const uint32_t*)(p->dev + p->off_qtiles),

@@ -41,6 +41,7 @@ struct MatDesc {
     const int8_t* xq;     // Q8_0 q, int8 [n][cols]
     const uint16_t* xd;   // Q8_0 d_x, binary16 [n][dstride]
     float* y;             // fp32 [n][rows]
+    const float* x;       // fp32 activation [n][cols] quantized by the GEMV launch itself, or NULL
     int32_t rows, cols;
     int32_t nb, G, C, ks; // blocks per row, row groups, chunks, K splits (1, 2 or 4)
     int32_t dstride;      // d_x row stride: nb rounded up to a multiple of 8
@@ -80,6 +81,9 @@ hipError_t launch_gemv(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st)
 hipError_t launch_sweep(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles,
                         int n, hipStream_t st);
 hipError_t launch_block_sums(const MatDesc& m, int n, int32_t* s, hipStream_t st);
+// The 1-row sweep with the activation quantized by the GEMV waves themselves.
+hipError_t launch_sweep_fused(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles,
+                              hipStream_t st);
 // Q8_0 weights (q4s_q8w.hip).
 hipError_t launch_repack_q8_0(const uint8_t* w, uint8_t* packed, int64_t rows, int64_t cols,
                               hipStream_t st);

@@ -83,10 +83,104 @@ __device__ __forceinline__ int block_dot16(const Unpacked& u, const u32x8& q) {
 // the product of the two scales is exact, so it equals fmaf(d_w * d_x,
 // (float)s, .) bit for bit.  The MFMA path forms exactly these chains.
 
+// ---------------------------------------------------------------- Q8_0 quantization
+
+// 8 consecutive lanes quantize one block, 4 values each: d = max|x| / 127
+// (correctly rounded fp32 division), q = roundf(x / d) (half away from zero),
+// d_x = binary16(d) rounded to nearest even.  All-zero blocks give d = 0, q = 0.
+// quant8_amax is called by all 8 lanes of a block (it shuffles among them).
+__device__ __forceinline__ float quant8_amax(const f32x4& v) {
+    float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 8));
+    return a;
+}
+
+// this lane's 4 quantized values (packed) and the block's binary16 d_x
+__device__ __forceinline__ void quant8_codes(const f32x4& v, float a, uint32_t& packed, uint16_t& h) {
+    const float dd = a / 127.0f;
+    packed = 0;
+    if (a != 0.0f) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) packed |= ((uint32_t)(uint8_t)(int8_t)(int)roundf(v[k] / dd)) << (8 * k);
+    }
+    h = __half_as_ushort(__float2half_rn(dd));
+}
+
+// Where the lane-per-row path gets the Q8_0 activation.  load(slot, c) runs
+// when chunk c's weight loads are issued (slot 0 or 1 follows the chunk
+// buffer), prepare(slot, c) when chunk c is consumed; q and d then give block
+// blk (b within the chunk) as scalar operands.
+//
+// ActGlobal: the planar buffer in global memory, through scalar loads.
+struct ActGlobal {
+    const MatDesc& m;
+    struct Prep {};
+    __device__ __forceinline__ void load(int, int) {}
+    __device__ __forceinline__ Prep prepare(int, int) { return {}; }
+    __device__ __forceinline__ u32x8 q(const Prep&, int t, int blk, int) const {
+        return act_q(m.xq, (int64_t)t * m.cols + (int64_t)blk * 32);
+    }
+    __device__ __forceinline__ float d(const Prep&, int t, int blk, int) const {
+        return act_d(m.xd, (int64_t)t * m.dstride + blk);
+    }
+};
+
+// ActQuant (the fused 1-row sweep): the wave quantizes the 256 fp32 values of
+// the chunk it is about to consume itself -- lane l holds values 4(l%8) ..
+// 4(l%8)+3 of block l/8, 8 lanes per Q8_0 block with the standalone
+// quantizer's arithmetic -- and broadcasts codes and scales with v_readlane.
+// The activation load travels with the chunk's weight loads, so no barrier or
+// prologue stands between the launch and the weight stream.  With `publish`
+// (the waves of row group 0) the codes are also written to x_q8.
+struct ActQuant {
+    const MatDesc& m;
+    bool publish;
+    f32x4 xs[2];
+    struct Prep {
+        uint32_t packed;  // this lane's 4 codes
+        uint32_t dbits;   // fp32 bits of its block's binary16 d_x
+    };
+    __device__ __forceinline__ void load(int slot, int c) {
+        const int lane = threadIdx.x & 63;
+        // clamped, so the load is unconditional; lanes past the row are zeroed in prepare
+        const int64_t i = min((int64_t)c * 256 + 4 * lane, (int64_t)m.cols - 4);
+        xs[slot] = *gp<f32x4>(m.x + i);
+    }
+    __device__ __forceinline__ Prep prepare(int slot, int c) {
+        const int lane = threadIdx.x & 63;
+        const int blk = c * kChunkBlocks + (lane >> 3);
+        const bool valid = blk < m.nb;  // uniform over the 8 lanes of a block
+        f32x4 v = xs[slot];
+        if (!valid) v = (f32x4){0.f, 0.f, 0.f, 0.f};
+        const float a = quant8_amax(v);
+        uint32_t packed;
+        uint16_t h;
+        quant8_codes(v, a, packed, h);
+        if (publish && valid) {
+            const int o = lane & 7;
+            *gwr<uint32_t>((void*)(m.xq + (int64_t)c * 256 + 4 * lane)) = packed;
+            if (o == 0) *gwr<uint16_t>((void*)(m.xd + blk)) = h;
+            if (blk == m.nb - 1 && o < m.dstride - m.nb) gwr<uint16_t>((void*)m.xd)[m.nb + o] = 0;
+        }
+        return {packed, __float_as_uint(__half2float(__ushort_as_half(h)))};
+    }
+    __device__ __forceinline__ u32x8 q(const Prep& p, int, int, int b) const {
+        u32x8 r;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) r[k] = __builtin_amdgcn_readlane(p.packed, 8 * b + k);
+        return r;
+    }
+    __device__ __forceinline__ float d(const Prep& p, int, int, int b) const {
+        return __uint_as_float(__builtin_amdgcn_readlane(p.dbits, 8 * b));
+    }
+};
+
 // Adds chunk `c` (held in ch) of the lane's row into the chains pa / pb.
-template <int N>
+template <int N, class Act>
 __device__ __forceinline__ void chunk_fma(const MatDesc& m, int c, const Chunk& ch, float (&pa)[N],
-                                          float (&pb)[N]) {
+                                          float (&pb)[N], Act& act, int slot) {
+    const auto pr = act.prepare(slot, c);
 #pragma unroll
     for (int b = 0; b < kChunkBlocks; ++b) {
         // padding blocks of the last chunk have zero nibbles and scale; read a
@@ -97,20 +191,18 @@ __device__ __forceinline__ void chunk_fma(const MatDesc& m, int c, const Chunk& 
         const Unpacked u = unpack(ch.nib[b]);
 #pragma unroll
         for (int t = 0; t < N; ++t) {
-            const u32x8 q = act_q(m.xq, (int64_t)t * m.cols + (int64_t)blk * 32);
+            const u32x8 q = act.q(pr, t, blk, b);
             const int s16 = block_dot16(u, q);
-            const float dx = act_d(m.xd, (int64_t)t * m.dstride + blk);
+            const float dx = act.d(pr, t, blk, b);
             float& p = (b < kChunkBlocks / 2) ? pa[t] : pb[t];
             p = fmaf(dw16 * dx, (float)s16, p);
         }
     }
 }
 
-// One wave streams chunks [c0, c1) of row group g; lane = row.  Two chunks are
-// in flight per wave: the next chunk's loads are issued before the current
-// chunk is consumed.
-template <int N>
-__device__ __forceinline__ void wave_task(const MatDesc& m, int g, int c0, int c1, float (&acc)[N]) {
+// One wave streams chunks [c0, c1) of row group g; lane = row.
+template <int N, class Act>
+__device__ __forceinline__ void wave_task(const MatDesc& m, int g, int c0, int c1, float (&acc)[N], Act& act) {
     const int lane = threadIdx.x & 63;
     float pa[N], pb[N];
 #pragma unroll
@@ -131,23 +223,27 @@ __device__ __forceinline__ void wave_task(const MatDesc& m, int g, int c0, int c
     // prefetch makes the compiler wait for all loads, the prefetch included).
     Chunk a, b;
     load_chunk(a, wp);
+    act.load(0, c0);
     int c = c0;
     for (; c + 2 < c1; c += 2, wp += 2 * kChunkBytes) {
         load_chunk(b, wp + kChunkBytes);
-        chunk_fma<N>(m, c, a, pa, pb);
+        act.load(1, c + 1);
+        chunk_fma<N>(m, c, a, pa, pb, act, 0);
         seg_end(c);
         load_chunk(a, wp + 2 * kChunkBytes);
-        chunk_fma<N>(m, c + 1, b, pa, pb);
+        act.load(0, c + 2);
+        chunk_fma<N>(m, c + 1, b, pa, pb, act, 1);
         seg_end(c + 1);
     }
     if (c + 1 < c1) {  // two chunks left
         load_chunk(b, wp + kChunkBytes);
-        chunk_fma<N>(m, c, a, pa, pb);
+        act.load(1, c + 1);
+        chunk_fma<N>(m, c, a, pa, pb, act, 0);
         seg_end(c);
-        chunk_fma<N>(m, c + 1, b, pa, pb);
+        chunk_fma<N>(m, c + 1, b, pa, pb, act, 1);
         seg_end(c + 1);
     } else {           // one chunk left
-        chunk_fma<N>(m, c, a, pa, pb);
+        chunk_fma<N>(m, c, a, pa, pb, act, 0);
         seg_end(c);
     }
 }
@@ -298,7 +394,10 @@ __device__ __forceinline__ void run_tile_mfma(const MatDesc& m, int64_t gset, fl
 
 template <int N>
 __device__ __forceinline__ void run_tile(const MatDesc& m, int64_t gset, float* red) {
-    run_tile_with<N>(m, gset, red, [&](int g, int c0, int c1, float (&acc)[N]) { wave_task<N>(m, g, c0, c1, acc); });
+    run_tile_with<N>(m, gset, red, [&](int g, int c0, int c1, float (&acc)[N]) {
+        ActGlobal act{m};
+        wave_task<N>(m, g, c0, c1, acc, act);
+    });
 }
 
 template <int N>
@@ -386,26 +485,18 @@ __global__ __launch_bounds__(256) void k_repack(const uint8_t* __restrict__ w, u
 
 // ---------------------------------------------------------------- quantize
 
-// 8 consecutive lanes quantize one block, 4 values each: d = max|x| / 127
-// (correctly rounded fp32 division), q = roundf(x / d) (half away from zero),
-// d_x = binary16(d) rounded to nearest even.  All-zero blocks give d = 0, q = 0.
-// `valid` is uniform over the 8 lanes of a block.
+// One block per 8 lanes; `valid` is uniform over the 8 lanes of a block.
 __device__ __forceinline__ void quant_block8(const float* x, int8_t* q, uint16_t* d, bool valid) {
     const int o = threadIdx.x & 7;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     if (valid) v = *gp<f32x4>(x + 4 * o);
-    float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-#pragma unroll
-    for (int off = 1; off < 8; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 8));
+    const float a = quant8_amax(v);
     if (!valid) return;
-    const float dd = a / 127.0f;
-    uint32_t packed = 0;
-    if (a != 0.0f) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) packed |= ((uint32_t)(uint8_t)(int8_t)(int)roundf(v[k] / dd)) << (8 * k);
-    }
+    uint32_t packed;
+    uint16_t h;
+    quant8_codes(v, a, packed, h);
     *gwr<uint32_t>(q + 4 * o) = packed;
-    if (o == 0) *gwr<uint16_t>(d) = __half_as_ushort(__float2half_rn(dd));
+    if (o == 0) *gwr<uint16_t>(d) = h;
 }
 
 // Block lb (row-major over [n][nb]) of one activation; the lanes of a row's
@@ -437,6 +528,25 @@ __global__ __launch_bounds__(256) void k_quantize_batch(const QuantDesc* __restr
     const int64_t total = (int64_t)qd.n * (qd.cols / 32);
     const int64_t lb = (int64_t)b0 + (threadIdx.x >> 3);
     quant_local(qd, lb, lb < total);
+}
+
+// ---------------------------------------------------------------- fused 1-row sweep
+//
+// With one activation row the sweep quantizes inside the GEMV launch (the
+// pages' mega kernel quantizes the activation once per step inside its single
+// kernel, milestone M15): every wave quantizes the chunks it streams (see
+// ActQuant), so the bytes -- and the results -- equal those of a separate
+// quantize launch, and the group-0 waves publish them to x_q8.
+__global__ __launch_bounds__(kThreads, 1) void k_sweep_fused(const MatDesc* __restrict__ mats,
+                                                            const uint32_t* __restrict__ tiles) {
+    __shared__ float red[kWaves * 64];
+    const uint32_t mi = tiles[2 * (size_t)blockIdx.x];
+    const uint32_t gs = tiles[2 * (size_t)blockIdx.x + 1];
+    const MatDesc m = mats[mi];
+    run_tile_with<1>(m, gs, red, [&](int g, int c0, int c1, float (&acc)[1]) {
+        ActQuant act{m, g == 0, {}};
+        wave_task<1>(m, g, c0, c1, acc, act);
+    });
 }
 
 // ---------------------------------------------------------------- measurement
@@ -534,6 +644,13 @@ hipError_t launch_sweep(const MatDesc* dev_mats, const uint32_t* dev_tiles, int6
         case 8: sweep_n<8>(dev_mats, dev_tiles, n_tiles, st); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_sweep_fused(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles,
+                              hipStream_t st) {
+    if (n_tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_sweep_fused, dim3((unsigned)n_tiles), dim3(kThreads), 0, st, dev_mats, dev_tiles);
     return hipGetLastError();
 }
 

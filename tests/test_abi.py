@@ -124,8 +124,19 @@ def test_sweep_plan_host_side(L):
     assert d["weight_bytes"] == 868_257_792 == d["packed_bytes"]
     # group sets: q,o 6; k,v 1; gate,up 35; down 24 (4-way K split) per layer; lm_head 594
     assert d["n_tiles"] == 28 * (6 + 1 + 1 + 6 + 35 + 35 + 24) + 594
-    assert d["n_quant_blocks"] == 0 and d["dev_bytes"] == need
+    assert d["n_quant_blocks"] == 0 and d["dev_bytes"] == need and d["fused_quantize"] == 0
     assert d["out_bytes"] == 4 * sum(s.rows for s in shapes)
+    L.q4s_sweep_plan_destroy(plan)
+    # with fp32 activations at n = 1 the plan quantizes inside the GEMV launch
+    fx = base
+    mats_x = []
+    for (w, _, x, y, rows, cols) in mats:
+        mats_x.append((w, fx, x, y, rows, cols))
+        fx += (4 * cols + 4095) // 4096 * 4096
+    st, plan, _ = _plan(L, mats_x, 1)
+    assert st == 0, _err(L)
+    assert L.q4s_sweep_plan_info(plan, ctypes.byref(info)) == 0
+    assert info.fused_quantize == 1 and info.n_quant_blocks == sum(s.cols // 32 for s in shapes)
     L.q4s_sweep_plan_destroy(plan)
     # an output aliasing another matrix's input is rejected
     bad = list(mats)

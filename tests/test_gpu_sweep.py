@@ -62,6 +62,47 @@ def test_sweep_small_mixed_equals_standalone(oracle):
         assert (mats[5]["y"] == 0).all()
 
 
+def test_sweep_fused_quantize_equals_two_launches(oracle):
+    # n = 1 with every activation given as fp32: one launch whose waves quantize
+    # the chunks they stream; x_q8 and y equal the separate quantize + GEMV bit
+    # for bit (rows over 32768 columns and padded d_x rows included)
+    require_gpu()
+    shapes = [synth.MatShape("a", 257, 1536), synth.MatShape("b", 64, 8960), synth.MatShape("c", 1, 32),
+              synth.MatShape("d", 130, 4128), synth.MatShape("e", 90, 96), synth.MatShape("f", 70, 18944),
+              synth.MatShape("g", 3, 33792)]
+    _, hx, mats = _stack(78, shapes, 1)
+    for m in mats:
+        m["x_q8"].fill_(0xA5)                                # every byte must be written
+    sw = q.Sweep(mats, 1)
+    info = sw.info()
+    assert info["fused_quantize"] == 1
+    assert info["n_quant_blocks"] == sum(s.cols // 32 for s in shapes)
+    sw.run()
+    torch.cuda.synchronize()
+    for m, x in zip(mats, hx):
+        xq = q.quantize_q8_0(to_dev(x))
+        assert torch.equal(xq, m["x_q8"])                    # q, d_x and the zeroed padding
+        assert np.array_equal(q.q8_views(xq, 1, m["cols"])[0].cpu().numpy().view(np.uint8).reshape(-1),
+                              oracle.quantize_q8_0(x)[0, :, 2:].reshape(-1))
+        y = q.gemv_q4_0(m["w_packed"], xq, m["rows"], m["cols"], 1)
+        assert torch.equal(y, m["y"])
+
+
+def test_sweep_not_fused_with_a_prequantized_activation():
+    # a matrix without x reads its x_q8 as given: the plan keeps two launches
+    require_gpu()
+    shapes = [synth.MatShape("a", 65, 1536), synth.MatShape("b", 3, 2048)]
+    _, hx, mats = _stack(79, shapes, 1)
+    mats[1]["x_q8"] = q.quantize_q8_0(mats[1].pop("x"))
+    sw = q.Sweep(mats, 1)
+    assert sw.info()["fused_quantize"] == 0
+    sw.run()
+    torch.cuda.synchronize()
+    for m, x in zip(mats, hx):
+        y = q.gemv_q4_0(m["w_packed"], q.quantize_q8_0(to_dev(x)), m["rows"], m["cols"], 1)
+        assert torch.equal(y, m["y"])
+
+
 def test_qwen15_n1_full_parity(oracle, qwen15):
     hw, hx, mats = qwen15
     sw = q.Sweep(mats, 1)
