@@ -266,11 +266,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen2.5-1.5b", choices=["qwen2.5-1.5b", "qwen2.5-7b", "lm_head", "lm_head_q8"])
-    ap.add_argument("--n", type=int, default=1, help="activation rows per GEMV (1..8)")
+    ap.add_argument("--n", type=int, default=1, help="activation rows per GEMV (1..24; 1..8 for lm_head_q8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify-ratio", action="store_true", help="skip the N=8 / N=1 step-cost ratio")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--verify-n", default="8", help="comma list of row counts for the t(N)/t(1) ratios")
+    ap.add_argument("--verify-n", default="2,4,8,16,24",
+                    help="comma list of row counts for the step-cost curve t(N)/t(1)")
     ap.add_argument("--profile-only", action="store_true",
                     help="run a few GEMV-only sweeps plus a 1 GiB copy, for rocprofv3 counter runs")
     args = ap.parse_args()
@@ -278,8 +279,8 @@ def main() -> int:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU part; see DESIGN.md for how it would shard)", file=sys.stderr)
         return 2
-    if not 1 <= args.n <= 8:
-        raise SystemExit("--n must be in 1..8")
+    if not 1 <= args.n <= (8 if args.workload == "lm_head_q8" else 24):
+        raise SystemExit("--n must be in 1..24 (1..8 for lm_head_q8)")
 
     import torch
 

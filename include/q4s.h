@@ -14,7 +14,8 @@
  *     accumulated in fp32 ("How it works", mega.cu bullet; milestone M16);
  *   - a step carries up to 8 activation rows that share one pass over the
  *     weights (mega.cu bullet; milestone M16), with every row's result
- *     bit-identical to the same row computed alone;
+ *     bit-identical to the same row computed alone; here up to 24 rows share a
+ *     pass (prefill chunks and longer verifies, milestones M7 and M17);
  *   - a whole decode step's projections stream in one launch instead of one
  *     launch per matrix (Results paragraph on the roofline; milestone M15).
  *
@@ -30,7 +31,8 @@
  *   - A launch failure reported by the HIP runtime returns Q4S_ERR_HIP; faults
  *     inside a kernel surface at the caller's next stream synchronization.
  *   - A pointer may be NULL only when the buffer it names has 0 bytes.
- *   - Shapes: rows >= 0, cols >= 0 with cols % 32 == 0, n in 0..8, and
+ *   - Shapes: rows >= 0, cols >= 0 with cols % 32 == 0, n in 0..24 (Q4_0
+ *     weights; 0..8 for Q8_0 weights), and
  *     rows, cols < 2^31.  rows == 0 or n == 0 is a no-op; cols == 0 writes
  *     y = 0 (the empty sum).
  *
@@ -85,7 +87,8 @@ extern "C" {
 #endif
 
 #define Q4S_ABI_VERSION 2
-#define Q4S_MAX_N 8
+#define Q4S_MAX_N 24   /* activation rows per Q4_0 product (one weight pass) */
+#define Q4S_MAX_N_Q8 8 /* activation rows per Q8_0-weight product */
 
 typedef enum {
     Q4S_OK = 0,
@@ -146,7 +149,9 @@ q4s_status q4s_quantize_q8_0(const float* x, void* x_q8, int n, int64_t cols, vo
  * y[t][r] = sum_b d_w[r][b] * d_x[t][b] * s[t][r][b] for t < n, r < rows.
  * w_packed: packed Q4_0 (16-byte aligned); x_q8: planar Q8_0 of n rows
  * (16-byte aligned); y: fp32 [n][rows] (4-byte aligned), must not overlap
- * either input.  n in 0..8.  Needs no workspace.
+ * either input.  n in 0..24: every row shares one pass over the weights (n = 1
+ * on v_dot4, 2..8 in one MFMA token tile, 9..24 in two or three); longer
+ * prefill chunks are split by the caller.  Needs no workspace.
  * Source: cuda_infer and mega.cu bullets of "How it works"; milestones M9,
  * M15, M16.
  */
@@ -202,7 +207,7 @@ q4s_status q4s_repack_q8_0(const void* w_q8_0, void* w_packed, int64_t rows, int
  * y[t][r] = sum_b d_w[r][b] * d_x[t][b] * sum_j w_{r,b,j} q_{t,b,j} for t < n,
  * r < rows.  w_packed: packed Q8_0 (16-byte aligned); x_q8: planar Q8_0
  * activation of n rows (16-byte aligned); y: fp32 [n][rows], must not overlap
- * either input.  n in 0..8.  Needs no workspace.  Source: milestone M6 and the
+ * either input.  n in 0..8 (Q4S_MAX_N_Q8).  Needs no workspace.  Source: milestone M6 and the
  * gemv_q8_dp4a bullet of "How it works".
  */
 q4s_status q4s_gemv_q8_0(const void* w_packed, const void* x_q8, float* y, int64_t rows,
@@ -261,7 +266,7 @@ typedef struct {
 } q4s_plan_info;
 
 /*
- * Build a plan for n activation rows (1..8) over n_mats matrices (the table is
+ * Build a plan for n activation rows (1..24) over n_mats matrices (the table is
  * copied; the buffers it names must stay valid for every run).  Every matrix
  * is checked as in q4s_gemv_q4_0 (a matrix with x is quantized even when
  * rows == 0).  No y may overlap any w_packed, x_q8 or x of the sweep, and no

@@ -16,7 +16,8 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libq4stream.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "q4s.h")
-MAX_N = 8
+MAX_N = 24
+MAX_N_Q8 = 8
 
 _lib = None
 

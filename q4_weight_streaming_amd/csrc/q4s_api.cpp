@@ -46,11 +46,11 @@ constexpr int64_t kMaxDim = (int64_t)1 << 31;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-q4s_status check_shape(int64_t rows, int64_t cols, int n) {
+q4s_status check_shape(int64_t rows, int64_t cols, int n, int max_n = Q4S_MAX_N) {
     if (rows < 0 || rows >= kMaxDim) return fail(Q4S_ERR_SHAPE, "rows=%lld out of [0, 2^31)", (long long)rows);
     if (cols < 0 || cols >= kMaxDim || cols % 32 != 0)
         return fail(Q4S_ERR_SHAPE, "cols=%lld must be a multiple of 32 in [0, 2^31)", (long long)cols);
-    if (n < 0 || n > Q4S_MAX_N) return fail(Q4S_ERR_SHAPE, "n=%d out of [0, %d]", n, Q4S_MAX_N);
+    if (n < 0 || n > max_n) return fail(Q4S_ERR_SHAPE, "n=%d out of [0, %d]", n, max_n);
     return Q4S_OK;
 }
 
@@ -94,7 +94,7 @@ MatDesc make_desc(const void* w, const void* xq8, float* y, int64_t rows, int64_
     m.C = (int32_t)chunks_of(cols);
     m.ks = choose_ksplit(m.C);
     m.dstride = (int32_t)dstride_of(cols);
-    m.pad_ = 0;
+    m.n = n;
     m.x = nullptr;
     return m;
 }
@@ -102,7 +102,7 @@ MatDesc make_desc(const void* w, const void* xq8, float* y, int64_t rows, int64_
 // validation shared by the GEMVs and each sweep matrix
 q4s_status check_gemv(const void* w, const void* xq8, const float* y, int64_t rows, int64_t cols,
                       int n, bool q8w = false) {
-    q4s_status s = check_shape(rows, cols, n);
+    q4s_status s = check_shape(rows, cols, n, q8w ? Q4S_MAX_N_Q8 : Q4S_MAX_N);
     if (s) return s;
     const bool live = rows > 0 && n > 0;
     const size_t wb = live ? (q8w ? packed_q8_bytes(rows, cols) : packed_bytes(rows, cols)) : 0;
@@ -203,7 +203,7 @@ namespace {
 
 q4s_status block_sums_any(const void* w_packed, const void* x_q8, int32_t* sums, int64_t rows, int64_t cols,
                           int n, void* stream, bool q8w) {
-    q4s_status s = check_shape(rows, cols, n);
+    q4s_status s = check_shape(rows, cols, n, q8w ? Q4S_MAX_N_Q8 : Q4S_MAX_N);
     if (s) return s;
     const bool live = rows > 0 && n > 0 && cols > 0;
     const size_t wb = live ? (q8w ? packed_q8_bytes(rows, cols) : packed_bytes(rows, cols)) : 0;

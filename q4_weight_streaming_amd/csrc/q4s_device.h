@@ -95,10 +95,11 @@ __device__ __forceinline__ void load_act(ActRaw& a, const MatDesc& m, int c) {
     const int j = lane & 15;
     const int blk = min(c * kChunkBlocks + (j >> 1), m.nb - 1);  // valid block for padding pieces
     const int64_t off = (int64_t)blk * 32 + (j & 1) * 16;
-    a.q0 = *gp<u32x4>(m.xq + (int64_t)min(lane >> 4, N - 1) * m.cols + off);
-    a.q1 = *gp<u32x4>(m.xq + (int64_t)min(4 + (lane >> 4), N - 1) * m.cols + off);
+    const int last = min(N, m.n) - 1;  // token slots past the rows repeat the last row
+    a.q0 = *gp<u32x4>(m.xq + (int64_t)min(lane >> 4, last) * m.cols + off);
+    a.q1 = *gp<u32x4>(m.xq + (int64_t)min(4 + (lane >> 4), last) * m.cols + off);
     // d_x rows are padded to a multiple of 8 entries (zero past the last block)
-    a.dxh = *gp<uint16_t>(m.xd + (int64_t)min(lane >> 3, N - 1) * m.dstride + c * kChunkBlocks + (lane & 7));
+    a.dxh = *gp<uint16_t>(m.xd + (int64_t)min(lane >> 3, last) * m.dstride + c * kChunkBlocks + (lane & 7));
 }
 
 // Per-workgroup LDS of the GEMV kernels: the split reduction buffer and, for
@@ -145,7 +146,7 @@ __device__ __forceinline__ void run_tile_mfma_with(const MatDesc& m, int64_t gse
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int tok = 4 * lg + r;
-            if (tok < N && row < m.rows) gwr<float>(m.y)[(int64_t)tok * m.rows + row] = acc[mt * 4 + r];
+            if (tok < min(N, m.n) && row < m.rows) gwr<float>(m.y)[(int64_t)tok * m.rows + row] = acc[mt * 4 + r];
         }
     }
 }

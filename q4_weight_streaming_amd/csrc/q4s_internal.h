@@ -20,7 +20,9 @@ constexpr int kChunkNibBytes = kChunkBlocks * kGroupRows * kBlockNibBytes;  // 8
 constexpr int kChunkBytes = kChunkNibBytes + kGroupRows * kChunkBlocks * 2;   // 9216
 constexpr int kWaves = 4;                 // wavefronts per workgroup
 constexpr int kThreads = kWaves * 64;     // workgroup size
-constexpr int kMaxN = 8;                  // activation rows per call
+constexpr int kMaxN = 24;                 // activation rows per call (Q4_0 weights)
+constexpr int kMaxNQ8 = 8;                // activation rows per call (Q8_0 weights)
+constexpr int kTokTile = 8;               // activation rows per MFMA token tile
 
 // Packed Q8_0 geometry.  Same 64-row groups and 8-block chunks; a chunk is
 // stored as two pieces of 4 blocks.  Per piece: the int8 values
@@ -45,7 +47,7 @@ struct MatDesc {
     int32_t rows, cols;
     int32_t nb, G, C, ks; // blocks per row, row groups, chunks, K splits (1, 2 or 4)
     int32_t dstride;      // d_x row stride: nb rounded up to a multiple of 8
-    int32_t pad_;
+    int32_t n;            // activation rows
 };
 
 // One activation of a batched Q8_0 quantization.

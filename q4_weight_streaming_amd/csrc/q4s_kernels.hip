@@ -270,20 +270,23 @@ __device__ __forceinline__ void wave_task(const MatDesc& m, int g, int c0, int c
 // written in A-operand order; the d_x and d_w scales are converted to fp32
 // once per chunk on the way in.
 
-__device__ __forceinline__ void stage_act(const ActRaw& a, WaveLds& L) {
+// q: the slice's 16-byte A-operand slots; dx: its d_x/16 [token][block] fp32
+__device__ __forceinline__ void stage_act_to(const ActRaw& a, u32x4* q, float* dx) {
     const int lane = threadIdx.x & 63;
     const int j = lane & 15, b = j >> 1, e = j & 1;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int t = (lane >> 4) + 4 * k;
         const u32x4 v = k ? a.q1 : a.q0;
-        u32x2* s0 = (u32x2*)&L.q[(t * 8 + b) * 2 + 0];
-        u32x2* s1 = (u32x2*)&L.q[(t * 8 + b) * 2 + 1];
+        u32x2* s0 = (u32x2*)&q[(t * 8 + b) * 2 + 0];
+        u32x2* s1 = (u32x2*)&q[(t * 8 + b) * 2 + 1];
         s0[e] = (u32x2){v[0], v[1]};
         s1[e] = (u32x2){v[2], v[3]};
     }
-    ((float*)L.dx)[lane] = __half2float(__ushort_as_half((uint16_t)a.dxh)) * 0.0625f;
+    dx[lane] = __half2float(__ushort_as_half((uint16_t)a.dxh)) * 0.0625f;
 }
+
+__device__ __forceinline__ void stage_act(const ActRaw& a, WaveLds& L) { stage_act_to(a, L.q, (float*)L.dx); }
 
 template <int N>
 __device__ __forceinline__ void chunk_mfma(Chunk& ch, const ActRaw& ar, float (&part)[16], WaveLds& L) {
@@ -427,6 +430,54 @@ __global__ __launch_bounds__(kThreads, N == 1 ? 1 : 2) void k_sweep(const MatDes
     const MatDesc m = mats[mi];
     run_any<N>(m, gs, l);
 }
+
+// ---------------------------------------------------------------- tiled steps (9..24 rows)
+//
+// A step of n > 8 rows as token tiles of 8 on separate workgroups, each
+// running the 8-row kernel on its rows (so every row is bit-identical to the
+// 1-row result).  The tiles of one unit (group set, or sweep table entry) get
+// block indices 8 apart: the dispatcher deals workgroups to the 8 XCDs in
+// turn, so they land on the same XCD at about the same time and the later
+// tiles read the weights from its L2 instead of HBM.
+__device__ __forceinline__ bool tiled_unit(int tt, int64_t n_units, int64_t& unit, int& tile) {
+    const int64_t i = blockIdx.x, x = i & 7, s = i >> 3;
+    unit = (s / tt) * 8 + x;
+    tile = (int)(s % tt);
+    return unit < n_units;
+}
+
+__device__ __forceinline__ MatDesc token_tile(const MatDesc& m, int tile) {
+    MatDesc t = m;
+    const int t0 = kTokTile * tile;
+    t.xq = m.xq + (int64_t)t0 * m.cols;
+    t.xd = m.xd + (int64_t)t0 * m.dstride;
+    t.y = m.y + (int64_t)t0 * m.rows;
+    t.n = min(kTokTile, m.n - t0);
+    return t;
+}
+
+__global__ __launch_bounds__(kThreads, 2) void k_gemv_tiled(MatDesc m, int tt, int64_t n_gsets) {
+    __shared__ TileLds<kTokTile> l;
+    int64_t gset;
+    int tile;
+    if (!tiled_unit(tt, n_gsets, gset, tile)) return;
+    run_tile_mfma<kTokTile>(token_tile(m, tile), gset, l.red, l.wl);
+}
+
+__global__ __launch_bounds__(kThreads, 2) void k_sweep_tiled(const MatDesc* __restrict__ mats,
+                                                            const uint32_t* __restrict__ tiles, int tt,
+                                                            int64_t n_entries) {
+    __shared__ TileLds<kTokTile> l;
+    int64_t e;
+    int tile;
+    if (!tiled_unit(tt, n_entries, e, tile)) return;
+    const uint32_t mi = tiles[2 * (size_t)e];
+    const uint32_t gs = tiles[2 * (size_t)e + 1];
+    run_tile_mfma<kTokTile>(token_tile(mats[mi], tile), gs, l.red, l.wl);
+}
+
+// grid of a tiled launch: 8 * tt * ceil(units / 8)
+inline unsigned tiled_grid(int tt, int64_t units) { return (unsigned)(8 * tt * ((units + 7) / 8)); }
 
 // Test hook: the exact per-block sums, from the same loads, unpack and dot.
 template <int N>
@@ -611,6 +662,11 @@ static void gemv_n(const MatDesc& m, int64_t n_gsets, hipStream_t st) {
 
 hipError_t launch_gemv(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st) {
     if (n_gsets == 0 || n == 0) return hipSuccess;
+    if (n > kTokTile) {
+        const int tt = (n + kTokTile - 1) / kTokTile;
+        hipLaunchKernelGGL(k_gemv_tiled, dim3(tiled_grid(tt, n_gsets)), dim3(kThreads), 0, st, m, tt, n_gsets);
+        return hipGetLastError();
+    }
     switch (n) {
         case 1: gemv_n<1>(m, n_gsets, st); break;
         case 2: gemv_n<2>(m, n_gsets, st); break;
@@ -633,6 +689,12 @@ static void sweep_n(const MatDesc* mats, const uint32_t* tiles, int64_t n_tiles,
 hipError_t launch_sweep(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles, int n,
                         hipStream_t st) {
     if (n_tiles == 0 || n == 0) return hipSuccess;
+    if (n > kTokTile) {
+        const int tt = (n + kTokTile - 1) / kTokTile;
+        hipLaunchKernelGGL(k_sweep_tiled, dim3(tiled_grid(tt, n_tiles)), dim3(kThreads), 0, st, dev_mats, dev_tiles,
+                           tt, n_tiles);
+        return hipGetLastError();
+    }
     switch (n) {
         case 1: sweep_n<1>(dev_mats, dev_tiles, n_tiles, st); break;
         case 2: sweep_n<2>(dev_mats, dev_tiles, n_tiles, st); break;
@@ -662,6 +724,18 @@ static void sums_n(const MatDesc& m, int32_t* s, hipStream_t st) {
 
 hipError_t launch_block_sums(const MatDesc& m, int n, int32_t* s, hipStream_t st) {
     if (m.G == 0 || n == 0 || m.nb == 0) return hipSuccess;
+    if (n > kTokTile) {  // slices of up to 8 rows
+        for (int t0 = 0; t0 < n; t0 += kTokTile) {
+            MatDesc ms = m;
+            ms.xq = m.xq + (int64_t)t0 * m.cols;
+            ms.xd = m.xd + (int64_t)t0 * m.dstride;
+            const int k = min(kTokTile, n - t0);
+            ms.n = k;
+            const hipError_t e = launch_block_sums(ms, k, s + (int64_t)t0 * m.rows * m.nb, st);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     switch (n) {
         case 1: sums_n<1>(m, s, st); break;
         case 2: sums_n<2>(m, s, st); break;

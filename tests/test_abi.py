@@ -40,7 +40,8 @@ def test_sizes():
     assert q.q8_bytes(8, 8960) == 8 * 8960 * 34 // 32
     assert q.q8_bytes(1, 32) == 32 + 16                    # d_x row padded to 8 entries
     assert q.q8_bytes(3, 288) == 3 * 288 + 3 * 16 * 2
-    assert q.packed_bytes(3, 33) == 0 and q.q8_bytes(9, 32) == 0 and q.q4_0_bytes(-1, 32) == 0
+    assert q.packed_bytes(3, 33) == 0 and q.q8_bytes(25, 32) == 0 and q.q4_0_bytes(-1, 32) == 0
+    assert q.q8_bytes(24, 1536) == 24 * 1536 * 34 // 32
     # Q8_0 weights: the 8-bit lm_head of milestone M14 is 248 MB at 151936 x 1536
     assert q.q8_0_bytes(151936, 1536) == 247_959_552
     assert q.packed_q8_0_bytes(151936, 1536) == 247_959_552   # no padding at config shapes
@@ -57,7 +58,7 @@ def test_gemv_validation(L):
     g = L.q4s_gemv_q4_0
     assert g(FAKE, FAKE, FAKE + (1 << 30), 64, 33, 1, None) == 2        # cols % 32
     assert "cols" in _err(L)
-    assert g(FAKE, FAKE, FAKE + (1 << 30), 64, 64, 9, None) == 2        # n > 8
+    assert g(FAKE, FAKE, FAKE + (1 << 30), 64, 64, 25, None) == 2       # n > 24
     assert g(FAKE, FAKE, FAKE + (1 << 30), -1, 64, 1, None) == 2
     assert g(None, FAKE, FAKE + (1 << 30), 64, 64, 1, None) == 1        # null weights
     assert g(FAKE + 8, FAKE, FAKE + (1 << 30), 64, 64, 1, None) == 3    # misaligned
@@ -86,6 +87,7 @@ def test_other_entry_points_validate(L):
     # Q8_0 weights
     g = L.q4s_gemv_q8_0
     assert g(FAKE, FAKE, FAKE + (1 << 30), 64, 33, 1, None) == 2
+    assert g(FAKE, FAKE, FAKE + (1 << 30), 64, 64, 9, None) == 2        # n > 8 for Q8_0 weights
     assert g(FAKE + 8, FAKE, FAKE + (1 << 30), 64, 64, 1, None) == 3
     assert g(FAKE, FAKE + (1 << 20), FAKE + 17408 - 4, 64, 64, 1, None) == 4   # y overlaps packed Q8_0
     assert g(None, None, None, 0, 64, 1, None) == 0
@@ -143,7 +145,7 @@ def test_sweep_plan_host_side(L):
     bad[1] = (mats[1][0], None, mats[1][2], mats[0][0], mats[1][4], mats[1][5])
     st, plan, _ = _plan(L, bad, 1)
     assert st == 4 and not plan.value
-    st, plan, _ = _plan(L, mats[:3], 9)
+    st, plan, _ = _plan(L, mats[:3], 25)
     assert st == 2
     st, plan, _ = _plan(L, [(FAKE, None, FAKE + 8, FAKE + (1 << 30), 64, 64)], 1)
     assert st == 3 and "matrix 0" in _err(L)

@@ -98,6 +98,14 @@ def test_block_sums_bit_exact(oracle, rows, cols, n):
     assert np.array_equal(got, ref)
 
 
+def test_block_sums_wide_bit_exact(oracle):
+    rows, cols, n = 130, 4128, 24
+    w, x = _inputs(rows, cols, n, tag=3)
+    xq = q.quantize_q8_0(to_dev(x))
+    got = q.block_sums(packed_weights(w, rows, cols), xq, rows, cols, n).cpu().numpy()
+    assert np.array_equal(got, oracle.block_sums(w, oracle.quantize_q8_0(x), rows, cols, n))
+
+
 def test_block_sums_extremes(oracle):
     # all nibbles 0 against q = -127 gives +32512 per block, the largest |s|
     rows, cols = 64, 256
@@ -138,6 +146,36 @@ def test_gemv_n_invariance_and_determinism(rows, cols):
         assert torch.equal(y1[0], y8[t])
 
 
+WIDE_SHAPES = [(1536, 1536), (256, 1536), (1536, 8960), (63, 288), (65, 64), (257, 1536), (130, 4128),
+               (70, 96)]
+
+
+@pytest.mark.parametrize("rows,cols", WIDE_SHAPES)
+@pytest.mark.parametrize("n", [9, 16, 17, 24])
+def test_gemv_wide_parity(oracle, rows, cols, n):
+    # 9..24 activation rows in one weight pass (token tiles of 8)
+    w, x = _inputs(rows, cols, n, tag=4)
+    wp = packed_weights(w, rows, cols)
+    y = q.gemv_q4_0(wp, q.quantize_q8_0(to_dev(x)), rows, cols, n).cpu().numpy()
+    y_ref, S = oracle.gemv(w, oracle.quantize_q8_0(x), rows, cols, n)
+    assert_within(y, y_ref, S, what=f"{rows}x{cols} n={n}")
+
+
+@pytest.mark.parametrize("rows,cols", [(257, 1536), (130, 4128), (1536, 8960), (70, 96)])
+def test_gemv_wide_rows_equal_one_row(rows, cols):
+    # every row of a 9..24-row call equals the 1-row call on that activation, bit for bit
+    w, x = _inputs(rows, cols, 24, tag=5)
+    wp = packed_weights(w, rows, cols)
+    y24 = q.gemv_q4_0(wp, q.quantize_q8_0(to_dev(x)), rows, cols, 24)
+    assert torch.equal(y24, q.gemv_q4_0(wp, q.quantize_q8_0(to_dev(x)), rows, cols, 24))
+    for n in (9, 12, 16, 17, 23):
+        yn = q.gemv_q4_0(wp, q.quantize_q8_0(to_dev(x[:n])), rows, cols, n)
+        assert torch.equal(yn, y24[:n])
+    for t in range(24):
+        y1 = q.gemv_q4_0(wp, q.quantize_q8_0(to_dev(x[t:t + 1])), rows, cols, 1)
+        assert torch.equal(y1[0], y24[t]), t
+
+
 def test_gemv_closed_forms():
     rows, cols = 200, 2560
     w, x = _inputs(rows, cols, 2)
@@ -159,5 +197,8 @@ def test_gemv_empty_and_zero_width():
     xq = torch.empty(0, dtype=torch.uint8, device=dev())
     y = torch.full((3, 40), 7.0, device=dev())
     q.gemv_q4_0(wp, xq, 40, 0, 3, out=y)                       # K = 0: the empty sum
+    assert (y == 0).all()
+    y = torch.full((20, 40), 7.0, device=dev())
+    q.gemv_q4_0(wp, xq, 40, 0, 20, out=y)                      # and on the wide path
     assert (y == 0).all()
     q.gemv_q4_0(wp, xq, 0, 64, 1, out=torch.empty((1, 0), device=dev()))   # no rows: no-op

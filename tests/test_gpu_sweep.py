@@ -47,7 +47,7 @@ def test_sweep_small_mixed_equals_standalone(oracle):
     require_gpu()
     shapes = [synth.MatShape("a", 257, 1536), synth.MatShape("b", 64, 8960), synth.MatShape("c", 1, 32),
               synth.MatShape("d", 130, 4128), synth.MatShape("e", 0, 64), synth.MatShape("f", 90, 0)]
-    for n in (1, 4, 8):
+    for n in (1, 4, 8, 16, 24):
         _, hx, mats = _stack(77, shapes, n)
         sw = q.Sweep(mats, n)
         sw.run()
@@ -125,10 +125,10 @@ def test_qwen15_n1_full_parity(oracle, qwen15):
         assert torch.equal(y, m["y"])
 
 
-def test_qwen15_n8_verify(oracle, qwen15):
+@pytest.mark.parametrize("n", [8, 24])
+def test_qwen15_multi_row_verify(oracle, qwen15, n):
     hw, _, mats1 = qwen15
     shapes = synth.qwen25_1p5b()
-    n = 8
     mats8, hx8 = [], []
     for mi, (s, m1) in enumerate(zip(shapes, mats1)):
         x = synth.activation(n, s.cols, synth.generator(3, mi, 0, 1))
@@ -145,8 +145,8 @@ def test_qwen15_n8_verify(oracle, qwen15):
         idx = np.unique(np.concatenate([rng.integers(0, s.rows, 48), [0, s.rows - 1]]))
         y_ref, S = oracle.gemv_rows(hw[i], oracle.quantize_q8_0(hx8[i]), s.cols, n, idx)
         assert_within(mats8[i]["y"].cpu().numpy()[:, idx], y_ref, S, what=f"matrix {i}")
-    # each row of the 8-row sweep equals the 1-row sweep of that activation
-    for t in (0, 5):
+    # each row of the n-row sweep equals the 1-row sweep of that activation
+    for t in (0, 5, n - 1):
         mats_t = [{"w_packed": m["w_packed"], "x": m["x"][t:t + 1].contiguous(),
                    "x_q8": torch.empty(q.q8_bytes(1, m["cols"]), dtype=torch.uint8, device=dev()),
                    "y": torch.empty((1, m["rows"]), dtype=torch.float32, device=dev()),
