@@ -65,6 +65,7 @@ def _bind(path: str):
     L.q4o_q8w_gemv.argtypes = [p, p, i64, i64, ctypes.c_int, p, p, p]
     L.q4o_requant_block_q8_0_to_q4_0.argtypes = [p, p]
     L.q4o_requant_q8_0_to_q4_0.argtypes = [p, p, i64]
+    L.q4o_attn_decode.argtypes = [p, p, p, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, p, p]
     L.q4o_set_threads.argtypes = [ctypes.c_int]
     L.q4o_max_threads.restype = ctypes.c_int
     return L
@@ -250,3 +251,22 @@ def requant_q8_0_to_q4_0(w_q8: np.ndarray) -> np.ndarray:
     out = np.empty(a.shape[:-1] + (Q4_BLOCK_BYTES,), np.uint8)
     lib().q4o_requant_q8_0_to_q4_0(_ptr(a), _ptr(out), nblk)
     return out
+
+
+# ---------------------------------------------------------------- attention
+
+def attn_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float | None = None):
+    """Decode attention in fp64: q [n_q][hd], k and v [L][n_kv][hd] (fp32).
+    Returns (o [n_q][hd] fp64, o_abs [n_q][hd] fp64 = sum_j p_hj |v_j|)."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    n_q, hd = q.shape
+    L, n_kv, hd2 = k.shape
+    assert hd2 == hd and v.shape == k.shape and n_q % n_kv == 0
+    if scale is None:
+        scale = 1.0 / np.sqrt(hd)
+    o = np.empty((n_q, hd), np.float64)
+    o_abs = np.empty((n_q, hd), np.float64)
+    lib().q4o_attn_decode(_ptr(q), _ptr(k), _ptr(v), L, n_q, n_kv, hd, float(scale), _ptr(o), _ptr(o_abs))
+    return o, o_abs

@@ -19,6 +19,8 @@
  *     the lm_head stored as Q8_0 weights (34 B blocks of 32 int8 values and a
  *     binary16 scale), multiplied by the same int8 activations.
  *   - Milestones M14 and M18: 8-bit heads requantized to Q4_0 at load.
+ *   - Milestones M5, M12 and M15, and the model details (12 query heads over
+ *     2 key/value heads of dimension 128): decode attention over a KV cache.
  *
  * Block formats (GGUF convention, where the pages leave the byte order open):
  *   Q4_0 (18 B / 32 weights): fp16 scale d (little-endian), then 16 bytes qs.
@@ -367,6 +369,60 @@ void q4o_requant_q8_0_to_q4_0(const uint8_t* w_q8, uint8_t* w_q4, int64_t n_bloc
 #pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < n_blocks; ++b)
         q4o_requant_block_q8_0_to_q4_0(w_q8 + b * Q8_BLOCK_BYTES, w_q4 + b * Q4_BLOCK_BYTES);
+}
+
+/* ------------------------------------------------------------------ */
+/* Decode attention over a KV cache (milestones M5, M12, M15; model     */
+/* details: 12 query heads share 2 key/value heads, head dim 128).      */
+/* One new query per head attends to all L cached positions:            */
+/*   s_hj = scale * sum_i q[h][i] * k[j][g][i],  g = h / (n_q / n_kv)  */
+/*   p_hj = exp(s_hj - max_j s_hj) / sum_j exp(s_hj - max_j s_hj)      */
+/*   o[h][i] = sum_j p_hj * v[j][g][i]                                  */
+/* all in fp64; o_abs[h][i] = sum_j p_hj * |v[j][g][i]| (tolerance).    */
+/* k, v: fp32 [L][n_kv][hd] (token-major); q, o: [n_q][hd].            */
+/* ------------------------------------------------------------------ */
+
+void q4o_attn_decode(const float* q, const float* k, const float* v, int64_t L, int n_q, int n_kv, int hd,
+                     double scale, double* o, double* o_abs)
+{
+    int group = n_q / n_kv;
+#pragma omp parallel for schedule(static)
+    for (int h = 0; h < n_q; ++h) {
+        int g = h / group;
+        double smax = -INFINITY;
+        for (int64_t j = 0; j < L; ++j) {
+            double dot = 0.0;
+            for (int i = 0; i < hd; ++i)
+                dot += (double)q[h * hd + i] * (double)k[(j * n_kv + g) * hd + i];
+            double sc = scale * dot;
+            if (sc > smax)
+                smax = sc;
+        }
+        double denom = 0.0;
+        for (int64_t j = 0; j < L; ++j) {
+            double dot = 0.0;
+            for (int i = 0; i < hd; ++i)
+                dot += (double)q[h * hd + i] * (double)k[(j * n_kv + g) * hd + i];
+            denom += exp(scale * dot - smax);
+        }
+        for (int i = 0; i < hd; ++i) {
+            o[h * hd + i] = 0.0;
+            if (o_abs)
+                o_abs[h * hd + i] = 0.0;
+        }
+        for (int64_t j = 0; j < L; ++j) {
+            double dot = 0.0;
+            for (int i = 0; i < hd; ++i)
+                dot += (double)q[h * hd + i] * (double)k[(j * n_kv + g) * hd + i];
+            double p = exp(scale * dot - smax) / denom;
+            for (int i = 0; i < hd; ++i) {
+                double vv = (double)v[(j * n_kv + g) * hd + i];
+                o[h * hd + i] += p * vv;
+                if (o_abs)
+                    o_abs[h * hd + i] += p * fabs(vv);
+            }
+        }
+    }
 }
 
 void q4o_set_threads(int nthreads)

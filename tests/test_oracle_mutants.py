@@ -12,6 +12,7 @@ import test_oracle_fp16 as t16
 import test_oracle_q4 as t4
 import test_oracle_q8 as t8
 import test_oracle_q8w as t8w
+import test_oracle_attn as tat
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
                    "q4_oracle.c")
@@ -57,6 +58,10 @@ MUTANTS = [
     ("requant_no_clamp", "nib[j] = n > 15 ? 15 : n;", "nib[j] = n & 15;"),
     ("requant_halves_swapped", "(uint8_t)(nib[j] | (nib[j + 16] << 4));",
      "(uint8_t)(nib[j + 16] | (nib[j] << 4));"),
+    ("attn_group_modulo", "int g = h / group;", "int g = h % n_kv;"),
+    ("attn_no_max_subtraction", "denom += exp(scale * dot - smax);", "denom += exp(scale * dot);"),
+    ("attn_scale_dropped", "double sc = scale * dot;", "double sc = dot;"),
+    ("attn_unnormalized", "double p = exp(scale * dot - smax) / denom;", "double p = exp(scale * dot - smax);"),
 ]
 
 
@@ -78,7 +83,14 @@ def _pins(o, b):
               ("q8w_brute", lambda: t8w.test_q8w_gemv_matches_fp64_bruteforce(o, b, 17, 288, 8)),
               ("q8w_unit", lambda: t8w.test_q8w_gemv_unit_weights_closed_form(o)),
               ("requant_round_trip", lambda: t8w.test_requant_round_trips_q4_0_blocks(o)),
-              ("requant_nearest", lambda: t8w.test_requant_rounds_to_nearest_level(o))]
+              ("requant_nearest", lambda: t8w.test_requant_rounds_to_nearest_level(o)),
+              ("attn_golden", lambda: tat.test_attn_golden(o)),
+              ("attn_one_position", lambda: tat.test_attn_single_position_returns_v(o)),
+              ("attn_equal_keys", lambda: tat.test_attn_equal_keys_average_values(o)),
+              ("attn_dominant", lambda: tat.test_attn_one_dominant_key_closed_form(o)),
+              ("attn_large", lambda: tat.test_attn_large_scores_stay_finite(o)),
+              ("attn_gqa", lambda: tat.test_attn_gqa_groups(o)),
+              ("attn_brute", lambda: tat.test_attn_matches_bruteforce(o, 7, 12, 2, 128))]
     checks += [(f"q8_golden_{c['name']}", (lambda c=c: t8.test_q8_0_golden_blocks(o, c)))
                for c in t8.CASES]
     checks += [(f"q4_golden_{c['name']}", (lambda c=c: t4.test_q4_0_golden_decode(o, c)))
