@@ -260,12 +260,91 @@ def run_q8_head(args, dev, stream) -> int:
     return 0
 
 
+def run_attn(args, dev, stream) -> int:
+    """Decode attention of one layer of the 1.5B model (12 query / 2 kv heads, head dim 128) at
+    the 32768-position context, over 8 rotated seeded KV caches (512 MB, beyond every cache)."""
+    import numpy as np
+    import torch
+
+    from q4_weight_streaming_amd import _lib as q
+    L, n_q, n_kv, ncopies = args.context, 12, 2, 8
+    if L % 64:
+        raise SystemExit("--context must be a multiple of 64")
+    log(f"generating {ncopies} KV caches, L={L}")
+    copies, host0 = [], None
+    for c in range(ncopies):
+        rng = np.random.default_rng([2026, 9, c])
+        qv = rng.standard_normal((n_q, 128), dtype=np.float32)
+        k = rng.standard_normal((L, n_kv, 128), dtype=np.float32)
+        v = rng.standard_normal((L, n_kv, 128), dtype=np.float32)
+        # the cache layouts the kernel reads: keys [kv][L/64][128][64], values [kv][L][128]
+        kb = np.ascontiguousarray(k.transpose(1, 0, 2).reshape(n_kv, L // 64, 64, 128).transpose(0, 1, 3, 2))
+        vh = np.ascontiguousarray(v.transpose(1, 0, 2))
+        copies.append({"q": torch.from_numpy(qv).to(dev), "kb": torch.from_numpy(kb).to(dev),
+                       "v": torch.from_numpy(vh).to(dev),
+                       "o": torch.empty((n_q, 128), dtype=torch.float32, device=dev),
+                       "ws": torch.empty(q.attn_workspace_bytes(n_q, L), dtype=torch.uint8, device=dev)})
+        if c == 0 and not args.no_cpu_baseline:
+            host0 = (qv, k, v)
+    torch.cuda.synchronize()
+    kv_bytes = 2 * L * n_kv * 128 * 4
+    launch_bytes = kv_bytes + 2 * n_q * 128 * 4
+
+    def step(c):
+        return lambda: q.attn_decode(c["q"], c["kb"], c["v"], L, workspace=c["ws"], out=c["o"])
+
+    if args.profile_only:
+        for i in range(10):
+            step(copies[i % ncopies])()
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        q.bench_copy(src, dst)
+        torch.cuda.synchronize()
+        log(f"profile run done: 10 attention steps of {launch_bytes} algorithmic bytes, one 1 GiB copy")
+        return 0
+
+    ms = time_steps([step(c) for c in copies], args.steps, args.warmup, stream)
+    log(f"attention step {ms * 1e3:.2f} us")
+    achieved = launch_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "decode attention KV-stream GB/s (% of 8 TB/s HBM peak)",
+        "value": round(kv_bytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"GQA decode attention, {n_q} query / {n_kv} kv heads x 128, L={L} fp32 KV "
+                               f"({kv_bytes} B), split-KV partial + combine, {ncopies} rotated seeded caches",
+                   "context": L, "kv_bytes": kv_bytes, "launches_per_step": 2},
+        "pct_of_peak": round(100 * kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "k_attn_partial + k_attn_combine", "algorithmic_bytes_per_launch": launch_bytes},
+    }
+    if host0 is not None:
+        from oracle import oracle
+        oracle.build(force=False)
+        qv, k, v = host0
+        t0 = time.perf_counter()
+        done = 0
+        while True:
+            oracle.attn_decode(qv, k, v)
+            done += 1
+            if time.perf_counter() - t0 > args.cpu_budget:
+                break
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(done * kv_bytes / dt / 1e9, 3), "unit": "GB/s",
+                               "cores": oracle.max_threads(), "kind": "oracle",
+                               "sample": f"{done} fp64 attention passes over KV cache 0 ({kv_bytes} B each), {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qwen2.5-1.5b", choices=["qwen2.5-1.5b", "qwen2.5-7b", "lm_head", "lm_head_q8"])
+    ap.add_argument("--workload", default="qwen2.5-1.5b", choices=["qwen2.5-1.5b", "qwen2.5-7b", "lm_head", "lm_head_q8", "attn"])
+    ap.add_argument("--context", type=int, default=32768, help="KV positions for --workload attn")
     ap.add_argument("--n", type=int, default=1, help="activation rows per GEMV (1..24; 1..8 for lm_head_q8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify-ratio", action="store_true", help="skip the N=8 / N=1 step-cost ratio")
@@ -292,6 +371,8 @@ def main() -> int:
 
     if args.workload == "lm_head_q8":
         return run_q8_head(args, dev, stream)
+    if args.workload == "attn":
+        return run_attn(args, dev, stream)
     shapes, cfg, ncopies = workload_shapes(args.workload)
     n = args.n
     log(f"generating {ncopies} copies of {args.workload} ({len(shapes)} matrices), n={n}")

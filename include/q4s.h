@@ -235,6 +235,33 @@ q4s_status q4s_block_sums_q8_0(const void* w_packed, const void* x_q8, int32_t* 
 q4s_status q4s_requant_q8_0_to_q4_0(const void* w_q8_0, void* w_q4_0, int64_t rows, int64_t cols,
                                     void* stream);
 
+/* ---------------------------------------------------- decode attention */
+
+/*
+ * One decode step's attention over a KV cache, for every query head: the
+ * split-KV attn_partial / attn_combine pair of milestone M12 of the "minfer"
+ * README, with one read of a key/value head serving all query heads of its
+ * group (milestone M15; Qwen2.5-1.5B: 12 query heads over 2 kv heads).
+ *   s_hj = scale * q_h . k_{j,g}, g = h / (n_q / n_kv), scale = 1/sqrt(128)
+ *   o_h  = sum_j softmax_j(s_hj) v_{j,g}, over positions j < L
+ * Head dimension 128 (Q4S_ATTN_HEAD_DIM); n_q / n_kv (the group) in 1..8.
+ * Cache layouts (one contiguous 32 KB block per kv head and 64 positions):
+ * k_blk: keys blocked and transposed, fp32 [n_kv][l_cap/64][128][64]
+ * (position j, dimension d of kv head g at ((g*l_cap/64 + j/64)*128 + d)*64
+ * + j%64); v: fp32 [n_kv][l_cap][128].  q: fp32 [n_q][128]; o: fp32
+ * [n_q][128].  q, k_blk and v 16-byte aligned; o 4-byte aligned and it
+ * must not overlap the inputs or the workspace.  1 <= L <= l_cap < 2^31,
+ * l_cap a multiple of 64.
+ * workspace: q4s_attn_workspace_bytes(n_q, L) bytes of caller device memory
+ * (16-byte aligned) for the per-split partials (max, sum, weighted values);
+ * fully overwritten.  Accumulation is fp32 with expf, in a fixed order
+ * (deterministic).  Two launches on `stream`.
+ */
+#define Q4S_ATTN_HEAD_DIM 128
+size_t q4s_attn_workspace_bytes(int n_q, int64_t L);
+q4s_status q4s_attn_decode(const float* q, const float* k_blk, const float* v, float* o, int n_q, int n_kv,
+                           int64_t L, int64_t l_cap, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------- layer-stack sweep */
 
 /*

@@ -68,6 +68,8 @@ def lib():
             "q4s_gemv_q8_0": ([p, p, p, i64, i64, i32, p], i32),
             "q4s_block_sums_q8_0": ([p, p, p, i64, i64, i32, p], i32),
             "q4s_requant_q8_0_to_q4_0": ([p, p, i64, i64, p], i32),
+            "q4s_attn_workspace_bytes": ([i32, i64], sz),
+            "q4s_attn_decode": ([p, p, p, p, i32, i32, i64, i64, p, sz, p], i32),
             "q4s_sweep_plan_create": ([p, i32, i32, ctypes.POINTER(sz), ctypes.POINTER(p)], i32),
             "q4s_sweep_plan_upload": ([p, p, sz, p], i32),
             "q4s_sweep_run": ([p, p], i32),
@@ -238,6 +240,31 @@ def requant_q8_0_to_q4_0(w_q8_0: torch.Tensor, rows: int, cols: int,
     _check("q4s_requant_q8_0_to_q4_0",
            lib().q4s_requant_q8_0_to_q4_0(_dev(w_q8_0, "w_q8_0"), _dev(out, "out", torch.uint8), rows, cols,
                                           _stream(w_q8_0.device)))
+    return out
+
+
+# ---------------------------------------------------------------- attention
+
+ATTN_HEAD_DIM = 128
+
+
+def attn_workspace_bytes(n_q: int, L: int) -> int:
+    return int(lib().q4s_attn_workspace_bytes(n_q, L))
+
+
+def attn_decode(q: torch.Tensor, k_blk: torch.Tensor, v: torch.Tensor, L: int,
+                workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention: q fp32 [n_q][128], k_blk fp32 [n_kv][l_cap/64][128][64], v fp32 [n_kv][l_cap][128]."""
+    n_q = q.shape[0]
+    n_kv, l_cap = v.shape[0], v.shape[1]
+    if out is None:
+        out = torch.empty((n_q, ATTN_HEAD_DIM), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(16, attn_workspace_bytes(n_q, L)), dtype=torch.uint8, device=q.device)
+    _check("q4s_attn_decode", lib().q4s_attn_decode(
+        _dev(q, "q", torch.float32), _dev(k_blk, "k_blk", torch.float32), _dev(v, "v", torch.float32),
+        _dev(out, "out", torch.float32), n_q, n_kv, L, l_cap, _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(q.device)))
     return out
 
 

@@ -1,0 +1,238 @@
+// gfx950 kernels for decode attention over a KV cache: split-KV partials and
+// their combine (the attn_partial / attn_combine kernels of the "minfer"
+// README, nano-inference page, milestone M12), grouped so one read of a
+// key/value head serves every query head of its group (milestone M15).
+//
+// Layout (one 32 KB block per (kv head, 64 positions) for keys and values):
+// keys blocked and transposed, K [n_kv][l_cap/64][128][64] (position c of
+// block b, dimension d at ((g*NB + b)*128 + d)*64 + c), so a thread reads 4
+// consecutive positions of a dimension and no dot product crosses lanes;
+// values head-major, V [n_kv][l_cap][128].
+//
+// A workgroup takes one (kv head, 64-position split) and issues all of its
+// loads up front: 4 waves each form the partial dots over 32 head dimensions
+// for all G query heads of the group, the partials are added in a fixed
+// order, then a local softmax (maximum, exp, sum by wave reduction), then the
+// weighted sum of the split's values over 8 position slices added in order.
+// The combine rescales each split by exp(m_s - M) and adds the splits in a
+// fixed order, so results are deterministic.
+#include "q4s_device.h"
+
+namespace q4s {
+namespace {
+
+constexpr int kHd = kAttnHeadDim;     // 128
+constexpr int kSplit = kAttnSplit;    // 64 positions per split
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// workspace of split s (attn_split_floats(n_q) floats, a multiple of 4): [n_q][128]
+// unnormalized outputs, then [n_q] maxima m, then [n_q] sums l
+struct AttnParams {
+    const float* q;      // [n_q][128]
+    const float* kb;     // [n_kv][l_cap/64][128][64]
+    const float* v;      // [n_kv][l_cap][128]
+    float* o;            // [n_q][128]
+    float* ws;           // [S][attn_split_floats(n_q)]
+    int64_t L, l_cap;
+    int n_q, n_kv, S;
+    float scale;
+};
+
+template <int G>
+__global__ __launch_bounds__(256) void k_attn_partial(AttnParams a) {
+    __shared__ f32x4 qs[G][kHd / 4];
+    __shared__ float pr[G][kSplit];
+    // the partial dots are dead once the scores are formed; the value slices reuse their space
+    __shared__ union {
+        f32x4 part[16][G][kSplit / 4];  // [dimension group][head][position quad]
+        f32x4 vred[8][G][kHd / 4];      // [position slice][head][dimension quad]
+    } u;
+    auto& part = u.part;
+    auto& vred = u.vred;
+    const int s = blockIdx.x, g = blockIdx.y;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int64_t j0 = (int64_t)s * kSplit;
+    const int nk = (int)min((int64_t)kSplit, a.L - j0);
+    // Every load of the split is issued up front (queries, keys, values), as
+    // 16-byte non-temporal loads; positions past L are masked below.
+    f32x4 qv = {0.f, 0.f, 0.f, 0.f};
+    if (t < G * kHd / 4) qv = gp<f32x4>(a.q + (int64_t)(g * G) * kHd)[t];
+    // keys: thread (dimension group dg = t/16: dimensions 8dg .. 8dg+7, position quad pq = t%16);
+    // the workgroup reads its split's 32 KB key block contiguously
+    const int pq = t & 15, dg = t >> 4;
+    f32x4 kv[8];
+    {
+        const float* kp = a.kb + (((int64_t)g * (a.l_cap / kSplit) + s) * kHd + 8 * dg) * kSplit + 4 * pq;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) kv[d] = __builtin_nontemporal_load(gp<f32x4>(kp + d * kSplit));
+    }
+    const int dq = t & 31, ks = t >> 5;  // values: dimensions 4dq .. 4dq+3, positions 8ks .. 8ks+7
+    f32x4 vv[8];
+    {
+        const float* vp = a.v + ((int64_t)g * a.l_cap + j0) * kHd + 4 * dq;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            vv[e] = __builtin_nontemporal_load(gp<f32x4>(vp + (int64_t)min(8 * ks + e, nk - 1) * kHd));
+    }
+    if (t < G * kHd / 4) qs[t / (kHd / 4)][t % (kHd / 4)] = qv;
+    __syncthreads();
+    // partial dots over the thread's 8 dimensions for its 4 positions
+    {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const f32x4 q0 = qs[h][2 * dg], q1 = qs[h][2 * dg + 1];
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                acc[0] = fmaf(q0[d], kv[d][0], acc[0]);
+                acc[1] = fmaf(q0[d], kv[d][1], acc[1]);
+                acc[2] = fmaf(q0[d], kv[d][2], acc[2]);
+                acc[3] = fmaf(q0[d], kv[d][3], acc[3]);
+            }
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                acc[0] = fmaf(q1[d], kv[4 + d][0], acc[0]);
+                acc[1] = fmaf(q1[d], kv[4 + d][1], acc[1]);
+                acc[2] = fmaf(q1[d], kv[4 + d][2], acc[2]);
+                acc[3] = fmaf(q1[d], kv[4 + d][3], acc[3]);
+            }
+            part[dg][h][pq] = acc;
+        }
+    }
+    __syncthreads();
+    // scores (the 16 dimension groups added in order) and the split's softmax:
+    // wave w takes heads w, w + 4; lane = position
+    for (int h = w; h < G; h += 4) {
+        float sc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) sc += ((const float*)part[k][h])[lane];
+        sc = lane < nk ? sc * a.scale : -INFINITY;
+        const float m = wave_max(sc);
+        const float p = lane < nk ? expf(sc - m) : 0.0f;
+        const float l = wave_sum(p);
+        pr[h][lane] = p;
+        if (lane == 0) {
+            float* wsm = a.ws + (int64_t)s * attn_split_floats(a.n_q) + (int64_t)a.n_q * kHd;
+            gwr<float>(wsm)[g * G + h] = m;
+            gwr<float>(wsm)[a.n_q + g * G + h] = l;
+        }
+    }
+    __syncthreads();
+    // weighted values over the thread's 8 positions, then the 8 position slices in order
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = pr[h][8 * ks + e];  // 0 past the split's last position
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = fmaf(p, vv[e][c], acc[c]);
+        }
+        vred[ks][h][dq] = acc;
+    }
+    __syncthreads();
+    if (t < G * kHd / 4) {
+        const int h = t / (kHd / 4), d4 = t % (kHd / 4);
+        f32x4 o = vred[0][h][d4];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) o += vred[k][h][d4];
+        float* wso = a.ws + (int64_t)s * attn_split_floats(a.n_q);
+        gwr<f32x4>(wso + (int64_t)(g * G + h) * kHd)[d4] = o;
+    }
+}
+
+// Workgroup (query head h, 16-dimension block), 1024 threads: thread (split
+// slice k, dimension) takes splits [k*S/64, (k+1)*S/64) in order, all of its
+// loads issued together; the 64 slices are then added in order.
+constexpr int kCombSlices = 64;
+constexpr int kCombDims = 16;
+constexpr int kCombBatch = 8;  // splits per slice whose loads are in flight together
+__global__ __launch_bounds__(kCombSlices * kCombDims) void k_attn_combine(AttnParams a) {
+    __shared__ float mred[kCombSlices];
+    __shared__ float num[kCombSlices][kCombDims];
+    __shared__ float den[kCombSlices];
+    const int h = blockIdx.x, d0 = blockIdx.y * kCombDims;
+    const int t = threadIdx.x, dd = t % kCombDims, k = t / kCombDims;
+    const int64_t stride = attn_split_floats(a.n_q);
+    const int64_t om = (int64_t)a.n_q * kHd, ol = om + a.n_q;  // offsets of m and l in a split
+    const int s0 = (int)((int64_t)k * a.S / kCombSlices), s1 = (int)((int64_t)(k + 1) * a.S / kCombSlices);
+    // the first batch of the slice (all of it up to 512 splits) loaded at once
+    float mm[kCombBatch], ll[kCombBatch], oo[kCombBatch];
+    auto load_batch = [&](int b) {
+#pragma unroll
+        for (int i = 0; i < kCombBatch; ++i) {
+            const float* wsm = a.ws + max(min(b + i, s1 - 1), 0) * stride;
+            mm[i] = wsm[om + h];
+            ll[i] = wsm[ol + h];
+            oo[i] = wsm[(int64_t)h * kHd + d0 + dd];
+        }
+    };
+    load_batch(s0);
+    float mk = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kCombBatch; ++i)
+        if (s0 + i < s1) mk = fmaxf(mk, mm[i]);
+    for (int b = s0 + kCombBatch; b < s1; ++b) mk = fmaxf(mk, a.ws[b * stride + om + h]);
+    if (dd == 0) mred[k] = mk;
+    __syncthreads();
+    float M = mred[0];
+    for (int i = 1; i < kCombSlices; ++i) M = fmaxf(M, mred[i]);
+    float nu = 0.0f, de = 0.0f;
+    for (int b = s0; b < s1; b += kCombBatch) {
+        if (b != s0) load_batch(b);
+#pragma unroll
+        for (int i = 0; i < kCombBatch; ++i) {
+            if (b + i >= s1) break;
+            const float f = expf(mm[i] - M);
+            de = fmaf(f, ll[i], de);
+            nu = fmaf(f, oo[i], nu);
+        }
+    }
+    num[k][dd] = nu;
+    if (dd == 0) den[k] = de;
+    __syncthreads();
+    if (k == 0) {
+        float n = num[0][dd], d = den[0];
+        for (int i = 1; i < kCombSlices; ++i) {
+            n += num[i][dd];
+            d += den[i];
+        }
+        gwr<float>(a.o)[(int64_t)h * kHd + d0 + dd] = n / d;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_decode(const float* q, const float* kb, const float* v, float* o, float* ws, int n_q,
+                              int n_kv, int64_t L, int64_t l_cap, float scale, hipStream_t st) {
+    AttnParams a{q, kb, v, o, ws, L, l_cap, n_q, n_kv, (int)((L + kSplit - 1) / kSplit), scale};
+    const dim3 grid((unsigned)a.S, (unsigned)n_kv);
+    switch (n_q / n_kv) {
+        case 1: hipLaunchKernelGGL(k_attn_partial<1>, grid, dim3(256), 0, st, a); break;
+        case 2: hipLaunchKernelGGL(k_attn_partial<2>, grid, dim3(256), 0, st, a); break;
+        case 3: hipLaunchKernelGGL(k_attn_partial<3>, grid, dim3(256), 0, st, a); break;
+        case 4: hipLaunchKernelGGL(k_attn_partial<4>, grid, dim3(256), 0, st, a); break;
+        case 5: hipLaunchKernelGGL(k_attn_partial<5>, grid, dim3(256), 0, st, a); break;
+        case 6: hipLaunchKernelGGL(k_attn_partial<6>, grid, dim3(256), 0, st, a); break;
+        case 7: hipLaunchKernelGGL(k_attn_partial<7>, grid, dim3(256), 0, st, a); break;
+        case 8: hipLaunchKernelGGL(k_attn_partial<8>, grid, dim3(256), 0, st, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)n_q, kHd / kCombDims), dim3(kCombSlices * kCombDims), 0, st,
+                       a);
+    return hipGetLastError();
+}
+
+}  // namespace q4s

@@ -92,6 +92,14 @@ hipError_t launch_repack_q8_0(const uint8_t* w, uint8_t* packed, int64_t rows, i
 hipError_t launch_gemv_q8_0(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st);
 hipError_t launch_block_sums_q8_0(const MatDesc& m, int n, int32_t* s, hipStream_t st);
 hipError_t launch_requant_q8_0_to_q4_0(const uint8_t* w8, uint8_t* w4, int64_t n_blocks, hipStream_t st);
+// Decode attention (q4s_attn.hip): split-KV partials over 64-position splits, then the combine.
+constexpr int kAttnHeadDim = 128;
+constexpr int kAttnSplit = 64;
+inline int64_t attn_splits(int64_t L) { return (L + kAttnSplit - 1) / kAttnSplit; }
+// floats per split in the workspace: n_q*128 outputs, n_q maxima, n_q sums, rounded up to 4
+__host__ __device__ inline int64_t attn_split_floats(int64_t n_q) { return (n_q * (kAttnHeadDim + 2) + 3) / 4 * 4; }
+hipError_t launch_attn_decode(const float* q, const float* kb, const float* v, float* o, float* ws, int n_q,
+                              int n_kv, int64_t L, int64_t l_cap, float scale, hipStream_t st);
 hipError_t launch_bench_read(const void* buf, size_t bytes, int lif, int n_blocks,
                              uint32_t* sink, hipStream_t st);
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t st);

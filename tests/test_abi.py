@@ -98,6 +98,22 @@ def test_other_entry_points_validate(L):
     assert L.q4s_requant_q8_0_to_q4_0(FAKE, FAKE + 64, 64, 64, None) == 4
     assert L.q4s_requant_q8_0_to_q4_0(None, FAKE, 64, 64, None) == 1
     assert L.q4s_requant_q8_0_to_q4_0(None, None, 0, 64, None) == 0
+    # decode attention
+    a = L.q4s_attn_decode
+    W = q.attn_workspace_bytes(12, 100)
+    assert W == 2 * 12 * 130 * 4 and q.attn_workspace_bytes(12, 0) == 0
+    assert q.attn_workspace_bytes(3, 64) == 392 * 4                    # 3*130 rounded up to 4 floats
+    ok = (FAKE, FAKE + (1 << 24), FAKE + (1 << 26), FAKE + (1 << 28), 12, 2, 100, 128, FAKE + (1 << 29), W, None)
+    assert a(*ok[:7], 130, *ok[8:]) == 2                                # l_cap not a multiple of 64
+    assert a(*ok[:4], 12, 5, *ok[6:]) == 2                              # 5 does not divide 12
+    assert a(*ok[:4], 18, 2, *ok[6:]) == 2                              # group of 9
+    assert a(*ok[:6], 129, 128, *ok[8:]) == 2                           # L > l_cap
+    assert a(FAKE, FAKE + (1 << 24) + 4, *ok[2:]) == 3                  # k_blk needs 16 bytes
+    assert a(*ok[:6], 0, 128, *ok[8:]) == 2
+    assert a(*ok[:9], W - 4, None) == 2                                 # workspace too small
+    assert a(FAKE + 4, *ok[1:]) == 3                                    # q needs 16 bytes
+    assert a(*ok[:3], FAKE, *ok[4:]) == 4                               # o overlaps q
+    assert a(*ok[:8], FAKE + (1 << 28) + 64, W, None) == 4              # workspace overlaps o
 
 
 def _plan(L, mats, n):
