@@ -260,6 +260,28 @@ def run_q8_head(args, dev, stream) -> int:
     return 0
 
 
+ATTN_SRCS = [os.path.join(ROOT, "q4_weight_streaming_amd", "csrc", f)
+              for f in ("q4s_attn.hip", "q4s_device.h", "q4s_internal.h")]
+
+
+def attn_traffic_from_profile(L: int):
+    """HBM bytes (fetch + write) of the attention step's two kernels from the committed
+    summary, if taken on the current attention source; else None."""
+    path = os.path.join(ROOT, "profiles", f"attn_decode_l{L}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = hashlib.sha256()
+    for f in ATTN_SRCS:
+        h.update(open(f, "rb").read())
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
+    if not m or m.group(1) != h.hexdigest()[:16]:
+        return None
+    mb = [float(v) for v in re.findall(r"\| `k_attn_\w+(?:<\d+>)?` \| ([0-9.]+) MB \| ([0-9.]+) MB \|", text)
+          for v in v]
+    return round(sum(mb) * 1e6) if mb else None
+
+
 def run_attn(args, dev, stream) -> int:
     """Decode attention of one layer of the 1.5B model (12 query / 2 kv heads, head dim 128) at
     the 32768-position context, over 8 rotated seeded KV caches (512 MB, beyond every cache)."""
@@ -316,7 +338,7 @@ def run_attn(args, dev, stream) -> int:
                    "context": L, "kv_bytes": kv_bytes, "launches_per_step": 2},
         "pct_of_peak": round(100 * kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": attn_traffic_from_profile(L),
                      "kernel": "k_attn_partial + k_attn_combine", "algorithmic_bytes_per_launch": launch_bytes},
     }
     if host0 is not None:

@@ -35,11 +35,17 @@ struct Chunk {
     u32x4 scale;
 };
 
+// Weights are streamed with non-temporal loads; the tiled many-row steps
+// (kTemporal) keep them in L2 for the other token tiles of the same rows.
+template <bool kTemporal = false>
 __device__ __forceinline__ void load_chunk(Chunk& ch, const uint8_t* p) {
 #pragma unroll
-    for (int b = 0; b < kChunkBlocks; ++b)
-        ch.nib[b] = __builtin_nontemporal_load(gp<u32x4>(p + b * (kGroupRows * kBlockNibBytes)));
-    ch.scale = __builtin_nontemporal_load(gp<u32x4>(p + kChunkNibBytes));
+    for (int b = 0; b < kChunkBlocks; ++b) {
+        const Q4S_GLOBAL u32x4* a = gp<u32x4>(p + b * (kGroupRows * kBlockNibBytes));
+        ch.nib[b] = kTemporal ? *a : __builtin_nontemporal_load(a);
+    }
+    const Q4S_GLOBAL u32x4* a = gp<u32x4>(p + kChunkNibBytes);
+    ch.scale = kTemporal ? *a : __builtin_nontemporal_load(a);
 }
 
 // ---------------------------------------------------------------- block dot
@@ -337,7 +343,7 @@ __device__ __forceinline__ void chunk_mfma(Chunk& ch, const ActRaw& ar, float (&
 
 // acc[mt*4 + r] = y[token 4*(lg&1) + r][row g*64 + 16*mt + j] (lanes 0-31; lanes
 // 32-63 hold the same values)
-template <int N>
+template <int N, bool kTemporal = false>
 __device__ __forceinline__ void wave_task_mfma(const MatDesc& m, int g, int c0, int c1, float (&acc)[16],
                                                WaveLds& L) {
     const int lane = threadIdx.x & 63;
@@ -362,21 +368,21 @@ __device__ __forceinline__ void wave_task_mfma(const MatDesc& m, int g, int c0, 
     // unconditional prefetch in the steady state, as in the 1-row path
     Chunk wa, wb;
     ActRaw aa, ab;
-    load_chunk(wa, wp);
+    load_chunk<kTemporal>(wa, wp);
     load_act<N>(aa, m, c0);
     int c = c0;
     for (; c + 2 < c1; c += 2, wp += 2 * kChunkBytes) {
-        load_chunk(wb, wp + kChunkBytes);
+        load_chunk<kTemporal>(wb, wp + kChunkBytes);
         load_act<N>(ab, m, c + 1);
         chunk_mfma<N>(wa, aa, part, L);
         seg_end(c);
-        load_chunk(wa, wp + 2 * kChunkBytes);
+        load_chunk<kTemporal>(wa, wp + 2 * kChunkBytes);
         load_act<N>(aa, m, c + 2);
         chunk_mfma<N>(wb, ab, part, L);
         seg_end(c + 1);
     }
     if (c + 1 < c1) {
-        load_chunk(wb, wp + kChunkBytes);
+        load_chunk<kTemporal>(wb, wp + kChunkBytes);
         load_act<N>(ab, m, c + 1);
         chunk_mfma<N>(wa, aa, part, L);
         seg_end(c);
@@ -388,10 +394,10 @@ __device__ __forceinline__ void wave_task_mfma(const MatDesc& m, int g, int c0, 
     }
 }
 
-template <int N>
+template <int N, bool kTemporal = false>
 __device__ __forceinline__ void run_tile_mfma(const MatDesc& m, int64_t gset, float* red, WaveLds* wl) {
     run_tile_mfma_with<N>(m, gset, red, wl, [&](int g, int c0, int c1, float (&acc)[16], WaveLds& L) {
-        wave_task_mfma<N>(m, g, c0, c1, acc, L);
+        wave_task_mfma<N, kTemporal>(m, g, c0, c1, acc, L);
     });
 }
 
@@ -438,7 +444,8 @@ __global__ __launch_bounds__(kThreads, N == 1 ? 1 : 2) void k_sweep(const MatDes
 // 1-row result).  The tiles of one unit (group set, or sweep table entry) get
 // block indices 8 apart: the dispatcher deals workgroups to the 8 XCDs in
 // turn, so they land on the same XCD at about the same time and the later
-// tiles read the weights from its L2 instead of HBM.
+// tiles read the weights from its L2 (the tiled kernels load them without the
+// non-temporal hint) instead of HBM.
 __device__ __forceinline__ bool tiled_unit(int tt, int64_t n_units, int64_t& unit, int& tile) {
     const int64_t i = blockIdx.x, x = i & 7, s = i >> 3;
     unit = (s / tt) * 8 + x;
@@ -461,7 +468,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemv_tiled(MatDesc m, int tt, i
     int64_t gset;
     int tile;
     if (!tiled_unit(tt, n_gsets, gset, tile)) return;
-    run_tile_mfma<kTokTile>(token_tile(m, tile), gset, l.red, l.wl);
+    run_tile_mfma<kTokTile, true>(token_tile(m, tile), gset, l.red, l.wl);
 }
 
 __global__ __launch_bounds__(kThreads, 2) void k_sweep_tiled(const MatDesc* __restrict__ mats,
@@ -473,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_sweep_tiled(const MatDesc* __re
     if (!tiled_unit(tt, n_entries, e, tile)) return;
     const uint32_t mi = tiles[2 * (size_t)e];
     const uint32_t gs = tiles[2 * (size_t)e + 1];
-    run_tile_mfma<kTokTile>(token_tile(mats[mi], tile), gs, l.red, l.wl);
+    run_tile_mfma<kTokTile, true>(token_tile(mats[mi], tile), gs, l.red, l.wl);
 }
 
 // grid of a tiled launch: 8 * tt * ceil(units / 8)
