@@ -341,6 +341,35 @@ void q4s_sweep_plan_destroy(q4s_plan* plan);
 q4s_status q4s_bench_read(const void* buf, size_t bytes, int loads_in_flight, int n_blocks,
                           uint32_t* sink, void* stream);
 
+/*
+ * Grid-barrier microbenchmark (the phase barriers of a chained decode step):
+ * one persistent cooperative launch of n_workgroups x 256 threads (1..the
+ * number resident at once, see below) that passes `phases` grid barriers.
+ * kind 0: milestone M19's monotonic arrival counter (one device-scope atomic
+ * add per arrival on one word, everyone polls it with acquire loads);
+ * kind 1: each workgroup stores its phase number into its own 128-byte line,
+ * workgroup 0 polls them all and stores a release word; kind 2: a combining
+ * tree of monotonic counters (16 sub-counters, then a top counter whose last
+ * arrival stores the release word; relaxed polls and one acquire fence);
+ * kind 3: kind 0 with relaxed polls and one acquire fence; kinds 4, 5, 6:
+ * kind 2 with every sub-counter in its own 1 KB, 4 KB or 64 KB slot that also
+ * holds a copy of the release word, polled by that sub-counter's workgroups;
+ * kinds 7, 8: kind 2 with relaxed arrivals and an acquire fence, or with no
+ * fence; kind 9: kind 0 with no fence (fence-cost measurements only: they
+ * order no data).
+ * scratch:
+ * q4s_bench_grid_barrier_scratch_bytes bytes of device memory (4-byte
+ * aligned), zeroed by the call; word 1 becomes nonzero if a workgroup gave up
+ * waiting (a bounded poll: the launch always
+ * ends).  The caller times the launch.
+ */
+size_t q4s_bench_grid_barrier_scratch_bytes(int n_workgroups);
+q4s_status q4s_bench_grid_barrier(int kind, int n_workgroups, int phases, uint32_t* scratch,
+                                  size_t scratch_bytes, void* stream);
+
+/* Workgroups of q4s_bench_grid_barrier that fit on the device at once (0 on error). */
+int q4s_bench_grid_barrier_max_workgroups(void);
+
 /* Plain 16-byte copy of `bytes` (a multiple of 16) from src to dst. */
 q4s_status q4s_bench_copy(const void* src, void* dst, size_t bytes, void* stream);
 

@@ -77,6 +77,9 @@ def lib():
             "q4s_sweep_plan_destroy": ([p], None),
             "q4s_bench_read": ([p, sz, i32, i32, p, p], i32),
             "q4s_bench_copy": ([p, p, sz, p], i32),
+            "q4s_bench_grid_barrier": ([i32, i32, i32, p, sz, p], i32),
+            "q4s_bench_grid_barrier_scratch_bytes": ([i32], sz),
+            "q4s_bench_grid_barrier_max_workgroups": ([], i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -335,3 +338,18 @@ def bench_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
         raise ValueError("dst too small")
     _check("q4s_bench_copy", lib().q4s_bench_copy(_dev(src, "src"), _dev(dst, "dst"), nbytes,
                                                    _stream(src.device)))
+
+
+def bench_grid_barrier(kind: int, n_workgroups: int, phases: int, scratch: torch.Tensor) -> None:
+    """Launch a grid-barrier measurement kernel (kind 0: atomic counter, 1: per-workgroup flags)."""
+    _check("q4s_bench_grid_barrier", lib().q4s_bench_grid_barrier(
+        kind, n_workgroups, phases, _dev(scratch, "scratch"), scratch.numel() * scratch.element_size(),
+        _stream(scratch.device)))
+
+
+def grid_barrier_scratch_bytes(n_workgroups: int) -> int:
+    return int(lib().q4s_bench_grid_barrier_scratch_bytes(n_workgroups))
+
+
+def grid_barrier_max_workgroups() -> int:
+    return int(lib().q4s_bench_grid_barrier_max_workgroups())

@@ -509,6 +509,34 @@ q4s_status q4s_bench_read(const void* buf, size_t bytes, int loads_in_flight, in
                       "bench_read launch");
 }
 
+size_t q4s_bench_grid_barrier_scratch_bytes(int n_workgroups) {
+    if (n_workgroups < 1 || n_workgroups > (1 << 20)) return 0;
+    return grid_barrier_scratch_words(n_workgroups) * 4;
+}
+
+q4s_status q4s_bench_grid_barrier(int kind, int n_workgroups, int phases, uint32_t* scratch, size_t scratch_bytes,
+                                  void* stream) {
+    if (kind < 0 || kind > 9) return fail(Q4S_ERR_SHAPE, "kind must be 0..9");
+    if (phases < 1 || phases > (1 << 20)) return fail(Q4S_ERR_SHAPE, "phases must be in 1..2^20");
+    int max_wg = 0;
+    hipError_t e = grid_barrier_max_workgroups(&max_wg);
+    if (e != hipSuccess) return hip_status(e, "occupancy query");
+    if (n_workgroups < 1 || n_workgroups > max_wg)
+        return fail(Q4S_ERR_SHAPE, "n_workgroups=%d out of [1, %d] (all must be resident at once)", n_workgroups,
+                    max_wg);
+    const size_t need = q4s_bench_grid_barrier_scratch_bytes(n_workgroups);
+    q4s_status s;
+    if ((s = check_ptr(scratch, need, 4, "scratch"))) return s;
+    if (scratch_bytes < need) return fail(Q4S_ERR_SHAPE, "scratch holds %zu bytes, needs %zu", scratch_bytes, need);
+    return hip_status(launch_grid_barrier(kind, n_workgroups, phases, scratch, (hipStream_t)stream),
+                      "barrier launch");
+}
+
+int q4s_bench_grid_barrier_max_workgroups(void) {
+    int n = 0;
+    return grid_barrier_max_workgroups(&n) == hipSuccess ? n : 0;
+}
+
 q4s_status q4s_bench_copy(const void* src, void* dst, size_t bytes, void* stream) {
     if (bytes % 16) return fail(Q4S_ERR_SHAPE, "bytes must be a multiple of 16");
     q4s_status s;

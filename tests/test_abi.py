@@ -84,6 +84,9 @@ def test_other_entry_points_validate(L):
     assert L.q4s_bench_read(FAKE, 32, 3, 0, FAKE + (1 << 30), None) == 2
     assert L.q4s_bench_copy(FAKE, FAKE + 16, 64, None) == 4
     assert L.q4s_sweep_run(None, None) == 1
+    assert L.q4s_bench_grid_barrier(0, 4, 0, FAKE, 1 << 20, None) == 2      # phases >= 1
+    assert L.q4s_bench_grid_barrier(10, 4, 10, FAKE, 1 << 20, None) == 2     # unknown kind
+    assert q.grid_barrier_scratch_bytes(4) == (64 + 16 * 16384) * 4
     # Q8_0 weights
     g = L.q4s_gemv_q8_0
     assert g(FAKE, FAKE, FAKE + (1 << 30), 64, 33, 1, None) == 2
