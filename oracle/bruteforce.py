@@ -51,3 +51,31 @@ def gemv64(w: np.ndarray, xq8: np.ndarray, rows: int, cols: int, n: int) -> np.n
     W = dequant_q4_0(w, rows, cols)
     X = dequant_q8_0(xq8, n, cols)
     return X @ W.T
+
+
+def chain64(weights, E: int, D: int, F: int, V: int, h0: np.ndarray):
+    """The chained step with exact (unquantized) activations, in fp64: each matrix is
+    dequantized and applied to the activation itself, norms in fp64.  Differs from the
+    quantized chain only by the Q8_0 rounding of the activations.
+    Returns (dict of per-layer vectors, logits)."""
+    layers = len(weights) // 7
+    def nrm(x):
+        return x / np.sqrt(np.mean(x * x) + 1e-6)
+    h = np.asarray(h0, dtype=np.float64)
+    out = []
+    for l in range(layers):
+        Wq, Wk, Wv, Wo, Wg, Wu, Wd = (
+            dequant_q4_0(weights[7 * l + i], r, c)
+            for i, (r, c) in enumerate([(E, E), (D, E), (D, E), (E, E), (F, E), (F, E), (E, F)]))
+        a = nrm(h)
+        q, k, v = Wq @ a, Wk @ a, Wv @ a
+        o = Wo @ q
+        h1 = h + o
+        c = nrm(h1)
+        g, u = Wg @ c, Wu @ c
+        dn = Wd @ (g * u)
+        h2 = h1 + dn
+        out.append(dict(q=q, k=k, v=v, o=o, h1=h1, g=g, u=u, dn=dn, h2=h2))
+        h = h2
+    logits = dequant_q4_0(weights[-1], V, E) @ nrm(h)
+    return out, logits

@@ -66,6 +66,11 @@ def _bind(path: str):
     L.q4o_requant_block_q8_0_to_q4_0.argtypes = [p, p]
     L.q4o_requant_q8_0_to_q4_0.argtypes = [p, p, i64]
     L.q4o_attn_decode.argtypes = [p, p, p, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, p, p]
+    L.q4o_gemv_f32.argtypes = [p, p, i64, i64, ctypes.c_int, p]
+    L.q4o_gemv_f32_rows.argtypes = [p, p, i64, ctypes.c_int, p, i64, p]
+    L.q4o_rmsnorm.argtypes = [p, i64, p]
+    L.q4o_rmsnorm.restype = ctypes.c_float
+    L.q4o_chain_step.argtypes = [p, ctypes.c_int, i64, i64, i64, i64, p, p, p]
     L.q4o_set_threads.argtypes = [ctypes.c_int]
     L.q4o_max_threads.restype = ctypes.c_int
     return L
@@ -207,6 +212,68 @@ def gemv_rows(w: np.ndarray, xq8: np.ndarray, cols: int, n: int, row_idx: np.nda
     S = np.empty((n, idx.size), np.float64)
     lib().q4o_gemv_rows(_ptr(w), _ptr(xq8), cols, n, _ptr(idx), idx.size, _ptr(y), _ptr(S))
     return y, S
+
+
+def gemv_f32(w: np.ndarray, xq8: np.ndarray, rows: int, cols: int, n: int) -> np.ndarray:
+    """The GEMV in the fixed fp32 order (milestone M16 reading) -> y float32 [n][rows]."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    xq8 = np.ascontiguousarray(xq8, dtype=np.uint8)
+    assert w.size == rows * (cols // QK) * Q4_BLOCK_BYTES
+    assert xq8.size == n * (cols // QK) * Q8_BLOCK_BYTES
+    y = np.empty((n, rows), np.float32)
+    lib().q4o_gemv_f32(_ptr(w), _ptr(xq8), rows, cols, n, _ptr(y))
+    return y
+
+
+def gemv_f32_rows(w: np.ndarray, xq8: np.ndarray, cols: int, n: int, row_idx: np.ndarray) -> np.ndarray:
+    """Selected rows of the fixed-order fp32 GEMV -> y float32 [n][len(row_idx)]."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    xq8 = np.ascontiguousarray(xq8, dtype=np.uint8)
+    idx = np.ascontiguousarray(row_idx, dtype=np.int64)
+    rows = w.size // ((cols // QK) * Q4_BLOCK_BYTES)
+    assert idx.size == 0 or (idx.min() >= 0 and idx.max() < rows)
+    y = np.empty((n, idx.size), np.float32)
+    lib().q4o_gemv_f32_rows(_ptr(w), _ptr(xq8), cols, n, _ptr(idx), idx.size, _ptr(y))
+    return y
+
+
+# ---------------------------------------------------------------- chained step
+
+def rmsnorm(x: np.ndarray):
+    """-> (x / sqrt(ss/n + 1e-6) float32, ss) with ss in the fixed order (see q4_oracle.c)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty_like(x)
+    ss = lib().q4o_rmsnorm(_ptr(x), x.size, _ptr(out))
+    return out, float(ss)
+
+
+def chain_layout(E: int, D: int, F: int):
+    """Offsets of q, k, v, o, h1, g, u, dn, h2 within one layer's block of activations."""
+    sizes = [("q", E), ("k", D), ("v", D), ("o", E), ("h1", E), ("g", F), ("u", F), ("dn", E), ("h2", E)]
+    off, out = 0, {}
+    for name, n in sizes:
+        out[name] = (off, n)
+        off += n
+    return out, off
+
+
+def chain_step(weights, E: int, D: int, F: int, V: int, h0: np.ndarray):
+    """One chained decode step.  weights: 7*layers + 1 canonical Q4_0 arrays (q, k, v, o, gate,
+    up, down per layer, then the head).  Returns (acts float32 [layers][per_layer], logits [V])."""
+    assert len(weights) % 7 == 1
+    layers = len(weights) // 7
+    shapes = [(E, E), (D, E), (D, E), (E, E), (F, E), (F, E), (E, F)] * layers + [(V, E)]
+    ws = [np.ascontiguousarray(w, dtype=np.uint8) for w in weights]
+    for w, (r, c) in zip(ws, shapes):
+        assert w.size == r * (c // QK) * Q4_BLOCK_BYTES
+    h0 = np.ascontiguousarray(h0, dtype=np.float32)
+    assert h0.size == E
+    _, per = chain_layout(E, D, F)
+    acts = np.empty((layers, per), np.float32)
+    logits = np.empty(V, np.float32)
+    ptrs = (ctypes.c_void_p * len(ws))(*[w.ctypes.data for w in ws])
+    lib().q4o_chain_step(ptrs, layers, E, D, F, V, _ptr(h0), _ptr(acts), _ptr(logits))
+    return acts, logits
 
 
 # ---------------------------------------------------------------- Q8_0 weights

@@ -21,6 +21,11 @@
  *   - Milestones M14 and M18: 8-bit heads requantized to Q4_0 at load.
  *   - Milestones M5, M12 and M15, and the model details (12 query heads over
  *     2 key/value heads of dimension 128): decode attention over a KV cache.
+ *   - Milestone M16 ("every float operation explicitly rounded", logits
+ *     independent of the step size): the GEMV in one fixed fp32 order.
+ *   - "How it works", src/mega.cu bullet, and milestones M15 and M19: a
+ *     token's layers run as dependent phases (norm prologue, activation
+ *     quantize, GEMV, residual) inside one kernel -- the chained step.
  *
  * Block formats (GGUF convention, where the pages leave the byte order open):
  *   Q4_0 (18 B / 32 weights): fp16 scale d (little-endian), then 16 bytes qs.
@@ -45,6 +50,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -268,6 +274,175 @@ void q4o_gemv_rows(const uint8_t* w, const uint8_t* xq8, int64_t cols, int n,
             gemv_one(w + row_idx[i] * nb * Q4_BLOCK_BYTES, xq8 + (int64_t)t * nb * Q8_BLOCK_BYTES,
                      nb, y ? y + o : 0, 0, scale ? scale + o : 0);
         }
+}
+
+/* ------------------------------------------------------------------ */
+/* The GEMV in one fixed fp32 order.                                    */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Milestone M16 makes every float operation of a token explicitly rounded so
+ * that its result does not depend on how many tokens share the step; that
+ * fixes one expression per block and one accumulation order.  The pages leave
+ * the order itself open; the one taken (the GPU path's) is:
+ *   - the blocks of a row are cut into chunks of 8, nc = ceil(nb / 8) chunks;
+ *   - the chunks are split into ks contiguous ranges, ks = 1 if nc <= 8,
+ *     2 if nc <= 16, else 4; range s is [floor(s*nc/ks), floor((s+1)*nc/ks));
+ *   - within a range, blocks 0-3 of every chunk feed chain A and blocks 4-7
+ *     chain B, one fmaf(d_w * d_x, (float)s, chain) per block in chunk order
+ *     (d_w * d_x, two binary16 values, is exact in fp32);
+ *   - after the 16th, 32nd, ... chunk of a range and after its last chunk:
+ *     total = total + (A + B), and both chains restart at 0;
+ *   - y = ((total_0 + total_1) + total_2) + total_3, left to right.
+ * Missing blocks of a last, partial chunk add nothing.
+ */
+static float gemv_one_f32(const uint8_t* wrow, const uint8_t* xrow, int64_t nb)
+{
+    const int64_t nc = (nb + 7) / 8;
+    const int64_t ks = nc <= 8 ? 1 : (nc <= 16 ? 2 : 4);
+    float y = 0.0f;
+    for (int64_t s = 0; s < ks; ++s) {
+        const int64_t c0 = s * nc / ks, c1 = (s + 1) * nc / ks;
+        float total = 0.0f, chain_a = 0.0f, chain_b = 0.0f;
+        for (int64_t c = c0; c < c1; ++c) {
+            for (int64_t k = 0; k < 8 && c * 8 + k < nb; ++k) {
+                const uint8_t* wb = wrow + (c * 8 + k) * Q4_BLOCK_BYTES;
+                const uint8_t* xb = xrow + (c * 8 + k) * Q8_BLOCK_BYTES;
+                const float scale = q4o_fp16_to_f32(load_u16_le(wb)) * q4o_fp16_to_f32(load_u16_le(xb));
+                const float sum = (float)q4o_block_dot(wb, xb);
+                if (k < 4)
+                    chain_a = fmaf(scale, sum, chain_a);
+                else
+                    chain_b = fmaf(scale, sum, chain_b);
+            }
+            if (c + 1 == c1 || (c + 1 - c0) % 16 == 0) {
+                total = total + (chain_a + chain_b);
+                chain_a = 0.0f;
+                chain_b = 0.0f;
+            }
+        }
+        y = s == 0 ? total : y + total;
+    }
+    return y;
+}
+
+/* y : [n][rows], every element in the order above */
+void q4o_gemv_f32(const uint8_t* w, const uint8_t* xq8, int64_t rows, int64_t cols, int n, float* y)
+{
+    int64_t nb = cols / QK;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int t = 0; t < n; ++t)
+            y[(int64_t)t * rows + r] =
+                gemv_one_f32(w + r * nb * Q4_BLOCK_BYTES, xq8 + (int64_t)t * nb * Q8_BLOCK_BYTES, nb);
+}
+
+/* selected rows of the full matrix: y : [n][n_idx] */
+void q4o_gemv_f32_rows(const uint8_t* w, const uint8_t* xq8, int64_t cols, int n, const int64_t* row_idx,
+                       int64_t n_idx, float* y)
+{
+    int64_t nb = cols / QK;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n_idx; ++i)
+        for (int t = 0; t < n; ++t)
+            y[(int64_t)t * n_idx + i] =
+                gemv_one_f32(w + row_idx[i] * nb * Q4_BLOCK_BYTES, xq8 + (int64_t)t * nb * Q8_BLOCK_BYTES, nb);
+}
+
+/* ------------------------------------------------------------------ */
+/* RMS normalization and the chained token step.                        */
+/* ------------------------------------------------------------------ */
+
+/*
+ * out_i = x_i / sqrt(ss / n + 1e-6), all fp32, sqrt and division correctly
+ * rounded, with no learned weight (the synthetic model's norm weights are 1).
+ * Qwen2.5's RMS norm with its epsilon of 1e-6; the pages name "norm
+ * prologues" (M19) without a formula.  The sum of squares ss is taken in a
+ * fixed order: 64 partial sums p_l = fmaf chains over x_l, x_{l+64}, ... in
+ * increasing index, then for d = 32, 16, 8, 4, 2, 1 every p_l becomes
+ * p_l + p_{l xor d} (all at once); ss = p_0.  Returns ss.
+ */
+float q4o_rmsnorm(const float* x, int64_t n, float* out)
+{
+    float p[64], q[64];
+    for (int l = 0; l < 64; ++l) {
+        p[l] = 0.0f;
+        for (int64_t i = l; i < n; i += 64)
+            p[l] = fmaf(x[i], x[i], p[l]);
+    }
+    for (int d = 32; d >= 1; d /= 2) {
+        for (int l = 0; l < 64; ++l)
+            q[l] = p[l] + p[l ^ d];
+        memcpy(p, q, sizeof p);
+    }
+    const float ss = p[0];
+    const float s = sqrtf(ss / (float)n + 1e-6f);
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = x[i] / s;
+    return ss;
+}
+
+/* y = W * Q8(x) for one token, in the fixed fp32 order (scratch: cols/32 Q8_0 blocks) */
+static void chain_gemv(const uint8_t* w, int64_t rows, int64_t cols, const float* x, uint8_t* scratch, float* y)
+{
+    q4o_quantize_q8_0(x, scratch, cols);
+    q4o_gemv_f32(w, scratch, rows, cols, 1, y);
+}
+
+/*
+ * One chained decode step for one token.  The pages' mega kernel runs a
+ * token's layers as dependent phases (norm prologue, activation quantize,
+ * GEMV, residual; "How it works", src/mega.cu bullet, M15, M19).  The chain
+ * keeps the projections and the glue between them; RoPE, attention and the
+ * SiLU are outside it (q goes straight to the output projection, where
+ * attention's result would enter, and the MLP product is g * u).  Per layer,
+ * with h the layer input (h_0 given):
+ *   q = Wq Q8(norm h),  k = Wk Q8(norm h),  v = Wv Q8(norm h)
+ *   o = Wo Q8(q),       h1 = h + o
+ *   g = Wg Q8(norm h1), u = Wu Q8(norm h1)
+ *   dn = Wd Q8(g * u),  h2 = h1 + dn          (the next layer's h)
+ * and the logits z = Wout Q8(norm h_L).  + and * are single fp32 operations.
+ *
+ * w    : 7 * layers + 1 canonical Q4_0 matrices: per layer q [E x E], k, v
+ *        [D x E], o [E x E], gate, up [F x E], down [E x F]; then the head [V x E]
+ * acts : per layer [q E | k D | v D | o E | h1 E | g F | u F | dn E | h2 E]
+ */
+void q4o_chain_step(const uint8_t* const* w, int layers, int64_t E, int64_t D, int64_t F, int64_t V,
+                    const float* h0, float* acts, float* logits)
+{
+    const int64_t big = E > F ? E : F;
+    float* nrm = (float*)malloc((size_t)big * sizeof(float));
+    float* prod = (float*)malloc((size_t)F * sizeof(float));
+    uint8_t* xq = (uint8_t*)malloc((size_t)(big / QK) * Q8_BLOCK_BYTES);
+    const int64_t per_layer = 5 * E + 2 * D + 2 * F;
+    const float* h = h0;
+    for (int l = 0; l < layers; ++l) {
+        const uint8_t* const* lw = w + 7 * l;
+        float* a = acts + l * per_layer;
+        float *q = a, *k = q + E, *v = k + D, *o = v + D, *h1 = o + E, *g = h1 + E, *u = g + F, *dn = u + F,
+              *h2 = dn + E;
+        q4o_rmsnorm(h, E, nrm);
+        chain_gemv(lw[0], E, E, nrm, xq, q);
+        chain_gemv(lw[1], D, E, nrm, xq, k);
+        chain_gemv(lw[2], D, E, nrm, xq, v);
+        chain_gemv(lw[3], E, E, q, xq, o);
+        for (int64_t i = 0; i < E; ++i)
+            h1[i] = h[i] + o[i];
+        q4o_rmsnorm(h1, E, nrm);
+        chain_gemv(lw[4], F, E, nrm, xq, g);
+        chain_gemv(lw[5], F, E, nrm, xq, u);
+        for (int64_t i = 0; i < F; ++i)
+            prod[i] = g[i] * u[i];
+        chain_gemv(lw[6], E, F, prod, xq, dn);
+        for (int64_t i = 0; i < E; ++i)
+            h2[i] = h1[i] + dn[i];
+        h = h2;
+    }
+    q4o_rmsnorm(h, E, nrm);
+    chain_gemv(w[7 * layers], V, E, nrm, xq, logits);
+    free(nrm);
+    free(prod);
+    free(xq);
 }
 
 /* ------------------------------------------------------------------ */

@@ -13,6 +13,7 @@ import test_oracle_q4 as t4
 import test_oracle_q8 as t8
 import test_oracle_q8w as t8w
 import test_oracle_attn as tat
+import test_oracle_pinned as tpn
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
                    "q4_oracle.c")
@@ -62,6 +63,30 @@ MUTANTS = [
     ("attn_no_max_subtraction", "denom += exp(scale * dot - smax);", "denom += exp(scale * dot);"),
     ("attn_scale_dropped", "double sc = scale * dot;", "double sc = dot;"),
     ("attn_unnormalized", "double p = exp(scale * dot - smax) / denom;", "double p = exp(scale * dot - smax);"),
+    ("pinned_one_chain", "if (k < 4)\n                    chain_a", "if (1)\n                    chain_a"),
+    ("pinned_even_odd_chains", "if (k < 4)\n                    chain_a", "if (k % 2 == 0)\n                    chain_a"),
+    ("pinned_segments_of_8", "(c + 1 - c0) % 16 == 0", "(c + 1 - c0) % 8 == 0"),
+    ("pinned_no_segments", "if (c + 1 == c1 || (c + 1 - c0) % 16 == 0)", "if (c + 1 == c1)"),
+    ("pinned_split_rounds_up", "const int64_t c0 = s * nc / ks, c1 = (s + 1) * nc / ks;",
+     "const int64_t c0 = (s * nc + ks - 1) / ks, c1 = ((s + 1) * nc + ks - 1) / ks;"),
+    ("pinned_four_splits_early", "nc <= 8 ? 1 : (nc <= 16 ? 2 : 4)", "nc <= 8 ? 1 : 4"),
+    ("pinned_two_splits_late", "nc <= 8 ? 1 : (nc <= 16 ? 2 : 4)", "nc <= 8 ? 1 : (nc <= 32 ? 2 : 4)"),
+    ("pinned_splits_pairwise", "y = s == 0 ? total : y + total;", "y = s == 0 ? total : (s == 3 ? y + total : (s == 2 ? total : y + total));"),
+    ("pinned_drops_partial_chunk", "for (int64_t k = 0; k < 8 && c * 8 + k < nb; ++k) {",
+     "for (int64_t k = 0; k < 8 && c * 8 + k < nb - 1; ++k) {"),
+    ("rms_sequential", "p[l] = fmaf(x[i], x[i], p[l]);", "p[0] = fmaf(x[i], x[i], p[0]);"),
+    ("rms_reverse_tree", "for (int d = 32; d >= 1; d /= 2) {", "for (int d = 1; d <= 32; d *= 2) {"),
+    ("rms_epsilon", "sqrtf(ss / (float)n + 1e-6f)", "sqrtf(ss / (float)n + 1e-5f)"),
+    ("rms_no_mean", "sqrtf(ss / (float)n + 1e-6f)", "sqrtf(ss + 1e-6f)"),
+    ("chain_o_reads_k", "chain_gemv(lw[3], E, E, q, xq, o);", "chain_gemv(lw[3], E, E, k, xq, o);"),
+    ("chain_no_attention_residual", "h1[i] = h[i] + o[i];", "h1[i] = o[i];"),
+    ("chain_gate_only", "prod[i] = g[i] * u[i];", "prod[i] = g[i];"),
+    ("chain_qkv_unnormed", "q4o_rmsnorm(h, E, nrm);\n        chain_gemv(lw[0], E, E, nrm, xq, q);",
+     "memcpy(nrm, h, (size_t)E * sizeof(float));\n        chain_gemv(lw[0], E, E, nrm, xq, q);"),
+    ("chain_mlp_reads_h", "q4o_rmsnorm(h1, E, nrm);", "q4o_rmsnorm(h, E, nrm);"),
+    ("chain_mlp_residual_from_h", "h2[i] = h1[i] + dn[i];", "h2[i] = h[i] + dn[i];"),
+    ("chain_head_unnormed", "q4o_rmsnorm(h, E, nrm);\n    chain_gemv(w[7 * layers], V, E, nrm, xq, logits);",
+     "chain_gemv(w[7 * layers], V, E, h, xq, logits);"),
 ]
 
 
@@ -90,7 +115,16 @@ def _pins(o, b):
               ("attn_dominant", lambda: tat.test_attn_one_dominant_key_closed_form(o)),
               ("attn_large", lambda: tat.test_attn_large_scores_stay_finite(o)),
               ("attn_gqa", lambda: tat.test_attn_gqa_groups(o)),
-              ("attn_brute", lambda: tat.test_attn_matches_bruteforce(o, 7, 12, 2, 128))]
+              ("attn_brute", lambda: tat.test_attn_matches_bruteforce(o, 7, 12, 2, 128)),
+              ("pinned_exact", lambda: tpn.test_pinned_exact_with_unit_scales(o, 9, 4608, 1)),
+              ("pinned_bound", lambda: tpn.test_pinned_within_fp32_bound_of_fp64(o, 40, 800, 3)),
+              ("rms_golden", lambda: tpn.test_rmsnorm_order_golden(o)),
+              ("rms_closed_form", lambda: tpn.test_rmsnorm_constant_vector_closed_form(o, 3.0, 128)),
+              ("rms_closed_form_small", lambda: tpn.test_rmsnorm_constant_vector_closed_form(o, 1e-4, 3584)),
+              ("chain_unquantized", lambda: tpn.test_chain_matches_unquantized_fp64(o, b)),
+              ("chain_one_gemv", lambda: tpn.test_chain_without_residual_branches_is_one_gemv(o))]
+    checks += [(f"pinned_golden_{c['name']}", (lambda c=c: tpn.test_pinned_order_golden(o, c)))
+               for c in tpn.CASES]
     checks += [(f"q8_golden_{c['name']}", (lambda c=c: t8.test_q8_0_golden_blocks(o, c)))
                for c in t8.CASES]
     checks += [(f"q4_golden_{c['name']}", (lambda c=c: t4.test_q4_0_golden_decode(o, c)))
