@@ -86,7 +86,7 @@
 extern "C" {
 #endif
 
-#define Q4S_ABI_VERSION 2
+#define Q4S_ABI_VERSION 3
 #define Q4S_MAX_N 24   /* activation rows per Q4_0 product (one weight pass) */
 #define Q4S_MAX_N_Q8 8 /* activation rows per Q8_0-weight product */
 
@@ -97,7 +97,8 @@ typedef enum {
     Q4S_ERR_ALIGN = 3,     /* pointer misaligned for its layout             */
     Q4S_ERR_ALIAS = 4,     /* an output buffer overlaps an input buffer     */
     Q4S_ERR_PLAN = 5,      /* invalid plan, plan memory or matrix table     */
-    Q4S_ERR_HIP = 6        /* the HIP runtime reported an error             */
+    Q4S_ERR_HIP = 6,       /* the HIP runtime reported an error             */
+    Q4S_ERR_WAIT = 7       /* a bounded wait of a chained step gave up      */
 } q4s_status;
 
 /* ---------------------------------------------------------------- general */
@@ -328,6 +329,105 @@ q4s_status q4s_sweep_run(const q4s_plan* plan, void* stream);
 q4s_status q4s_sweep_plan_info(const q4s_plan* plan, q4s_plan_info* info);
 
 void q4s_sweep_plan_destroy(q4s_plan* plan);
+
+/* ------------------------------------------------------ chained step */
+
+/*
+ * One decode step for one token with its layers as dependent phases inside a
+ * single persistent launch (the pages' mega kernel: "How it works",
+ * src/mega.cu bullet; milestones M15 and M19).  A Qwen2-shaped stack of
+ * `layers` layers, hidden size E, k/v size D, MLP size F, vocabulary V.  Per
+ * layer, with h the layer input (h_0 given):
+ *   q = Wq Q8(norm h),  k = Wk Q8(norm h),  v = Wv Q8(norm h)
+ *   o = Wo Q8(q),       h1 = h + o
+ *   g = Wg Q8(norm h1), u = Wu Q8(norm h1)
+ *   dn = Wd Q8(g * u),  h2 = h1 + dn          (the next layer's h)
+ * then logits = Wout Q8(norm h_L).  norm(x) = x / sqrt(mean(x^2) + 1e-6)
+ * (RMS norm without a learned weight; the sum of squares in a fixed order);
+ * Q8 is the Q8_0 quantization of q4s_quantize_q8_0; every GEMV is the
+ * q4s_gemv_q4_0 product of that activation, bit for bit; + and * are single
+ * fp32 operations.  RoPE, attention and the SiLU are not part of the chain:
+ * q feeds the output projection where attention's result would, and the MLP
+ * product is g * u.
+ *
+ * Phase synchronisation (sync_mode):
+ *   Q4S_CHAIN_COUNTER  M19's monotonic arrival counter: one device-scope
+ *                      release add per workgroup and phase, one acquire fence;
+ *   Q4S_CHAIN_TREE     a combining tree of such counters (16 + 1);
+ *   Q4S_CHAIN_TAGGED   no barrier: every activation word carries the step's tag
+ *                      and readers poll the words they need (relaxed
+ *                      device-scope atomics, no fences).
+ * The three modes give identical results.
+ */
+typedef struct {
+    int32_t layers; /* >= 0 (0: the head alone)            */
+    int32_t hidden; /* E, a multiple of 32                  */
+    int32_t kv_dim; /* D >= 1 (rows of Wk and Wv)           */
+    int32_t ff;     /* F, a multiple of 32                  */
+    int32_t vocab;  /* V >= 1                               */
+} q4s_chain_shape;
+
+#define Q4S_CHAIN_COUNTER 0
+#define Q4S_CHAIN_TREE 1
+#define Q4S_CHAIN_TAGGED 2
+
+typedef struct q4s_chain q4s_chain; /* opaque; host memory only */
+
+typedef struct {
+    int64_t n_mats;       /* 7 * layers + 1                              */
+    int64_t n_phases;     /* 4 * layers + 1                              */
+    int64_t n_tiles;      /* GEMV workgroup tiles over all phases        */
+    int64_t workgroups;   /* persistent workgroups (after upload)        */
+    int64_t act_words;    /* 64-bit words of the activation buffer       */
+    int64_t packed_bytes; /* packed weight bytes read by one step        */
+    int64_t dev_bytes;    /* device memory the chain's tables need       */
+    int64_t steps;        /* steps run since the upload                  */
+} q4s_chain_info;
+
+/*
+ * 64-bit words of the activation buffer: per layer [q E | k D | v D | o E |
+ * h1 E | g F | u F | dn E | h2 E], layers one after another.  Word = fp32
+ * bits in the low 32 bits, the step's tag in the high 32 bits.  0 on a bad shape.
+ */
+int64_t q4s_chain_act_words(const q4s_chain_shape* shape);
+
+/*
+ * Build a chained step.  w_packed: 7 * layers + 1 packed Q4_0 matrices
+ * (q4s_repack_q4_0 output, 16-byte aligned): per layer q [E x E], k, v
+ * [D x E], o [E x E], gate, up [F x E], down [E x F], then the head [V x E].
+ * h0: fp32 [E] (16-byte aligned), read by every step.  acts: the activation
+ * buffer (q4s_chain_act_words words, 16-byte aligned), written by every step.
+ * logits: fp32 [V].  Outputs may not overlap inputs or each other.
+ * workgroups: 0 for one per compute unit, else the count (at most the number
+ * resident at once, checked at upload).  *dev_bytes_needed receives the
+ * device memory q4s_chain_upload needs.  The buffers must stay valid while
+ * the chain is used.
+ */
+q4s_status q4s_chain_create(const q4s_chain_shape* shape, const void* const* w_packed, const float* h0,
+                            uint64_t* acts, float* logits, int sync_mode, int workgroups,
+                            size_t* dev_bytes_needed, q4s_chain** out);
+
+/*
+ * Copy the chain's tables into dev_mem (16-byte aligned, caller-owned, kept
+ * alive while the chain is used) and zero `acts`, both on `stream`.  Needs
+ * the GPU: resolves and checks the workgroup count.
+ */
+q4s_status q4s_chain_upload(q4s_chain* chain, void* dev_mem, size_t dev_bytes, void* stream);
+
+/*
+ * One step: a small clearing launch, then one cooperative launch of the
+ * persistent workgroups on `stream`.  Each step gets a new tag.  Steps on one
+ * chain must not overlap in time.  Waits inside the launch are bounded; when
+ * one gives up the step's results are invalid and q4s_chain_check reports it.
+ */
+q4s_status q4s_chain_run(q4s_chain* chain, void* stream);
+
+/* Synchronize `stream`; Q4S_ERR_WAIT if a wait of the last step gave up. */
+q4s_status q4s_chain_check(const q4s_chain* chain, void* stream);
+
+q4s_status q4s_chain_get_info(const q4s_chain* chain, q4s_chain_info* info);
+
+void q4s_chain_destroy(q4s_chain* chain);
 
 /* -------------------------------------------------- measurement helpers */
 

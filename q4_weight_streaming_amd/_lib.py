@@ -42,6 +42,22 @@ class PlanInfo(ctypes.Structure):
         return {k: int(getattr(self, k)) for k, _ in self._fields_}
 
 
+class ChainShape(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_int32) for k in ("layers", "hidden", "kv_dim", "ff", "vocab")]
+
+
+class ChainInfo(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_int64) for k in
+                ("n_mats", "n_phases", "n_tiles", "workgroups", "act_words", "packed_bytes", "dev_bytes", "steps")]
+
+    def as_dict(self) -> dict:
+        return {k: int(getattr(self, k)) for k, _ in self._fields_}
+
+
+CHAIN_COUNTER, CHAIN_TREE, CHAIN_TAGGED = 0, 1, 2
+ERR_WAIT = 7
+
+
 def lib():
     """The loaded library; raises if libq4stream.so has not been built."""
     global _lib
@@ -75,6 +91,14 @@ def lib():
             "q4s_sweep_run": ([p, p], i32),
             "q4s_sweep_plan_info": ([p, ctypes.POINTER(PlanInfo)], i32),
             "q4s_sweep_plan_destroy": ([p], None),
+            "q4s_chain_act_words": ([ctypes.POINTER(ChainShape)], i64),
+            "q4s_chain_create": ([ctypes.POINTER(ChainShape), p, p, p, p, i32, i32, ctypes.POINTER(sz),
+                                  ctypes.POINTER(p)], i32),
+            "q4s_chain_upload": ([p, p, sz, p], i32),
+            "q4s_chain_run": ([p, p], i32),
+            "q4s_chain_check": ([p, p], i32),
+            "q4s_chain_get_info": ([p, ctypes.POINTER(ChainInfo)], i32),
+            "q4s_chain_destroy": ([p], None),
             "q4s_bench_read": ([p, sz, i32, i32, p, p], i32),
             "q4s_bench_copy": ([p, p, sz, p], i32),
             "q4s_bench_grid_barrier": ([i32, i32, i32, p, sz, p], i32),
@@ -85,7 +109,7 @@ def lib():
             f = getattr(L, name)
             f.argtypes = args
             f.restype = res
-        if L.q4s_abi_version() != 2:
+        if L.q4s_abi_version() != 3:
             raise RuntimeError("libq4stream ABI version mismatch")
         _lib = L
     return _lib
@@ -313,6 +337,72 @@ class Sweep:
         if self._plan:
             lib().q4s_sweep_plan_destroy(self._plan)
             self._plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def chain_act_words(layers: int, hidden: int, kv_dim: int, ff: int, vocab: int) -> int:
+    return int(lib().q4s_chain_act_words(ctypes.byref(ChainShape(layers, hidden, kv_dim, ff, vocab))))
+
+
+def chain_layout(hidden: int, kv_dim: int, ff: int):
+    """Offsets (in words) of q, k, v, o, h1, g, u, dn, h2 within one layer of the activation buffer."""
+    E, D, F = hidden, kv_dim, ff
+    sizes = [("q", E), ("k", D), ("v", D), ("o", E), ("h1", E), ("g", F), ("u", F), ("dn", E), ("h2", E)]
+    out, off = {}, 0
+    for name, n in sizes:
+        out[name] = (off, n)
+        off += n
+    return out, off
+
+
+def chain_values(acts: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """Split tagged activation words (int64) into (fp32 values, int64 tags)."""
+    halves = acts.contiguous().view(torch.int32).view(-1, 2)   # little-endian: [low, high]
+    return halves[:, 0].contiguous().view(torch.float32), halves[:, 1].to(torch.int64) & 0xFFFFFFFF
+
+
+class Chain:
+    """One chained decode step (see q4s_chain_create): w_packed is the list of 7*layers + 1
+    packed matrices; h0 fp32 [hidden]; acts int64 [chain_act_words]; logits fp32 [vocab]."""
+
+    def __init__(self, layers: int, hidden: int, kv_dim: int, ff: int, vocab: int, w_packed, h0: torch.Tensor,
+                 acts: torch.Tensor, logits: torch.Tensor, sync_mode: int = CHAIN_TAGGED, workgroups: int = 0):
+        self.shape = ChainShape(layers, hidden, kv_dim, ff, vocab)
+        self._keep = (list(w_packed), h0, acts, logits)
+        ws = (ctypes.c_void_p * len(w_packed))(*[_dev(w, "w_packed", torch.uint8) for w in w_packed])
+        need = ctypes.c_size_t(0)
+        handle = ctypes.c_void_p(None)
+        _check("q4s_chain_create", lib().q4s_chain_create(
+            ctypes.byref(self.shape), ws, _dev(h0, "h0", torch.float32), _dev(acts, "acts", torch.int64),
+            _dev(logits, "logits", torch.float32), sync_mode, workgroups, ctypes.byref(need), ctypes.byref(handle)))
+        self._chain = handle
+        self.device = h0.device
+        self.dev_mem = torch.empty(int(need.value), dtype=torch.uint8, device=self.device)
+        _check("q4s_chain_upload", lib().q4s_chain_upload(self._chain, self.dev_mem.data_ptr(), int(need.value),
+                                                          _stream(self.device)))
+        torch.cuda.current_stream(self.device).synchronize()
+
+    def info(self) -> dict:
+        inf = ChainInfo()
+        _check("q4s_chain_get_info", lib().q4s_chain_get_info(self._chain, ctypes.byref(inf)))
+        return inf.as_dict()
+
+    def run(self) -> None:
+        _check("q4s_chain_run", lib().q4s_chain_run(self._chain, _stream(self.device)))
+
+    def check(self) -> None:
+        """Synchronize; raise Q4SError (status 7) if a bounded wait of the last step gave up."""
+        _check("q4s_chain_check", lib().q4s_chain_check(self._chain, _stream(self.device)))
+
+    def close(self) -> None:
+        if self._chain:
+            lib().q4s_chain_destroy(self._chain)
+            self._chain = None
 
     def __del__(self):
         try:

@@ -134,6 +134,7 @@ const char* q4s_status_string(int s) {
         case Q4S_ERR_ALIAS: return "output overlaps input";
         case Q4S_ERR_PLAN: return "invalid plan";
         case Q4S_ERR_HIP: return "HIP runtime error";
+        case Q4S_ERR_WAIT: return "a bounded wait gave up";
         default: return "unknown status";
     }
 }
@@ -493,6 +494,233 @@ q4s_status q4s_sweep_plan_info(const q4s_plan* p, q4s_plan_info* info) {
 }
 
 void q4s_sweep_plan_destroy(q4s_plan* p) { delete p; }
+
+// ============================================================ chained step
+
+struct q4s_chain {
+    q4s_chain_shape shape{};
+    int mode = 0;
+    int workgroups_req = 0;
+    int workgroups = 0;
+    uint64_t* acts = nullptr;
+    int64_t act_words = 0;
+    std::vector<ChainMat> mats;
+    std::vector<uint32_t> tiles;      // (matrix, group set), phase by phase, largest first within a phase
+    std::vector<uint32_t> phase_end;  // cumulative tile count per phase
+    q4s_chain_info info{};
+    // device image: [ChainMat x n][tiles][phase_end][sync words], 16-byte aligned parts
+    size_t off_tiles = 0, off_phase = 0, off_sync = 0, dev_bytes = 0;
+    std::vector<uint8_t> image;
+    uint8_t* dev = nullptr;
+    uint32_t gen = 0;
+    int64_t steps = 0;
+};
+
+static bool chain_shape_ok(const q4s_chain_shape* s) {
+    return s && s->layers >= 0 && s->layers <= (1 << 16) && s->hidden >= 32 && s->hidden % 32 == 0 &&
+           s->hidden <= (1 << 20) && s->ff >= 32 && s->ff % 32 == 0 && s->ff <= (1 << 20) && s->kv_dim >= 1 &&
+           s->kv_dim <= (1 << 20) && s->vocab >= 1 && s->vocab <= (1 << 24);
+}
+
+static int64_t chain_layer_words(const q4s_chain_shape* s) {
+    return 5 * (int64_t)s->hidden + 2 * (int64_t)s->kv_dim + 2 * (int64_t)s->ff;
+}
+
+int64_t q4s_chain_act_words(const q4s_chain_shape* s) {
+    if (!chain_shape_ok(s)) return 0;
+    return (int64_t)s->layers * chain_layer_words(s);
+}
+
+q4s_status q4s_chain_create(const q4s_chain_shape* shape, const void* const* w_packed, const float* h0,
+                            uint64_t* acts, float* logits, int sync_mode, int workgroups,
+                            size_t* dev_bytes_needed, q4s_chain** out) {
+    if (!out || !dev_bytes_needed || !shape || !w_packed) return fail(Q4S_ERR_NULL, "shape, w_packed, dev_bytes_needed and out are required");
+    *out = nullptr;
+    if (!chain_shape_ok(shape))
+        return fail(Q4S_ERR_SHAPE, "chain shape needs layers >= 0, hidden and ff multiples of 32, kv_dim and vocab >= 1");
+    if (sync_mode < Q4S_CHAIN_COUNTER || sync_mode > Q4S_CHAIN_TAGGED)
+        return fail(Q4S_ERR_SHAPE, "sync_mode=%d is not a chain sync mode", sync_mode);
+    if (workgroups < 0 || workgroups > (1 << 16)) return fail(Q4S_ERR_SHAPE, "workgroups=%d out of range", workgroups);
+    const int64_t L = shape->layers, E = shape->hidden, D = shape->kv_dim, F = shape->ff, V = shape->vocab;
+    const int64_t n_mats = 7 * L + 1;
+    const int64_t words = L * chain_layer_words(shape);
+    q4s_status s;
+    if ((s = check_ptr(h0, (size_t)E * 4, 16, "h0"))) return s;
+    if ((s = check_ptr(acts, (size_t)words * 8, 16, "acts"))) return s;
+    if ((s = check_ptr(logits, (size_t)V * 4, 4, "logits"))) return s;
+    const int64_t dims[7][2] = {{E, E}, {D, E}, {D, E}, {E, E}, {F, E}, {F, E}, {E, F}};
+    std::vector<std::pair<const void*, size_t>> ins = {{h0, (size_t)E * 4}};
+    for (int64_t i = 0; i < n_mats; ++i) {
+        const int64_t r = i == 7 * L ? V : dims[i % 7][0], c = i == 7 * L ? E : dims[i % 7][1];
+        if ((s = check_ptr(w_packed[i], packed_bytes(r, c), 16, "w_packed"))) return prefix_matrix(s, (int)i);
+        ins.push_back({w_packed[i], packed_bytes(r, c)});
+    }
+    for (const auto& in : ins)
+        if (overlap(acts, (size_t)words * 8, in.first, in.second) || overlap(logits, (size_t)V * 4, in.first, in.second))
+            return fail(Q4S_ERR_ALIAS, "an output of the chain overlaps an input");
+    if (overlap(acts, (size_t)words * 8, logits, (size_t)V * 4)) return fail(Q4S_ERR_ALIAS, "acts overlaps logits");
+
+    q4s_chain* p = new (std::nothrow) q4s_chain;
+    if (!p) return fail(Q4S_ERR_PLAN, "out of host memory");
+    p->shape = *shape;
+    p->mode = sync_mode;
+    p->workgroups_req = workgroups;
+    p->acts = acts;
+    p->act_words = words;
+    const int64_t per = chain_layer_words(shape);
+    auto word = [&](int64_t l, int64_t off) { return acts + l * per + off; };
+    const int64_t oq = 0, ok_ = E, ov = E + D, oo = E + 2 * D, oh1 = 2 * E + 2 * D, og = 3 * E + 2 * D,
+                  ou = 3 * E + 2 * D + F, odn = 3 * E + 2 * D + 2 * F, oh2 = 4 * E + 2 * D + 2 * F;
+    auto base = [&](const void* w, int64_t r, int64_t c) {
+        ChainMat cm{};
+        cm.m = make_desc(w, nullptr, nullptr, r, c, 1);
+        cm.m.xd = nullptr;
+        p->info.packed_bytes += (int64_t)packed_bytes(r, c);
+        return cm;
+    };
+    struct Tile { uint32_t mat, gset; int64_t bytes; };
+    std::vector<Tile> phase;
+    auto add = [&](const ChainMat& cm) {
+        const uint32_t i = (uint32_t)p->mats.size();
+        p->mats.push_back(cm);
+        const int gpw = kWaves / cm.m.ks;
+        const int64_t ng = gsets_of(cm.m.G, cm.m.ks);
+        for (int64_t gs = 0; gs < ng; ++gs) {
+            const int64_t groups = std::min<int64_t>(gpw, cm.m.G - gs * gpw);
+            phase.push_back({i, (uint32_t)gs, groups * cm.m.C * kChunkBytes});
+        }
+    };
+    auto close = [&]() {
+        std::stable_sort(phase.begin(), phase.end(), [](const Tile& a, const Tile& b) { return a.bytes > b.bytes; });
+        for (const Tile& t : phase) {
+            p->tiles.push_back(t.mat);
+            p->tiles.push_back(t.gset);
+        }
+        p->phase_end.push_back((uint32_t)(p->tiles.size() / 2));
+        phase.clear();
+    };
+    for (int64_t l = 0; l < L; ++l) {
+        const void* const* lw = w_packed + 7 * l;
+        const void* h = l == 0 ? (const void*)h0 : (const void*)word(l - 1, oh2);
+        const int hp = l == 0 ? 1 : 0;
+        // q, k, v: one activation of norm(h)
+        const int64_t qkv_rows[3] = {E, D, D}, qkv_off[3] = {oq, ok_, ov};
+        for (int j = 0; j < 3; ++j) {
+            ChainMat cm = base(lw[j], qkv_rows[j], E);
+            cm.x = h, cm.x_plain = hp, cm.norm = 1, cm.y = word(l, qkv_off[j]);
+            add(cm);
+        }
+        close();
+        {   // o = Wo Q8(q); h1 = h + o
+            ChainMat cm = base(lw[3], E, E);
+            cm.x = word(l, oq), cm.y = word(l, oo), cm.res = h, cm.res_plain = hp, cm.y2 = word(l, oh1);
+            add(cm);
+        }
+        close();
+        for (int j = 0; j < 2; ++j) {  // gate, up: one activation of norm(h1)
+            ChainMat cm = base(lw[4 + j], F, E);
+            cm.x = word(l, oh1), cm.norm = 1, cm.y = word(l, j == 0 ? og : ou);
+            add(cm);
+        }
+        close();
+        {   // dn = Wd Q8(g * u); h2 = h1 + dn
+            ChainMat cm = base(lw[6], E, F);
+            cm.x = word(l, og), cm.x2 = word(l, ou), cm.y = word(l, odn), cm.res = word(l, oh1),
+            cm.y2 = word(l, oh2);
+            add(cm);
+        }
+        close();
+    }
+    {
+        ChainMat cm = base(w_packed[7 * L], V, E);
+        cm.x = L == 0 ? (const void*)h0 : (const void*)word(L - 1, oh2), cm.x_plain = L == 0 ? 1 : 0, cm.norm = 1,
+        cm.yf = logits;
+        add(cm);
+        close();
+    }
+    auto up16 = [](size_t v) { return (v + 15) & ~(size_t)15; };
+    p->off_tiles = up16(p->mats.size() * sizeof(ChainMat));
+    p->off_phase = p->off_tiles + up16(p->tiles.size() * sizeof(uint32_t));
+    p->off_sync = p->off_phase + up16(p->phase_end.size() * sizeof(uint32_t));
+    p->dev_bytes = p->off_sync + up16(kChainSyncWords * sizeof(uint32_t));
+    p->image.assign(p->dev_bytes, 0);
+    memcpy(p->image.data(), p->mats.data(), p->mats.size() * sizeof(ChainMat));
+    memcpy(p->image.data() + p->off_tiles, p->tiles.data(), p->tiles.size() * sizeof(uint32_t));
+    memcpy(p->image.data() + p->off_phase, p->phase_end.data(), p->phase_end.size() * sizeof(uint32_t));
+    p->info.n_mats = n_mats;
+    p->info.n_phases = (int64_t)p->phase_end.size();
+    p->info.n_tiles = (int64_t)p->tiles.size() / 2;
+    p->info.act_words = words;
+    p->info.dev_bytes = (int64_t)p->dev_bytes;
+    *dev_bytes_needed = p->dev_bytes;
+    *out = p;
+    return ok();
+}
+
+q4s_status q4s_chain_upload(q4s_chain* p, void* dev_mem, size_t dev_bytes, void* stream) {
+    if (!p) return fail(Q4S_ERR_NULL, "chain is NULL");
+    if (!dev_mem) return fail(Q4S_ERR_NULL, "dev_mem is NULL");
+    if (!aligned(dev_mem, 16)) return fail(Q4S_ERR_ALIGN, "dev_mem must be 16-byte aligned");
+    if (dev_bytes < p->dev_bytes)
+        return fail(Q4S_ERR_PLAN, "dev_mem holds %zu bytes, the chain needs %zu", dev_bytes, p->dev_bytes);
+    int max_wg = 0;
+    hipError_t e = chain_max_workgroups(p->mode, &max_wg);
+    if (e != hipSuccess) return hip_status(e, "occupancy query");
+    int cus = 0, dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return hip_status(e, "hipGetDevice");
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+        return hip_status(e, "device attribute");
+    const int wg = p->workgroups_req ? p->workgroups_req : std::min(cus, max_wg);
+    if (wg < 1 || wg > max_wg)
+        return fail(Q4S_ERR_SHAPE, "workgroups=%d out of [1, %d] (all must be resident at once)", wg, max_wg);
+    hipStream_t st = (hipStream_t)stream;
+    if ((e = hipMemcpyAsync(dev_mem, p->image.data(), p->dev_bytes, hipMemcpyHostToDevice, st)) != hipSuccess)
+        return hip_status(e, "chain upload");
+    if (p->act_words > 0 && (e = hipMemsetAsync(p->acts, 0, (size_t)p->act_words * 8, st)) != hipSuccess)
+        return hip_status(e, "acts clear");
+    p->dev = (uint8_t*)dev_mem;
+    p->workgroups = wg;
+    p->info.workgroups = wg;
+    p->gen = 0;
+    p->steps = 0;
+    return ok();
+}
+
+q4s_status q4s_chain_run(q4s_chain* p, void* stream) {
+    if (!p) return fail(Q4S_ERR_NULL, "chain is NULL");
+    if (!p->dev) return fail(Q4S_ERR_PLAN, "chain was not uploaded");
+    if (++p->gen == 0) p->gen = 1;  // tag 0 marks words never written
+    ChainParams cp;
+    cp.mats = (const ChainMat*)p->dev;
+    cp.tiles = (const uint32_t*)(p->dev + p->off_tiles);
+    cp.phase_end = (const uint32_t*)(p->dev + p->off_phase);
+    cp.sync = (uint32_t*)(p->dev + p->off_sync);
+    cp.n_phases = (int32_t)p->phase_end.size();
+    cp.gen = p->gen;
+    q4s_status s = hip_status(launch_chain(p->mode, cp, p->workgroups, (hipStream_t)stream), "chain launch");
+    if (s == Q4S_OK) ++p->steps;
+    return s;
+}
+
+q4s_status q4s_chain_check(const q4s_chain* p, void* stream) {
+    if (!p) return fail(Q4S_ERR_NULL, "chain is NULL");
+    if (!p->dev) return fail(Q4S_ERR_PLAN, "chain was not uploaded");
+    uint32_t err = 0;
+    hipError_t e = hipMemcpyAsync(&err, p->dev + p->off_sync, 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "chain check");
+    if (err) return fail(Q4S_ERR_WAIT, "a bounded wait of the chained step gave up");
+    return ok();
+}
+
+q4s_status q4s_chain_get_info(const q4s_chain* p, q4s_chain_info* info) {
+    if (!p || !info) return fail(Q4S_ERR_NULL, "chain and info are required");
+    *info = p->info;
+    info->steps = p->steps;
+    return ok();
+}
+
+void q4s_chain_destroy(q4s_chain* p) { delete p; }
 
 // ============================================================= measurement
 

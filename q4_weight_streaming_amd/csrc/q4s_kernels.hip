@@ -607,6 +607,297 @@ __global__ __launch_bounds__(kThreads, 1) void k_sweep_fused(const MatDesc* __re
     });
 }
 
+// ---------------------------------------------------------------- chained step
+//
+// One decode step's layers as dependent phases in one persistent cooperative
+// launch, as the pages' mega kernel runs a token ("How it works", src/mega.cu
+// bullet; milestones M15 and M19): per layer the q/k/v GEMVs share one Q8_0
+// activation of the normalized layer input, the output projection reads q,
+// gate and up share one activation of the normalized residual stream, and down
+// reads their product; the residual adds ride in the output projections'
+// epilogues.  The norm (RMS, no learned weight, fixed-order sum of squares)
+// and the quantization run in every wave's prologue on the activation blocks
+// it streams, so a phase starts with its weight loads in flight.
+//
+// A wave's GEMV is the lane-per-row task of the sweep (same chains, segments
+// and K splits), so every output is bit-identical to the standalone GEMV of
+// the same Q8_0 activation.  Workgroups take the tiles of a phase round-robin,
+// starting where the previous phase's tiles ended, so phase p+1's tiles land
+// on workgroups that had none in phase p.
+//
+// Activations that cross phases are tagged words (fp32 bits | step tag << 32).
+// Phases are separated by
+//  * kChainCounter: milestone M19's monotonic arrival counter -- one
+//    device-scope release add per workgroup, polls, one acquire fence;
+//  * kChainTree: a combining tree of such counters (16 sub-counters, the last
+//    arrival of each adds to a top counter whose last arrival releases);
+//  * kChainTagged: no barrier -- outputs are stored as relaxed device-scope
+//    atomic words and every reader polls the words it needs until they carry
+//    this step's tag.  Each word is its own flag, so no fence is needed; this
+//    avoids the per-workgroup L2 write-back and invalidate that device-scope
+//    release and acquire cost on the multi-XCD chip.
+// Every wait is bounded: past the limit the error word is set, every other
+// wait then gives up within ~1000 polls, and the launch runs to its end with
+// whatever values it has.
+
+constexpr int64_t kChainSpin = 1 << 20;
+
+__device__ __forceinline__ uint64_t tag_word(float v, uint32_t gen) {
+    return ((uint64_t)gen << 32) | (uint64_t)__float_as_uint(v);
+}
+
+template <int kSync>
+__device__ __forceinline__ uint64_t chain_ld(const uint64_t* p) {
+    if constexpr (kSync == kChainTagged)
+        return __hip_atomic_load((const Q4S_GLOBAL uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        return *gp<uint64_t>(p);
+}
+
+template <int kSync>
+__device__ __forceinline__ void chain_st(uint64_t* p, uint64_t w) {
+    if constexpr (kSync == kChainTagged)
+        __hip_atomic_store((Q4S_GLOBAL uint64_t*)p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *gwr<uint64_t>(p) = w;
+}
+
+__device__ __forceinline__ bool chain_failed(const uint32_t* err) {
+    return __hip_atomic_load((const Q4S_GLOBAL uint32_t*)err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+}
+
+__device__ __forceinline__ void chain_fail(uint32_t* err) {
+    __hip_atomic_fetch_or((Q4S_GLOBAL uint32_t*)err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The value of word w (read from p): with tagged phases, poll p until it
+// carries this step's tag; after a barrier the tag is only checked.
+template <int kSync>
+__device__ __forceinline__ float chain_value(const uint64_t* p, uint64_t w, uint32_t gen, uint32_t* err) {
+    if constexpr (kSync == kChainTagged) {
+        int64_t spins = 0;
+        while ((uint32_t)(w >> 32) != gen) {
+            // give up past the limit, or at once once any other wait has given up
+            if (++spins > kChainSpin || ((spins & 1023) == 0 && chain_failed(err))) {
+                chain_fail(err);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            w = chain_ld<kSync>(p);
+        }
+    } else if ((uint32_t)(w >> 32) != gen) {
+        chain_fail(err);
+    }
+    return __uint_as_float((uint32_t)w);
+}
+
+// The RMS-norm divisor of an activation of n values: sqrt(ss / n + 1e-6),
+// with ss from 64 lane partials (fmaf chains over i = lane, lane + 64, ...)
+// and the xor butterfly 32, 16, ..., 1 -- every lane ends with the same ss,
+// since each step adds the same two values on both lanes.
+template <int kSync>
+__device__ __noinline__ float chain_norm(const void* x, int plain, int n, uint32_t gen, uint32_t* err) {
+    const int lane = threadIdx.x & 63;
+    float p = 0.0f;
+    for (int i0 = lane; i0 < n; i0 += 64 * 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int i = i0 + 64 * k;
+            if (i >= n) {
+                v[k] = 0.0f;
+            } else if (plain) {
+                v[k] = ((const float*)x)[i];
+            } else {
+                const uint64_t* q = (const uint64_t*)x + i;
+                v[k] = chain_value<kSync>(q, chain_ld<kSync>(q), gen, err);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (i0 + 64 * k < n) p = fmaf(v[k], v[k], p);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
+    return sqrtf(p / (float)n + 1e-6f);
+}
+
+// The activation source of a chained-step wave (see ActQuant): element values
+// come from tagged words (or the fp32 input), optionally times a second
+// factor, optionally divided by the RMS of the whole vector.
+template <int kSync>
+struct ActChain {
+    const ChainMat& cm;
+    uint32_t gen;
+    uint32_t* err;
+    bool have_s;
+    float s;
+    uint64_t raw[2][4], raw2[2][4];
+    struct Prep {
+        uint32_t packed;
+        uint32_t dbits;
+    };
+    __device__ __forceinline__ int64_t elem(int c) const {
+        const int lane = threadIdx.x & 63;
+        return min((int64_t)c * 256 + 4 * lane, (int64_t)cm.m.cols - 4);
+    }
+    __device__ __forceinline__ void load(int slot, int c) {
+        const int64_t i = elem(c);
+        if (cm.x_plain) {
+            const f32x4 v = *gp<f32x4>((const float*)cm.x + i);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) raw[slot][k] = tag_word(v[k], gen);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) raw[slot][k] = chain_ld<kSync>((const uint64_t*)cm.x + i + k);
+        }
+        if (cm.x2) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) raw2[slot][k] = chain_ld<kSync>(cm.x2 + i + k);
+        }
+    }
+    __device__ __forceinline__ Prep prepare(int slot, int c) {
+        if (cm.norm && !have_s) {
+            s = chain_norm<kSync>(cm.x, cm.x_plain, cm.m.cols, gen, err);
+            have_s = true;
+        }
+        const int lane = threadIdx.x & 63;
+        const int blk = c * kChunkBlocks + (lane >> 3);
+        const bool valid = blk < cm.m.nb;
+        const int64_t i = elem(c);
+        f32x4 v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[k] = cm.x_plain ? __uint_as_float((uint32_t)raw[slot][k])
+                              : chain_value<kSync>((const uint64_t*)cm.x + i + k, raw[slot][k], gen, err);
+            if (cm.x2) v[k] = v[k] * chain_value<kSync>(cm.x2 + i + k, raw2[slot][k], gen, err);
+            if (cm.norm) v[k] = v[k] / s;
+        }
+        if (!valid) v = (f32x4){0.f, 0.f, 0.f, 0.f};
+        const float a = quant8_amax(v);
+        uint32_t packed;
+        uint16_t h;
+        quant8_codes(v, a, packed, h);
+        return {packed, __float_as_uint(__half2float(__ushort_as_half(h)))};
+    }
+    __device__ __forceinline__ u32x8 q(const Prep& p, int, int, int b) const {
+        u32x8 r;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) r[k] = __builtin_amdgcn_readlane(p.packed, 8 * b + k);
+        return r;
+    }
+    __device__ __forceinline__ float d(const Prep& p, int, int, int b) const {
+        return __uint_as_float(__builtin_amdgcn_readlane(p.dbits, 8 * b));
+    }
+};
+
+// One tile (group set) of a chained-step matrix: the GEMV as in run_tile_with,
+// then the epilogue stores (tagged output, residual sum, plain logits).
+template <int kSync>
+__device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, float* red, uint32_t gen,
+                                           uint32_t* err) {
+    const MatDesc& m = cm.m;
+    const int wave = wave_uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int ks = m.ks;
+    const int gpw = kWaves / ks;
+    const int64_t g = gset * gpw + wave / ks;
+    const int sp = wave % ks;
+    const int c0 = (int)((int64_t)sp * m.C / ks);
+    const int c1 = (int)((int64_t)(sp + 1) * m.C / ks);
+    float acc[1];
+    ActChain<kSync> act{cm, gen, err, false, 0.0f, {}, {}};
+    wave_task<1>(m, (int)g, c0, c1, acc, act);
+    float v = acc[0];
+    if (ks > 1) {
+        red[wave * 64 + lane] = v;
+        __syncthreads();
+        if (sp != 0) return;
+        v = red[wave * 64 + lane];
+        for (int j = 1; j < ks; ++j) v += red[(wave + j) * 64 + lane];
+    }
+    const int64_t row = g * kGroupRows + lane;
+    if (g >= m.G || row >= m.rows) return;
+    if (cm.y) chain_st<kSync>(cm.y + row, tag_word(v, gen));
+    if (cm.yf) gwr<float>(cm.yf)[row] = v;
+    if (cm.res) {
+        float r;
+        if (cm.res_plain) {
+            r = ((const float*)cm.res)[row];
+        } else {
+            const uint64_t* p = (const uint64_t*)cm.res + row;
+            r = chain_value<kSync>(p, chain_ld<kSync>(p), gen, err);
+        }
+        chain_st<kSync>(cm.y2 + row, tag_word(r + v, gen));
+    }
+}
+
+// Phase barrier number k (1-based) of a launch; sync: [0] error word,
+// [32] top counter, [64 + 32 i] sub-counter i.  Counters start at 0 per launch.
+template <int kSync>
+__device__ __forceinline__ void chain_barrier(uint32_t* sync, uint32_t k) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        Q4S_GLOBAL uint32_t* err = (Q4S_GLOBAL uint32_t*)sync;
+        Q4S_GLOBAL uint32_t* top = (Q4S_GLOBAL uint32_t*)sync + 32;
+        const uint32_t n = gridDim.x;
+        Q4S_GLOBAL uint32_t* watch;
+        uint32_t target;
+        if constexpr (kSync == kChainCounter) {
+            __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            watch = top;
+            target = k * n;
+        } else {
+            const uint32_t fan = n < 16 ? n : 16;
+            const uint32_t sub = blockIdx.x % fan;
+            const uint32_t size = (n - sub + fan - 1) / fan;  // workgroups b < n with b mod fan == sub
+            Q4S_GLOBAL uint32_t* mine = (Q4S_GLOBAL uint32_t*)sync + 64 + 32 * sub;
+            const uint32_t old = __hip_atomic_fetch_add(mine, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            if (old + 1 == k * size) {
+                const uint32_t t = __hip_atomic_fetch_add(top, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                if (t + 1 == k * fan)
+                    __hip_atomic_store(err + 1, k, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);  // release word
+            }
+            watch = err + 1;
+            target = k;
+        }
+        int64_t spins = 0;
+        while (__hip_atomic_load(watch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            if (++spins > kChainSpin || ((spins & 1023) == 0 && chain_failed(sync))) {
+                __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+}
+
+template <int kSync>
+__global__ __launch_bounds__(kThreads, 1) void k_chain(ChainParams P) {
+    __shared__ float red[kWaves * 64];
+    const uint32_t nwg = gridDim.x, b = blockIdx.x;
+    uint32_t begin = 0;
+    for (int p = 0; p < P.n_phases; ++p) {
+        const uint32_t end = P.phase_end[p];
+        const uint32_t j0 = (b + nwg - begin % nwg) % nwg;  // phase tiles start on workgroup begin mod nwg
+        for (uint32_t j = j0; begin + j < end; j += nwg) {
+            const uint32_t t = begin + j;
+            const ChainMat cm = P.mats[P.tiles[2 * (size_t)t]];
+            chain_tile<kSync>(cm, P.tiles[2 * (size_t)t + 1], red, P.gen, P.sync);
+            __syncthreads();
+        }
+        if constexpr (kSync != kChainTagged)
+            if (p + 1 < P.n_phases) chain_barrier<kSync>(P.sync, (uint32_t)p + 1);
+        begin = end;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_zero_words(uint32_t* w, int n) {
+    for (int i = threadIdx.x; i < n; i += 256) w[i] = 0;
+}
+
 // ---------------------------------------------------------------- measurement
 
 template <int L>
@@ -721,6 +1012,30 @@ hipError_t launch_sweep_fused(const MatDesc* dev_mats, const uint32_t* dev_tiles
     if (n_tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_sweep_fused, dim3((unsigned)n_tiles), dim3(kThreads), 0, st, dev_mats, dev_tiles);
     return hipGetLastError();
+}
+
+hipError_t launch_chain(int sync_mode, const ChainParams& p, int workgroups, hipStream_t st) {
+    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, st, p.sync, kChainSyncWords);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ChainParams a = p;
+    void* args[] = {&a};
+    const void* fn = sync_mode == kChainCounter ? (const void*)k_chain<kChainCounter>
+                     : sync_mode == kChainTree  ? (const void*)k_chain<kChainTree>
+                                                : (const void*)k_chain<kChainTagged>;
+    return hipLaunchCooperativeKernel(fn, dim3(workgroups), dim3(kThreads), args, 0, st);
+}
+
+hipError_t chain_max_workgroups(int sync_mode, int* n) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const void* fn = sync_mode == kChainCounter ? (const void*)k_chain<kChainCounter>
+                     : sync_mode == kChainTree  ? (const void*)k_chain<kChainTree>
+                                                : (const void*)k_chain<kChainTagged>;
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0);
+    *n = e == hipSuccess ? cus * per_cu : 0;
+    return e;
 }
 
 template <int N>

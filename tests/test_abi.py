@@ -19,12 +19,12 @@ def test_exports_every_declared_function(L):
     assert len(names) >= 23
     for n in names:
         assert hasattr(L, n), n
-    assert L.q4s_abi_version() == 2
+    assert L.q4s_abi_version() == 3
 
 
 def test_status_strings(L):
-    for s in range(7):
-        assert q.status_string(s)
+    for s in range(8):
+        assert q.status_string(s) != "unknown status"
     assert q.status_string(99) == "unknown status"
 
 
@@ -168,6 +168,66 @@ def test_sweep_plan_host_side(L):
     assert st == 2
     st, plan, _ = _plan(L, [(FAKE, None, FAKE + 8, FAKE + (1 << 30), 64, 64)], 1)
     assert st == 3 and "matrix 0" in _err(L)
+
+
+def _chain(L, shape, ws, h0, acts, logits, mode=2, wg=0):
+    arr = (ctypes.c_void_p * max(1, len(ws)))(*ws)
+    need = ctypes.c_size_t(0)
+    h = ctypes.c_void_p(None)
+    st = L.q4s_chain_create(ctypes.byref(shape), arr, h0, acts, logits, mode, wg, ctypes.byref(need),
+                            ctypes.byref(h))
+    return st, h, need.value
+
+
+def test_chain_host_side(L):
+    """Plan building and validation of the chained step (no GPU: upload is not called)."""
+    Lr, E, D, F, V = 28, 1536, 256, 8960, 151936
+    shape = q.ChainShape(Lr, E, D, F, V)
+    assert L.q4s_chain_act_words(ctypes.byref(shape)) == 28 * (5 * 1536 + 2 * 256 + 2 * 8960)
+    assert q.chain_layout(E, D, F)[1] == 5 * 1536 + 2 * 256 + 2 * 8960
+    dims = [(E, E), (D, E), (D, E), (E, E), (F, E), (F, E), (E, F)] * Lr + [(V, E)]
+    ws, base = [], FAKE
+    for r, c in dims:
+        ws.append(base)
+        base += (q.packed_bytes(r, c) + 4095) // 4096 * 4096
+    h0 = base; base += 1 << 16
+    acts = base; base += (8 * L.q4s_chain_act_words(ctypes.byref(shape)) + 4095) // 4096 * 4096
+    logits = base
+    st, h, need = _chain(L, shape, ws, h0, acts, logits)
+    assert st == 0, _err(L)
+    info = q.ChainInfo()
+    assert L.q4s_chain_get_info(h, ctypes.byref(info)) == 0
+    d = info.as_dict()
+    assert d["n_mats"] == 197 and d["n_phases"] == 113 and d["workgroups"] == 0 and d["steps"] == 0
+    assert d["packed_bytes"] == 868_257_792 and d["dev_bytes"] == need
+    # tiles per layer: q 6 + k 1 + v 1 | o 6 | gate 35 + up 35 | down 24; the head 594
+    assert d["n_tiles"] == 28 * (8 + 6 + 70 + 24) + 594
+    assert L.q4s_chain_run(h, None) == 5                  # not uploaded
+    L.q4s_chain_destroy(h)
+    # bad shapes, modes, counts, pointers and aliasing
+    for bad in (q.ChainShape(2, 100, 64, 256, 10), q.ChainShape(2, 128, 0, 256, 10),
+                q.ChainShape(2, 128, 64, 250, 10), q.ChainShape(-1, 128, 64, 256, 10),
+                q.ChainShape(2, 128, 64, 256, 0)):
+        assert L.q4s_chain_act_words(ctypes.byref(bad)) == 0
+        assert _chain(L, bad, ws, h0, acts, logits)[0] == 2
+    assert _chain(L, shape, ws, h0, acts, logits, mode=3)[0] == 2
+    assert _chain(L, shape, ws, h0, acts, logits, wg=-1)[0] == 2
+    assert _chain(L, shape, ws, h0 + 4, acts, logits)[0] == 3          # h0 not 16-byte aligned
+    assert _chain(L, shape, ws, h0, acts + 8, logits)[0] == 3
+    assert _chain(L, shape, ws, None, acts, logits)[0] == 1
+    wbad = list(ws)
+    wbad[5] = None
+    st, _, _ = _chain(L, shape, wbad, h0, acts, logits)
+    assert st == 1 and "matrix 5" in _err(L)
+    assert _chain(L, shape, ws, h0, ws[3], logits)[0] == 4             # acts over a weight
+    assert _chain(L, shape, ws, h0, acts, h0)[0] == 4                  # logits over h0
+    assert _chain(L, shape, ws, h0, acts, acts + 64)[0] == 4           # logits inside acts
+    # the head alone
+    one = q.ChainShape(0, 128, 64, 64, 200)
+    st, h, _ = _chain(L, one, [FAKE], FAKE + (1 << 20), FAKE + (1 << 21), FAKE + (1 << 22))
+    assert st == 0, _err(L)
+    assert L.q4s_chain_get_info(h, ctypes.byref(info)) == 0 and info.n_phases == 1 and info.act_words == 0
+    L.q4s_chain_destroy(h)
 
 
 def test_library_refuses_when_missing(monkeypatch, tmp_path):

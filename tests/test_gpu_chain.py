@@ -1,0 +1,131 @@
+"""GPU parity of the chained decode step (q4s_chain_*): every intermediate vector
+and the logits equal the oracle's chained step (the fixed fp32 order of the
+milestone M16 reading, the Q8_0 quantizer and the RMS norm) bit for bit, in all
+three phase-synchronisation modes, at small, ragged and full Qwen2.5-1.5B
+shapes (28 layers, 868 MB), with the persistent workgroup count both one per
+compute unit and below the number of tiles of a phase."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import dev, packed_weights, require_gpu, to_dev
+from q4_weight_streaming_amd import _lib as q
+from q4_weight_streaming_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+MODES = [q.CHAIN_COUNTER, q.CHAIN_TREE, q.CHAIN_TAGGED]
+MODE_IDS = ["counter", "tree", "tagged"]
+
+
+def _inputs(cfg, layers, E, D, F, V, scale=1.0, outliers=8):
+    shapes = [(E, E), (D, E), (D, E), (E, E), (F, E), (F, E), (E, F)] * layers + [(V, E)]
+    ws = [synth.q4_0_weights(r, c, synth.generator(cfg, m, 0, 0)) for m, (r, c) in enumerate(shapes)]
+    h0 = (scale * synth.activation(1, E, synth.generator(cfg, 999, 0, 1), outliers=outliers)[0]).astype(np.float32)
+    return shapes, ws, h0
+
+
+def _device(shapes, ws, h0, layers, E, D, F, V):
+    wp = [packed_weights(w, r, c) for w, (r, c) in zip(ws, shapes)]
+    words = q.chain_act_words(layers, E, D, F, V)
+    acts = torch.empty(max(words, 1), dtype=torch.int64, device=dev())
+    logits = torch.empty(V, dtype=torch.float32, device=dev())
+    torch.cuda.synchronize()
+    return wp, to_dev(h0), acts, logits
+
+
+def _run(wp, h0d, acts, logits, layers, E, D, F, V, mode, workgroups, steps=1):
+    ch = q.Chain(layers, E, D, F, V, wp, h0d, acts, logits, sync_mode=mode, workgroups=workgroups)
+    for _ in range(steps):
+        ch.run()
+    ch.check()
+    info = ch.info()
+    ch.close()
+    words = q.chain_act_words(layers, E, D, F, V)
+    vals, tags = q.chain_values(acts[:words])
+    return vals.cpu().numpy(), tags.cpu().numpy(), logits.cpu().numpy().copy(), info
+
+
+def _compare(oracle_acts, oracle_logits, vals, logits, layers, E, D, F, what):
+    lay, per = q.chain_layout(E, D, F)
+    got = vals.reshape(layers, per) if layers else vals[:0]
+    for l in range(layers):
+        for name, (off, n) in lay.items():
+            a, b = got[l, off:off + n], oracle_acts[l, off:off + n]
+            bad = np.flatnonzero(a != b)
+            assert bad.size == 0, f"{what}: layer {l} {name}: {bad.size} of {n} differ, first at {bad[0]}: {a[bad[0]]!r} vs {b[bad[0]]!r}"
+    bad = np.flatnonzero(logits != oracle_logits)
+    assert bad.size == 0, f"{what}: {bad.size} logits differ, first at {bad[0]}"
+
+
+@pytest.mark.parametrize("workgroups", [0, 5], ids=["per_cu", "wg5"])
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_chain_small_bit_exact(oracle, mode, workgroups):
+    require_gpu()
+    L, E, D, F, V = 2, 256, 64, 384, 320
+    shapes, ws, h0 = _inputs(40, L, E, D, F, V)
+    ref_acts, ref_logits = oracle.chain_step(ws, E, D, F, V, h0)
+    wp, h0d, acts, logits = _device(shapes, ws, h0, L, E, D, F, V)
+    vals, tags, lg, info = _run(wp, h0d, acts, logits, L, E, D, F, V, mode, workgroups)
+    assert info["n_phases"] == 4 * L + 1 and info["steps"] == 1
+    assert (tags == 1).all()
+    _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, f"mode {mode}")
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_chain_ragged_shapes(oracle, mode):
+    """hidden 96 and ff 160 (partial chunks), kv_dim 5 and vocab 77 (partial row groups),
+    three layers, three workgroups (fewer than the tiles of most phases)."""
+    require_gpu()
+    L, E, D, F, V = 3, 96, 5, 160, 77
+    shapes, ws, h0 = _inputs(41, L, E, D, F, V)
+    ref_acts, ref_logits = oracle.chain_step(ws, E, D, F, V, h0)
+    wp, h0d, acts, logits = _device(shapes, ws, h0, L, E, D, F, V)
+    vals, tags, lg, _ = _run(wp, h0d, acts, logits, L, E, D, F, V, mode, 3)
+    assert (tags == 1).all()
+    _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, "ragged")
+
+
+def test_chain_head_only(oracle):
+    require_gpu()
+    L, E, D, F, V = 0, 128, 64, 64, 200
+    shapes, ws, h0 = _inputs(42, L, E, D, F, V)
+    _, ref_logits = oracle.chain_step(ws, E, D, F, V, h0)
+    wp, h0d, acts, logits = _device(shapes, ws, h0, L, E, D, F, V)
+    _, _, lg, info = _run(wp, h0d, acts, logits, L, E, D, F, V, q.CHAIN_TAGGED, 0)
+    assert info["n_phases"] == 1
+    np.testing.assert_array_equal(lg, ref_logits)
+
+
+def test_chain_repeated_steps_are_identical(oracle):
+    """Three steps on one chain: every word carries the third step's tag, same values."""
+    require_gpu()
+    L, E, D, F, V = 2, 256, 64, 384, 320
+    shapes, ws, h0 = _inputs(43, L, E, D, F, V)
+    ref_acts, ref_logits = oracle.chain_step(ws, E, D, F, V, h0)
+    wp, h0d, acts, logits = _device(shapes, ws, h0, L, E, D, F, V)
+    vals, tags, lg, info = _run(wp, h0d, acts, logits, L, E, D, F, V, q.CHAIN_TAGGED, 0, steps=3)
+    assert info["steps"] == 3 and (tags == 3).all()
+    _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, "third step")
+
+
+@pytest.fixture(scope="module")
+def qwen15_chain(oracle):
+    require_gpu()
+    L, E, D, F, V = 28, 1536, 256, 8960, 151936
+    shapes, ws, h0 = _inputs(44, L, E, D, F, V)
+    ref = oracle.chain_step(ws, E, D, F, V, h0)
+    dv = _device(shapes, ws, h0, L, E, D, F, V)
+    del ws
+    return (L, E, D, F, V), ref, dv
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_chain_qwen15_full_bit_exact(qwen15_chain, mode):
+    """The Qwen2.5-1.5B-shaped chain (28 layers, 868 MB of weights), one workgroup per
+    compute unit: all 28 x 9 vectors and the 151936 logits equal the oracle's."""
+    (L, E, D, F, V), (ref_acts, ref_logits), (wp, h0d, acts, logits) = qwen15_chain
+    vals, tags, lg, info = _run(wp, h0d, acts, logits, L, E, D, F, V, mode, 0)
+    assert info["n_phases"] == 113 and (tags == 1).all()
+    assert np.isfinite(lg).all()
+    _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, f"1.5B mode {mode}")
