@@ -358,17 +358,22 @@ void q4o_gemv_f32_rows(const uint8_t* w, const uint8_t* xq8, int64_t cols, int n
  * rounded, with no learned weight (the synthetic model's norm weights are 1).
  * Qwen2.5's RMS norm with its epsilon of 1e-6; the pages name "norm
  * prologues" (M19) without a formula.  The sum of squares ss is taken in a
- * fixed order: 64 partial sums p_l = fmaf chains over x_l, x_{l+64}, ... in
- * increasing index, then for d = 32, 16, 8, 4, 2, 1 every p_l becomes
- * p_l + p_{l xor d} (all at once); ss = p_0.  Returns ss.
+ * fixed order: 64 partial sums, p_l an fmaf chain over the elements
+ * 256c + 4l + k (k = 0..3) of every 256-element chunk c in turn (those below
+ * n), then for d = 32, 16, 8, 4, 2, 1 every p_l becomes p_l + p_{l xor d}
+ * (all at once); ss = p_0.  Returns ss.
  */
 float q4o_rmsnorm(const float* x, int64_t n, float* out)
 {
     float p[64], q[64];
     for (int l = 0; l < 64; ++l) {
         p[l] = 0.0f;
-        for (int64_t i = l; i < n; i += 64)
-            p[l] = fmaf(x[i], x[i], p[l]);
+        for (int64_t c = 0; c * 256 < n; ++c)
+            for (int k = 0; k < 4; ++k) {
+                const int64_t i = c * 256 + 4 * l + k;
+                if (i < n)
+                    p[l] = fmaf(x[i], x[i], p[l]);
+            }
     }
     for (int d = 32; d >= 1; d /= 2) {
         for (int l = 0; l < 64; ++l)

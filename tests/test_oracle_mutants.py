@@ -75,6 +75,7 @@ MUTANTS = [
     ("pinned_drops_partial_chunk", "for (int64_t k = 0; k < 8 && c * 8 + k < nb; ++k) {",
      "for (int64_t k = 0; k < 8 && c * 8 + k < nb - 1; ++k) {"),
     ("rms_sequential", "p[l] = fmaf(x[i], x[i], p[l]);", "p[0] = fmaf(x[i], x[i], p[0]);"),
+    ("rms_lane_stride_64", "const int64_t i = c * 256 + 4 * l + k;", "const int64_t i = c * 256 + l + 64 * k;"),
     ("rms_reverse_tree", "for (int d = 32; d >= 1; d /= 2) {", "for (int d = 1; d <= 32; d *= 2) {"),
     ("rms_epsilon", "sqrtf(ss / (float)n + 1e-6f)", "sqrtf(ss / (float)n + 1e-5f)"),
     ("rms_no_mean", "sqrtf(ss / (float)n + 1e-6f)", "sqrtf(ss + 1e-6f)"),

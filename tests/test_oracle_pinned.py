@@ -101,18 +101,21 @@ def test_pinned_within_fp32_bound_of_fp64(oracle, rows, cols, n):
 # ---------------------------------------------------------------- RMS norm
 
 def test_rmsnorm_order_golden(oracle):
-    """64 values, one per partial sum: x_0 = 4096 (square 2^24), x_1 = x_2 = x_3 = x_32 = 1.
-    The tree (32, 16, 8, 4, 2, 1): p_0 = 2^24 + 1 -> 2^24 (tie to even); p_1 = 1, p_2 = 1,
-    p_3 = 1; at d = 2, p_0 = 2^24 + p_2 -> 2^24 and p_1 = p_1 + p_3 = 2; at d = 1,
-    p_0 = 2^24 + 2.  (The reverse tree gives 2^24 + 4, a sequential sum 2^24.)
-    Then ss / 64 = 2^18 + 2^-5 exactly, + 1e-6 rounds back, and sqrt(2^18 + 2^-5) =
-    512 + 2^-15 - tiny rounds to 512: the outputs are x / 512 exactly."""
-    x = np.zeros(64, np.float32)
+    """256 values: lane l of the 64 partial sums owns elements 4l..4l+3.  x_0 = 4096
+    (square 2^24) and x_1 = 1 (lane 0: 2^24 + 1 ties back to 2^24), x_4 = x_8 = x_12 = 1
+    (lanes 1, 2, 3), x_128 = 1 (lane 32).
+    The tree (32, 16, 8, 4, 2, 1): p_0 = 2^24 + 1 -> 2^24 (tie to even); at d = 2,
+    p_0 = 2^24 + p_2 -> 2^24 and p_1 = p_1 + p_3 = 2; at d = 1, p_0 = 2^24 + 2.  (The
+    reverse tree gives 2^24 + 4, a sequential sum 2^24; lanes owning elements l, l + 64,
+    l + 128, l + 192 put x_1 on lane 1 and end at 2^24 + 3 -> 2^24 + 4.)  Then ss / 256 = 2^16 + 2^-7
+    exactly, + 1e-6 rounds back, and sqrt(2^16 + 2^-7) = 256 + 2^-16 - tiny rounds to
+    256: the outputs are x / 256 exactly (2^24 + 4 would give 256 + 2^-15)."""
+    x = np.zeros(256, np.float32)
     x[0] = 4096.0
-    x[[1, 2, 3, 32]] = 1.0
+    x[[1, 4, 8, 12, 128]] = 1.0
     out, ss = oracle.rmsnorm(x)
     assert ss == 2.0 ** 24 + 2
-    np.testing.assert_array_equal(out, x / np.float32(512.0))
+    np.testing.assert_array_equal(out, x / np.float32(256.0))
 
 
 @pytest.mark.parametrize("c,n", [(2.0 ** -10, 64), (2.0 ** -10, 1536), (3.0, 128), (1e-4, 3584)])
