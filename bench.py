@@ -9,6 +9,7 @@ weight set so no step finds the previous step's bytes in the 256 MB Infinity
 Cache.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload qwen2.5-1.5b|qwen2.5-7b|lm_head] [--n N]
+  python bench.py --workload chain [--chain-model 1.5b|7b] [--sync all|tagged|tree|counter]
 """
 from __future__ import annotations
 
@@ -360,12 +361,116 @@ def run_attn(args, dev, stream) -> int:
     return 0
 
 
+CHAIN_MODES = {"tagged": 2, "tree": 1, "counter": 0}
+
+
+def run_chain(args, dev, stream) -> int:
+    """The chained decode step (a token's layers as dependent phases in one launch) over the
+    Qwen2.5-1.5B or -7B-shaped stack, each phase synchronisation mode, two rotated seeded
+    weight copies; a phase timeline from the step's own clock marks."""
+    import numpy as np
+    import torch
+
+    from q4_weight_streaming_amd import _lib as q
+    from q4_weight_streaming_amd import synth
+    model = args.chain_model
+    L, E, D, F, V = (28, 1536, 256, 8960, 151936) if model == "1.5b" else (28, 3584, 512, 18944, 152064)
+    shapes = [(E, E), (D, E), (D, E), (E, E), (F, E), (F, E), (E, F)] * L + [(V, E)]
+    ncopies = 2
+    log(f"generating {ncopies} copies of the {model} chain ({len(shapes)} matrices)")
+    copies, host0 = [], None
+    for c in range(ncopies):
+        ws = [synth.q4_0_weights(r, cc, synth.generator(70 + c, m, 0, 0)) for m, (r, cc) in enumerate(shapes)]
+        wp = [q.repack_q4_0(torch.from_numpy(w.reshape(-1)).to(dev), r, cc) for w, (r, cc) in zip(ws, shapes)]
+        h0 = synth.activation(1, E, synth.generator(70 + c, 999, 0, 1))[0]
+        copies.append({"wp": wp, "h0": torch.from_numpy(h0).to(dev),
+                       "acts": torch.empty(q.chain_act_words(L, E, D, F, V), dtype=torch.int64, device=dev),
+                       "logits": torch.empty(V, dtype=torch.float32, device=dev)})
+        if c == 0 and not args.no_cpu_baseline:
+            host0 = (ws, h0)
+        del ws
+    torch.cuda.synchronize()
+    modes = list(CHAIN_MODES) if args.sync == "all" else [args.sync]
+    results, chains_by_mode = {}, {}
+    for mode in modes:
+        chains = [q.Chain(L, E, D, F, V, c["wp"], c["h0"], c["acts"], c["logits"], sync_mode=CHAIN_MODES[mode],
+                          workgroups=args.chain_workgroups) for c in copies]
+        ms = time_steps([ch.run for ch in chains], args.steps, args.warmup, stream)
+        for ch in chains:
+            ch.check()
+        # phase timeline: the end of a phase is when its last workgroup finishes it
+        tr = chains[0].set_trace(True)
+        chains[0].run()
+        chains[0].check()
+        chains[0].set_trace(False)
+        info = chains[0].info()
+        t = tr.cpu().numpy().astype(np.float64)
+        P, wg = info["n_phases"], info["workgroups"]
+        ends = t[:P * wg].reshape(P, wg)
+        start = t[P * wg:P * wg + wg].min()
+        ready = t[2 * P * wg + wg:3 * P * wg + wg].reshape(P, wg)
+        crit = ends.max(axis=1)
+        dur = np.diff(np.concatenate([[start], crit])) / 100.0  # 100 MHz clock -> us
+        names = ["qkv", "o", "gate_up", "down"]
+        per = {name: round(float(np.median(dur[i:4 * L:4])), 2) for i, name in enumerate(names)}
+        per["head"] = round(float(dur[-1]), 2)
+        # per phase: how long after the previous phase's last workgroup the first tiles had
+        # their activation (median over the phase's workgroups), medians over the layers
+        wait = [float(np.median((ready[p][ready[p] > 0] - crit[p - 1]) / 100.0)) for p in range(1, P)]
+        ready_us = {name: round(float(np.median(wait[i - 1::4] if i else wait[3:P - 2:4])), 2)
+                    for i, name in enumerate(names)}   # (qkv: layers 1.. -- the head is phase P - 1)
+        results[mode] = {"us_per_step": round(ms * 1e3, 1), "workgroups": wg, "phase_us_median": per,
+                         "input_ready_after_us": ready_us}
+        log(f"chain {model} {mode}: {ms * 1e3:.1f} us per step; phases (median us) {per}; "
+            f"input ready after (median us) {ready_us}")
+        chains_by_mode[mode] = chains
+    packed = info["packed_bytes"]
+    best = min(results, key=lambda m: results[m]["us_per_step"])
+    us = results[best]["us_per_step"]
+    achieved = packed / (us * 1e-6) / 1e9
+    out = {
+        "metric": "chained decode step: weight-stream GB/s (% of 8 TB/s HBM peak), step time",
+        "value": round(achieved, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"Qwen2.5-{model}-shaped chained step: {L} layers x 4 dependent phases + head "
+                               f"({P} phases, {len(shapes)} Q4_0 matrices, {packed} B), norm + Q8_0 prologues, "
+                               f"residual epilogues, one cooperative launch, {ncopies} rotated seeded copies",
+                   "sync": best, "modes": results},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": f"k_chain<{best}>",
+                     "algorithmic_bytes_per_launch": packed},
+    }
+    if host0 is not None:
+        from oracle import oracle
+        oracle.build(force=False)
+        ws, h0 = host0
+        t0 = time.perf_counter()
+        done = 0
+        while True:
+            oracle.chain_step(ws, E, D, F, V, h0)
+            done += 1
+            if time.perf_counter() - t0 > args.cpu_budget:
+                break
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(done * packed / dt / 1e9, 3), "unit": "GB/s",
+                               "cores": oracle.max_threads(), "kind": "oracle",
+                               "sample": f"{done} fixed-order oracle chained steps over copy 0 ({packed} B each), "
+                                         f"{dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qwen2.5-1.5b", choices=["qwen2.5-1.5b", "qwen2.5-7b", "lm_head", "lm_head_q8", "attn"])
+    ap.add_argument("--workload", default="qwen2.5-1.5b",
+                    choices=["qwen2.5-1.5b", "qwen2.5-7b", "lm_head", "lm_head_q8", "attn", "chain"])
+    ap.add_argument("--chain-model", default="1.5b", choices=["1.5b", "7b"], help="stack of --workload chain")
+    ap.add_argument("--sync", default="all", choices=["all", *CHAIN_MODES], help="phase sync of --workload chain")
+    ap.add_argument("--chain-workgroups", type=int, default=0, help="persistent workgroups (0: one per CU)")
     ap.add_argument("--context", type=int, default=32768, help="KV positions for --workload attn")
     ap.add_argument("--n", type=int, default=1, help="activation rows per GEMV (1..24; 1..8 for lm_head_q8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -395,6 +500,8 @@ def main() -> int:
         return run_q8_head(args, dev, stream)
     if args.workload == "attn":
         return run_attn(args, dev, stream)
+    if args.workload == "chain":
+        return run_chain(args, dev, stream)
     shapes, cfg, ncopies = workload_shapes(args.workload)
     n = args.n
     log(f"generating {ncopies} copies of {args.workload} ({len(shapes)} matrices), n={n}")

@@ -361,9 +361,9 @@ void q4s_sweep_plan_destroy(q4s_plan* plan);
  */
 typedef struct {
     int32_t layers; /* >= 0 (0: the head alone)            */
-    int32_t hidden; /* E, a multiple of 32                  */
+    int32_t hidden; /* E, a multiple of 32, <= 32768        */
     int32_t kv_dim; /* D >= 1 (rows of Wk and Wv)           */
-    int32_t ff;     /* F, a multiple of 32                  */
+    int32_t ff;     /* F, a multiple of 32, <= 32768        */
     int32_t vocab;  /* V >= 1                               */
 } q4s_chain_shape;
 
@@ -426,6 +426,24 @@ q4s_status q4s_chain_run(q4s_chain* chain, void* stream);
 q4s_status q4s_chain_check(const q4s_chain* chain, void* stream);
 
 q4s_status q4s_chain_get_info(const q4s_chain* chain, q4s_chain_info* info);
+
+/*
+ * Phase timeline of later steps (the clock-delta profiling of milestone M19):
+ * with a trace buffer set, every step records, with P = n_phases and
+ * W = workgroups, slot s = p * W + b for phase p and workgroup b:
+ *   trace[s]              when workgroup b finished phase p;
+ *   trace[P * W + b]      when workgroup b started;
+ *   trace[P * W + W + s]  when b started its first tile of phase p;
+ *   trace[2 P W + W + s]  when that tile's activation prologue was done (its
+ *                         input had arrived, been normalized and quantized).
+ * The tile entries are left untouched for workgroups without a tile in a phase
+ * (q4s_chain_set_trace zeroes the buffer once).  Times are the GPU's 100 MHz
+ * constant clock.  trace: q4s_chain_trace_bytes bytes of device memory
+ * (8-byte aligned; 0 before upload); NULL turns tracing off.  One thread per
+ * workgroup stores the marks.
+ */
+size_t q4s_chain_trace_bytes(const q4s_chain* chain);
+q4s_status q4s_chain_set_trace(q4s_chain* chain, uint64_t* trace, size_t trace_bytes);
 
 void q4s_chain_destroy(q4s_chain* chain);
 

@@ -99,6 +99,8 @@ def lib():
             "q4s_chain_check": ([p, p], i32),
             "q4s_chain_get_info": ([p, ctypes.POINTER(ChainInfo)], i32),
             "q4s_chain_destroy": ([p], None),
+            "q4s_chain_trace_bytes": ([p], sz),
+            "q4s_chain_set_trace": ([p, p, sz], i32),
             "q4s_bench_read": ([p, sz, i32, i32, p, p], i32),
             "q4s_bench_copy": ([p, p, sz, p], i32),
             "q4s_bench_grid_barrier": ([i32, i32, i32, p, sz, p], i32),
@@ -394,6 +396,19 @@ class Chain:
 
     def run(self) -> None:
         _check("q4s_chain_run", lib().q4s_chain_run(self._chain, _stream(self.device)))
+
+    def set_trace(self, on: bool) -> torch.Tensor | None:
+        """Record the phase timeline of later steps; returns the zeroed int64 trace tensor
+        (layout in q4s.h: phase ends [P][W], workgroup starts [W], first-tile starts [P][W],
+        first-tile prologue ends [P][W]; 100 MHz clock)."""
+        if not on:
+            _check("q4s_chain_set_trace", lib().q4s_chain_set_trace(self._chain, None, 0))
+            self._trace = None
+            return None
+        n = int(lib().q4s_chain_trace_bytes(self._chain)) // 8
+        self._trace = torch.zeros(n, dtype=torch.int64, device=self.device)
+        _check("q4s_chain_set_trace", lib().q4s_chain_set_trace(self._chain, self._trace.data_ptr(), n * 8))
+        return self._trace
 
     def check(self) -> None:
         """Synchronize; raise Q4SError (status 7) if a bounded wait of the last step gave up."""

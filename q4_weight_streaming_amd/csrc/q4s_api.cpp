@@ -514,11 +514,13 @@ struct q4s_chain {
     uint8_t* dev = nullptr;
     uint32_t gen = 0;
     int64_t steps = 0;
+    uint64_t* trace = nullptr;
 };
 
 static bool chain_shape_ok(const q4s_chain_shape* s) {
+    // hidden and ff <= 32768 keep every wave's K range within its 32-chunk LDS slice
     return s && s->layers >= 0 && s->layers <= (1 << 16) && s->hidden >= 32 && s->hidden % 32 == 0 &&
-           s->hidden <= (1 << 20) && s->ff >= 32 && s->ff % 32 == 0 && s->ff <= (1 << 20) && s->kv_dim >= 1 &&
+           s->hidden <= 32768 && s->ff >= 32 && s->ff % 32 == 0 && s->ff <= 32768 && s->kv_dim >= 1 &&
            s->kv_dim <= (1 << 20) && s->vocab >= 1 && s->vocab <= (1 << 24);
 }
 
@@ -537,7 +539,8 @@ q4s_status q4s_chain_create(const q4s_chain_shape* shape, const void* const* w_p
     if (!out || !dev_bytes_needed || !shape || !w_packed) return fail(Q4S_ERR_NULL, "shape, w_packed, dev_bytes_needed and out are required");
     *out = nullptr;
     if (!chain_shape_ok(shape))
-        return fail(Q4S_ERR_SHAPE, "chain shape needs layers >= 0, hidden and ff multiples of 32, kv_dim and vocab >= 1");
+        return fail(Q4S_ERR_SHAPE,
+                    "chain shape needs layers >= 0, hidden and ff multiples of 32 up to 32768, kv_dim and vocab >= 1");
     if (sync_mode < Q4S_CHAIN_COUNTER || sync_mode > Q4S_CHAIN_TAGGED)
         return fail(Q4S_ERR_SHAPE, "sync_mode=%d is not a chain sync mode", sync_mode);
     if (workgroups < 0 || workgroups > (1 << 16)) return fail(Q4S_ERR_SHAPE, "workgroups=%d out of range", workgroups);
@@ -697,6 +700,7 @@ q4s_status q4s_chain_run(q4s_chain* p, void* stream) {
     cp.sync = (uint32_t*)(p->dev + p->off_sync);
     cp.n_phases = (int32_t)p->phase_end.size();
     cp.gen = p->gen;
+    cp.trace = p->trace;
     q4s_status s = hip_status(launch_chain(p->mode, cp, p->workgroups, (hipStream_t)stream), "chain launch");
     if (s == Q4S_OK) ++p->steps;
     return s;
@@ -710,6 +714,24 @@ q4s_status q4s_chain_check(const q4s_chain* p, void* stream) {
     if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "chain check");
     if (err) return fail(Q4S_ERR_WAIT, "a bounded wait of the chained step gave up");
+    return ok();
+}
+
+size_t q4s_chain_trace_bytes(const q4s_chain* p) {
+    if (!p || !p->dev) return 0;
+    return (3 * (size_t)p->phase_end.size() + 1) * (size_t)p->workgroups * 8;
+}
+
+q4s_status q4s_chain_set_trace(q4s_chain* p, uint64_t* trace, size_t trace_bytes) {
+    if (!p) return fail(Q4S_ERR_NULL, "chain is NULL");
+    if (!p->dev) return fail(Q4S_ERR_PLAN, "chain was not uploaded");
+    if (trace) {
+        q4s_status s;
+        const size_t need = q4s_chain_trace_bytes(p);
+        if ((s = check_ptr(trace, need, 8, "trace"))) return s;
+        if (trace_bytes < need) return fail(Q4S_ERR_SHAPE, "trace holds %zu bytes, needs %zu", trace_bytes, need);
+    }
+    p->trace = trace;
     return ok();
 }
 

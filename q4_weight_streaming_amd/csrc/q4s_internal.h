@@ -82,6 +82,7 @@ struct ChainParams {
     const uint32_t* tiles;      // (matrix, group set) pairs, phase by phase
     const uint32_t* phase_end;  // cumulative tile count at the end of each phase
     uint32_t* sync;             // error word, then barrier counters (zeroed before every launch)
+    uint64_t* trace;            // NULL, or the phase timeline (see q4s_chain_set_trace; 100 MHz clock)
     int32_t n_phases;
     uint32_t gen;               // this step's tag (never 0)
 };

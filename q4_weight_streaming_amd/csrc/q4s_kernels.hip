@@ -691,94 +691,196 @@ __device__ __forceinline__ float chain_value(const uint64_t* p, uint64_t w, uint
     return __uint_as_float((uint32_t)w);
 }
 
-// The RMS-norm divisor of an activation of n values: sqrt(ss / n + 1e-6),
-// with ss from 64 lane partials (fmaf chains over i = lane, lane + 64, ...)
-// and the xor butterfly 32, 16, ..., 1 -- every lane ends with the same ss,
-// since each step adds the same two values on both lanes.
+constexpr int kChainMaxChunks = 32;  // chunks of one wave's K range (its LDS slice)
+constexpr int kChainBatch = 6;       // chunks per prologue load batch (a 1536-wide vector in one)
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#define Q4S_LDS __attribute__((address_space(3)))
+
+// Lane's words of chunks [b0, b0 + cnt) (cnt <= kChainBatch) of a tagged
+// activation, element 256c + 4 lane + k clamped to the vector; with tagged
+// phases every word is re-read until all carry this step's tag.
 template <int kSync>
-__device__ __noinline__ float chain_norm(const void* x, int plain, int n, uint32_t gen, uint32_t* err) {
+__device__ __forceinline__ void chain_batch(const uint64_t* x, int n, int b0, int cnt, uint32_t gen, uint32_t* err,
+                                            uint64_t (&w)[kChainBatch][4]) {
     const int lane = threadIdx.x & 63;
-    float p = 0.0f;
-    for (int i0 = lane; i0 < n; i0 += 64 * 8) {
-        float v[8];
+    auto load_all = [&]() {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int i = i0 + 64 * k;
-            if (i >= n) {
-                v[k] = 0.0f;
-            } else if (plain) {
-                v[k] = ((const float*)x)[i];
-            } else {
-                const uint64_t* q = (const uint64_t*)x + i;
-                v[k] = chain_value<kSync>(q, chain_ld<kSync>(q), gen, err);
+        for (int cc = 0; cc < kChainBatch; ++cc)
+            if (cc < cnt) {
+                const int i = min((b0 + cc) * 256 + 4 * lane, n - 4);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) w[cc][k] = chain_ld<kSync>(x + i + k);
             }
+    };
+    auto all_tagged = [&]() {
+        bool ok = true;
+#pragma unroll
+        for (int cc = 0; cc < kChainBatch; ++cc)
+            if (cc < cnt) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) ok = ok && (uint32_t)(w[cc][k] >> 32) == gen;
+            }
+        return ok;
+    };
+    if constexpr (kSync == kChainTagged) {
+        int64_t spins = 0;
+        for (;;) {
+            load_all();
+            if (all_tagged()) break;
+            if (++spins > kChainSpin || ((spins & 1023) == 0 && chain_failed(err))) {
+                chain_fail(err);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
         }
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (i0 + 64 * k < n) p = fmaf(v[k], v[k], p);
+    } else {
+        load_all();
+        if (!all_tagged()) chain_fail(err);
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
-    return sqrtf(p / (float)n + 1e-6f);
 }
 
-// The activation source of a chained-step wave (see ActQuant): element values
-// come from tagged words (or the fp32 input), optionally times a second
-// factor, optionally divided by the RMS of the whole vector.
+// Values of chunks [b0, b0 + cnt): x (fp32 or tagged), times x2 when given.
+// What the prologue reads: the activation (fp32 or tagged), the optional second
+// factor, and the vector length.
+struct ChainSrc {
+    const void* x;
+    const uint64_t* x2;
+    int x_plain, n;
+};
+
 template <int kSync>
-struct ActChain {
+__device__ __forceinline__ void chain_values(const ChainSrc& cm, int b0, int cnt, uint32_t gen, uint32_t* err,
+                                             float (&v)[kChainBatch][4]) {
+    const int lane = threadIdx.x & 63;
+    const int n = cm.n;
+    if (cm.x_plain) {
+#pragma unroll
+        for (int cc = 0; cc < kChainBatch; ++cc)
+            if (cc < cnt) {
+                const f32x4 f = *gp<f32x4>((const float*)cm.x + min((b0 + cc) * 256 + 4 * lane, n - 4));
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[cc][k] = f[k];
+            }
+    } else {
+        uint64_t w[kChainBatch][4];
+        chain_batch<kSync>((const uint64_t*)cm.x, n, b0, cnt, gen, err, w);
+#pragma unroll
+        for (int cc = 0; cc < kChainBatch; ++cc)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[cc][k] = __uint_as_float((uint32_t)w[cc][k]);
+    }
+    if (cm.x2) {
+        uint64_t w[kChainBatch][4];
+        chain_batch<kSync>(cm.x2, n, b0, cnt, gen, err, w);
+#pragma unroll
+        for (int cc = 0; cc < kChainBatch; ++cc)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[cc][k] = v[cc][k] * __uint_as_float((uint32_t)w[cc][k]);
+    }
+}
+
+// Quantizes chunk c (the lane's 4 values) into the wave's LDS slice entry.
+__device__ __forceinline__ void chain_quant(f32x4 v, int c, int nb, Q4S_LDS u32x2* dst) {
+    const int lane = threadIdx.x & 63;
+    if (c * kChunkBlocks + (lane >> 3) >= nb) v = (f32x4){0.f, 0.f, 0.f, 0.f};  // past the row
+    const float a = quant8_amax(v);
+    uint32_t packed;
+    uint16_t h;
+    quant8_codes(v, a, packed, h);
+    dst[lane] = (u32x2){packed, __float_as_uint(__half2float(__ushort_as_half(h)))};
+}
+
+// Prologue of a chained-step wave that streams chunks [c0, c1): waits for the
+// activation, takes the RMS norm of the whole vector when asked, and leaves
+// the Q8_0 codes and scales of its chunks in its LDS slice ([chunk][lane]).
+// The norm divisor is sqrt(ss / n + 1e-6) with ss from 64 lane partials
+// (fmaf chains over elements 256c + 4 lane + k, chunk by chunk) and the xor
+// butterfly 32, 16, ..., 1 -- every lane ends with the same ss, since each
+// step adds the same two values on both lanes.
+template <int kSync>
+__device__ __noinline__ void chain_stage(const void* x, const uint64_t* x2, int x_plain, int norm, int n, int c0,
+                                         int c1, uint32_t gen, uint32_t* err, Q4S_LDS u32x2* slice) {
+    const int lane = threadIdx.x & 63;
+    const ChainSrc cm{x, x2, x_plain, n};
+    const int nb = n / 32;
+    const int nc = (nb + kChunkBlocks - 1) / kChunkBlocks;
+    float v[kChainBatch][4];
+    float s = 1.0f;
+    if (norm) {
+        float p = 0.0f;
+        for (int b0 = 0; b0 < nc; b0 += kChainBatch) {
+            const int cnt = min(kChainBatch, nc - b0);
+            chain_values<kSync>(cm, b0, cnt, gen, err, v);
+#pragma unroll
+            for (int cc = 0; cc < kChainBatch; ++cc)
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (cc < cnt && (b0 + cc) * 256 + 4 * lane + k < n) p = fmaf(v[cc][k], v[cc][k], p);
+        }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
+        s = sqrtf(p / (float)n + 1e-6f);
+        if (nc <= kChainBatch && c0 == 0 && c1 == nc) {  // the last batch was the whole range: reuse it
+#pragma unroll
+            for (int cc = 0; cc < kChainBatch; ++cc)
+                if (cc < nc)
+                    chain_quant((f32x4){v[cc][0] / s, v[cc][1] / s, v[cc][2] / s, v[cc][3] / s}, cc, nb,
+                                slice + cc * 64);
+            return;
+        }
+    }
+    for (int b0 = c0; b0 < c1; b0 += kChainBatch) {
+        const int cnt = min(kChainBatch, c1 - b0);
+        chain_values<kSync>(cm, b0, cnt, gen, err, v);
+#pragma unroll
+        for (int cc = 0; cc < kChainBatch; ++cc)
+            if (cc < cnt) {
+                f32x4 f = (f32x4){v[cc][0], v[cc][1], v[cc][2], v[cc][3]};
+                if (norm) f = (f32x4){f[0] / s, f[1] / s, f[2] / s, f[3] / s};
+                chain_quant(f, b0 + cc, nb, slice + (b0 + cc - c0) * 64);
+            }
+    }
+}
+
+// The activation source of a chained-step wave (see ActQuant): on first use
+// the prologue stages the wave's whole range, after the first two chunks'
+// weight loads are already in flight; every chunk then reads its codes and
+// scales from LDS.
+template <int kSync>
+struct ActStaged {
     const ChainMat& cm;
+    int64_t g;
+    int c0, c1;
     uint32_t gen;
     uint32_t* err;
-    bool have_s;
-    float s;
-    uint64_t raw[2][4], raw2[2][4];
+    Q4S_LDS u32x2* slice;
+    bool staged;
+    uint64_t* mark;  // NULL, or where to record when the first tile of the phase had its activation
     struct Prep {
         uint32_t packed;
         uint32_t dbits;
     };
-    __device__ __forceinline__ int64_t elem(int c) const {
-        const int lane = threadIdx.x & 63;
-        return min((int64_t)c * 256 + 4 * lane, (int64_t)cm.m.cols - 4);
-    }
-    __device__ __forceinline__ void load(int slot, int c) {
-        const int64_t i = elem(c);
-        if (cm.x_plain) {
-            const f32x4 v = *gp<f32x4>((const float*)cm.x + i);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) raw[slot][k] = tag_word(v[k], gen);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) raw[slot][k] = chain_ld<kSync>((const uint64_t*)cm.x + i + k);
+    __device__ __forceinline__ void load(int, int) {}
+    __device__ __forceinline__ Prep prepare(int, int c) {
+        if (!staged) {
+            // With tagged phases the wave usually waits here for the activation: touch the
+            // weight chunks after the two already in flight (one dword per 128-byte line) so
+            // that their loads after the wait hit this XCD's L2.  (After a barrier there is
+            // no wait to hide the touches behind, and they only delay the first loads.)
+            uint32_t touch = 0;
+            if constexpr (kSync == kChainTagged) {
+                const int lane = threadIdx.x & 63;
+                const uint8_t* w0 = cm.m.w + ((size_t)g * cm.m.C + c0 + 2) * kChunkBytes;
+                const int lines = max(c1 - c0 - 2, 0) * (kChunkBytes / 128);
+                for (int i = lane; i < lines; i += 64) touch ^= *gp<uint32_t>(w0 + (size_t)i * 128);
+            }
+            chain_stage<kSync>(cm.x, cm.x2, cm.x_plain, cm.norm, cm.m.cols, c0, c1, gen, err, slice);
+            if (gen == 0) err[2] = touch;  // never taken (tags start at 1); keeps the touches
+            staged = true;
+            if (mark && threadIdx.x == 0) gwr<uint64_t>(mark)[0] = __builtin_amdgcn_s_memrealtime();
         }
-        if (cm.x2) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) raw2[slot][k] = chain_ld<kSync>(cm.x2 + i + k);
-        }
-    }
-    __device__ __forceinline__ Prep prepare(int slot, int c) {
-        if (cm.norm && !have_s) {
-            s = chain_norm<kSync>(cm.x, cm.x_plain, cm.m.cols, gen, err);
-            have_s = true;
-        }
-        const int lane = threadIdx.x & 63;
-        const int blk = c * kChunkBlocks + (lane >> 3);
-        const bool valid = blk < cm.m.nb;
-        const int64_t i = elem(c);
-        f32x4 v;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[k] = cm.x_plain ? __uint_as_float((uint32_t)raw[slot][k])
-                              : chain_value<kSync>((const uint64_t*)cm.x + i + k, raw[slot][k], gen, err);
-            if (cm.x2) v[k] = v[k] * chain_value<kSync>(cm.x2 + i + k, raw2[slot][k], gen, err);
-            if (cm.norm) v[k] = v[k] / s;
-        }
-        if (!valid) v = (f32x4){0.f, 0.f, 0.f, 0.f};
-        const float a = quant8_amax(v);
-        uint32_t packed;
-        uint16_t h;
-        quant8_codes(v, a, packed, h);
-        return {packed, __float_as_uint(__half2float(__ushort_as_half(h)))};
+        const u32x2 e = slice[(c - c0) * 64 + (threadIdx.x & 63)];
+        return {e[0], e[1]};
     }
     __device__ __forceinline__ u32x8 q(const Prep& p, int, int, int b) const {
         u32x8 r;
@@ -794,8 +896,9 @@ struct ActChain {
 // One tile (group set) of a chained-step matrix: the GEMV as in run_tile_with,
 // then the epilogue stores (tagged output, residual sum, plain logits).
 template <int kSync>
-__device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, float* red, uint32_t gen,
-                                           uint32_t* err) {
+__device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, float* red, Q4S_LDS u32x2* stage,
+                                           uint32_t gen, uint32_t* err, uint64_t* mark_start, uint64_t* mark_ready) {
+    if (mark_start && threadIdx.x == 0) gwr<uint64_t>(mark_start)[0] = __builtin_amdgcn_s_memrealtime();
     const MatDesc& m = cm.m;
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -806,7 +909,12 @@ __device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, flo
     const int c0 = (int)((int64_t)sp * m.C / ks);
     const int c1 = (int)((int64_t)(sp + 1) * m.C / ks);
     float acc[1];
-    ActChain<kSync> act{cm, gen, err, false, 0.0f, {}, {}};
+    // the residual word of the lane's row goes out now, long before the epilogue needs it
+    const int64_t row = g * kGroupRows + lane;
+    const int64_t rrow = min(row, (int64_t)m.rows - 1);
+    uint64_t rword = 0;
+    if (cm.res && !cm.res_plain && sp == 0 && g < m.G) rword = chain_ld<kSync>((const uint64_t*)cm.res + rrow);
+    ActStaged<kSync> act{cm, g, c0, c1, gen, err, stage + wave * (kChainMaxChunks * 64), false, mark_ready};
     wave_task<1>(m, (int)g, c0, c1, acc, act);
     float v = acc[0];
     if (ks > 1) {
@@ -816,18 +924,12 @@ __device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, flo
         v = red[wave * 64 + lane];
         for (int j = 1; j < ks; ++j) v += red[(wave + j) * 64 + lane];
     }
-    const int64_t row = g * kGroupRows + lane;
     if (g >= m.G || row >= m.rows) return;
     if (cm.y) chain_st<kSync>(cm.y + row, tag_word(v, gen));
     if (cm.yf) gwr<float>(cm.yf)[row] = v;
     if (cm.res) {
-        float r;
-        if (cm.res_plain) {
-            r = ((const float*)cm.res)[row];
-        } else {
-            const uint64_t* p = (const uint64_t*)cm.res + row;
-            r = chain_value<kSync>(p, chain_ld<kSync>(p), gen, err);
-        }
+        const float r = cm.res_plain ? ((const float*)cm.res)[row]
+                                     : chain_value<kSync>((const uint64_t*)cm.res + row, rword, gen, err);
         chain_st<kSync>(cm.y2 + row, tag_word(r + v, gen));
     }
 }
@@ -877,7 +979,10 @@ __device__ __forceinline__ void chain_barrier(uint32_t* sync, uint32_t k) {
 template <int kSync>
 __global__ __launch_bounds__(kThreads, 1) void k_chain(ChainParams P) {
     __shared__ float red[kWaves * 64];
+    __shared__ u32x2 stage[kWaves * kChainMaxChunks * 64];
     const uint32_t nwg = gridDim.x, b = blockIdx.x;
+    if (P.trace && threadIdx.x == 0)  // when this workgroup started, after the phase-end plane
+        gwr<uint64_t>(P.trace)[(size_t)P.n_phases * nwg + b] = __builtin_amdgcn_s_memrealtime();
     uint32_t begin = 0;
     for (int p = 0; p < P.n_phases; ++p) {
         const uint32_t end = P.phase_end[p];
@@ -885,9 +990,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_chain(ChainParams P) {
         for (uint32_t j = j0; begin + j < end; j += nwg) {
             const uint32_t t = begin + j;
             const ChainMat cm = P.mats[P.tiles[2 * (size_t)t]];
-            chain_tile<kSync>(cm, P.tiles[2 * (size_t)t + 1], red, P.gen, P.sync);
+            // timeline marks of the workgroup's first tile of the phase
+            const size_t slot = (size_t)p * nwg + b, plane = (size_t)P.n_phases * nwg;
+            uint64_t* ms = P.trace && j == j0 ? P.trace + plane + nwg + slot : nullptr;
+            uint64_t* mr = P.trace && j == j0 ? P.trace + 2 * plane + nwg + slot : nullptr;
+            chain_tile<kSync>(cm, P.tiles[2 * (size_t)t + 1], red, (Q4S_LDS u32x2*)stage, P.gen, P.sync, ms, mr);
             __syncthreads();
         }
+        if (P.trace && threadIdx.x == 0)  // when this workgroup is done with the phase
+            gwr<uint64_t>(P.trace)[(size_t)p * nwg + b] = __builtin_amdgcn_s_memrealtime();
         if constexpr (kSync != kChainTagged)
             if (p + 1 < P.n_phases) chain_barrier<kSync>(P.sync, (uint32_t)p + 1);
         begin = end;

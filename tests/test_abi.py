@@ -207,7 +207,8 @@ def test_chain_host_side(L):
     # bad shapes, modes, counts, pointers and aliasing
     for bad in (q.ChainShape(2, 100, 64, 256, 10), q.ChainShape(2, 128, 0, 256, 10),
                 q.ChainShape(2, 128, 64, 250, 10), q.ChainShape(-1, 128, 64, 256, 10),
-                q.ChainShape(2, 128, 64, 256, 0)):
+                q.ChainShape(2, 128, 64, 256, 0), q.ChainShape(2, 32800, 64, 256, 10),
+                q.ChainShape(2, 128, 64, 32800, 10)):
         assert L.q4s_chain_act_words(ctypes.byref(bad)) == 0
         assert _chain(L, bad, ws, h0, acts, logits)[0] == 2
     assert _chain(L, shape, ws, h0, acts, logits, mode=3)[0] == 2

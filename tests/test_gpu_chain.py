@@ -129,3 +129,36 @@ def test_chain_qwen15_full_bit_exact(qwen15_chain, mode):
     assert info["n_phases"] == 113 and (tags == 1).all()
     assert np.isfinite(lg).all()
     _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, f"1.5B mode {mode}")
+
+
+@pytest.mark.parametrize("mode", [q.CHAIN_TREE, q.CHAIN_TAGGED], ids=["tree", "tagged"])
+def test_chain_trace_timeline(oracle, mode):
+    """With a trace buffer, a step records every workgroup's end of every phase after the
+    launch start; under a barrier every workgroup's ends are non-decreasing; results unchanged."""
+    require_gpu()
+    L, E, D, F, V = 2, 256, 64, 384, 320
+    shapes, ws, h0 = _inputs(45, L, E, D, F, V)
+    ref_acts, ref_logits = oracle.chain_step(ws, E, D, F, V, h0)
+    wp, h0d, acts, logits = _device(shapes, ws, h0, L, E, D, F, V)
+    ch = q.Chain(L, E, D, F, V, wp, h0d, acts, logits, sync_mode=mode, workgroups=6)
+    tr = ch.set_trace(True)
+    ch.run()
+    ch.check()
+    info = ch.info()
+    t = tr.cpu().numpy()
+    P, wg = info["n_phases"], info["workgroups"]
+    assert P == 9 and wg == 6 and t.size == (3 * P + 1) * wg
+    ends, wstart = t[:P * wg].reshape(P, wg), t[P * wg:P * wg + wg]
+    tstart = t[P * wg + wg:2 * P * wg + wg].reshape(P, wg)
+    tready = t[2 * P * wg + wg:].reshape(P, wg)
+    start = wstart.min()
+    assert (wstart > 0).all() and (ends >= wstart[None, :]).all()
+    has = tstart > 0                     # workgroups with a tile in the phase
+    assert has.any(axis=1).all() and ((tready > 0) == has).all()
+    assert (tstart[has] >= start).all() and (tready[has] >= tstart[has]).all() and (ends[has] >= tready[has]).all()
+    if mode != q.CHAIN_TAGGED:
+        assert (np.diff(ends, axis=0) >= 0).all()
+    ch.set_trace(False)
+    ch.close()
+    vals, _ = q.chain_values(acts[:q.chain_act_words(L, E, D, F, V)])
+    _compare(ref_acts, ref_logits, vals.cpu().numpy(), logits.cpu().numpy(), L, E, D, F, "traced")
