@@ -28,7 +28,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "Q4_0 GEMV weight-stream GB/s (% of 8 TB/s HBM peak) and implied tok/s at N=1"
 # the sources the sweep kernel is compiled from (a PMC summary applies only to these)
 KERNEL_SRCS = [os.path.join(ROOT, "q4_weight_streaming_amd", "csrc", f)
-               for f in ("q4s_kernels.hip", "q4s_device.h", "q4s_internal.h")]
+               for f in ("q4s_kernels.hip", "q4s_lane.h", "q4s_device.h", "q4s_internal.h")]
 
 
 def log(msg: str) -> None:

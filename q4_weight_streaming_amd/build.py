@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libq4stream.so")
-SOURCES = ["q4s_kernels.hip", "q4s_q8w.hip", "q4s_attn.hip", "q4s_barrier.hip", "q4s_api.cpp"]
+SOURCES = ["q4s_kernels.hip", "q4s_chain.hip", "q4s_q8w.hip", "q4s_attn.hip", "q4s_barrier.hip", "q4s_api.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

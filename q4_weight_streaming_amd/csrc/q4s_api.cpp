@@ -10,6 +10,7 @@
 #include <new>
 #include <vector>
 
+#include "q4s_chain.h"
 #include "q4s_internal.h"
 
 using namespace q4s;

@@ -61,36 +61,6 @@ struct QuantDesc {
     int32_t pad_;
 };
 
-// One matrix of the chained decode step (one token).  Activations that cross
-// phases are 64-bit words: fp32 bits in the low half, the step's tag in the
-// high half, so a reader can tell this step's value from an older one.
-struct ChainMat {
-    MatDesc m;            // w and geometry (rows, cols, nb, G, C, ks, dstride), n = 1
-    const void* x;        // activation: tagged words [cols], or fp32 when x_plain
-    const uint64_t* x2;   // second factor of an elementwise product (tagged), or NULL
-    const void* res;      // residual input added to the output: tagged, or fp32 when res_plain; or NULL
-    uint64_t* y;          // tagged output [rows], or NULL
-    uint64_t* y2;         // tagged res + y [rows] when res
-    float* yf;            // plain fp32 output [rows] (the logits), or NULL
-    int32_t norm;         // RMS-normalize the activation before quantizing it
-    int32_t x_plain, res_plain, pad_;
-};
-
-// Parameters of one chained-step launch.
-struct ChainParams {
-    const ChainMat* mats;
-    const uint32_t* tiles;      // (matrix, group set) pairs, phase by phase
-    const uint32_t* phase_end;  // cumulative tile count at the end of each phase
-    uint32_t* sync;             // error word, then barrier counters (zeroed before every launch)
-    uint64_t* trace;            // NULL, or the phase timeline (see q4s_chain_set_trace; 100 MHz clock)
-    int32_t n_phases;
-    uint32_t gen;               // this step's tag (never 0)
-};
-
-// Phase synchronisation of the chained step.
-enum ChainSync { kChainCounter = 0, kChainTree = 1, kChainTagged = 2 };
-constexpr int kChainSyncWords = 32 * 18;  // error line, top-counter line, 16 sub-counter lines
-
 // K split chosen from the chunk count alone (so every n and every entry point
 // uses the same partition of a given shape).
 inline int choose_ksplit(int64_t C) { return C <= 8 ? 1 : (C <= 16 ? 2 : 4); }
@@ -116,9 +86,6 @@ hipError_t launch_block_sums(const MatDesc& m, int n, int32_t* s, hipStream_t st
 // The 1-row sweep with the activation quantized by the GEMV waves themselves.
 hipError_t launch_sweep_fused(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles,
                               hipStream_t st);
-// The chained decode step (one cooperative launch; grid = resident workgroups).
-hipError_t launch_chain(int sync_mode, const ChainParams& p, int workgroups, hipStream_t st);
-hipError_t chain_max_workgroups(int sync_mode, int* n);
 // Q8_0 weights (q4s_q8w.hip).
 hipError_t launch_repack_q8_0(const uint8_t* w, uint8_t* packed, int64_t rows, int64_t cols,
                               hipStream_t st);

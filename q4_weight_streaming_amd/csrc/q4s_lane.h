@@ -1,0 +1,241 @@
+// The lane-per-row Q4_0 x Q8_0 GEMV core shared by the sweep kernels and the
+// chained step: the chunk loads, the nibble unpack and per-block integer dot,
+// the Q8_0 block quantizer, and the wave task that streams a row group's
+// chunks in the fixed fp32 order (see the "GEMV core" note below).
+#pragma once
+
+#include "q4s_device.h"
+
+namespace q4s {
+namespace {
+
+// ---------------------------------------------------------------- loads
+
+// The 9 x 16 bytes a lane reads per chunk: 8 blocks of nibbles, then its row's
+// 8 binary16 scales.
+struct Chunk {
+    u32x4 nib[kChunkBlocks];
+    u32x4 scale;
+};
+
+// Weights are streamed with non-temporal loads; the tiled many-row steps
+// (kTemporal) keep them in L2 for the other token tiles of the same rows.
+template <bool kTemporal = false>
+__device__ __forceinline__ void load_chunk(Chunk& ch, const uint8_t* p) {
+#pragma unroll
+    for (int b = 0; b < kChunkBlocks; ++b) {
+        const Q4S_GLOBAL u32x4* a = gp<u32x4>(p + b * (kGroupRows * kBlockNibBytes));
+        ch.nib[b] = kTemporal ? *a : __builtin_nontemporal_load(a);
+    }
+    const Q4S_GLOBAL u32x4* a = gp<u32x4>(p + kChunkNibBytes);
+    ch.scale = kTemporal ? *a : __builtin_nontemporal_load(a);
+}
+
+// ---------------------------------------------------------------- block dot
+
+// Unpacked int8 operands of one block: lo[k] holds elements 4k..4k+3 and hi[k]
+// elements 16+4k..16+4k+3, each as 16*(nibble-8).
+struct Unpacked {
+    uint32_t lo[4], hi[4];
+};
+
+__device__ __forceinline__ Unpacked unpack(u32x4 w) {
+    Unpacked u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        u.lo[k] = (w[k] << 4) & 0xF0F0F0F0u;
+        u.hi[k] = w[k] & 0xF0F0F0F0u;
+    }
+    return u;
+}
+
+// 16 * sum_j (nibble_j - 8) * q_j, exact in int32 (|.| <= 16 * 32512).
+__device__ __forceinline__ int block_dot16(const Unpacked& u, const u32x8& q) {
+    int s = __builtin_amdgcn_sdot4((int)u.lo[0], (int)q[0], 0, false);
+    s = __builtin_amdgcn_sdot4((int)u.lo[1], (int)q[1], s, false);
+    s = __builtin_amdgcn_sdot4((int)u.lo[2], (int)q[2], s, false);
+    s = __builtin_amdgcn_sdot4((int)u.lo[3], (int)q[3], s, false);
+    s = __builtin_amdgcn_sdot4((int)u.hi[0], (int)q[4], s, false);
+    s = __builtin_amdgcn_sdot4((int)u.hi[1], (int)q[5], s, false);
+    s = __builtin_amdgcn_sdot4((int)u.hi[2], (int)q[6], s, false);
+    s = __builtin_amdgcn_sdot4((int)u.hi[3], (int)q[7], s, false);
+    return s;
+}
+
+// ---------------------------------------------------------------- GEMV core
+
+// Summation order shared by every path.  A wave task streams chunks [c0, c1)
+// of one row group.  Within a segment of up to kSegChunks chunks, blocks 0-3
+// of every chunk form chain A and blocks 4-7 chain B, each one fmaf per block
+// in chunk order; at the end of the segment the task accumulator takes
+// acc += (A + B).  The per-block term is fmaf(d_w/16 * d_x, (float)(16 s), .):
+// the product of the two scales is exact, so it equals fmaf(d_w * d_x,
+// (float)s, .) bit for bit.  The MFMA path forms exactly these chains.
+
+// ---------------------------------------------------------------- Q8_0 quantization
+
+// 8 consecutive lanes quantize one block, 4 values each: d = max|x| / 127
+// (correctly rounded fp32 division), q = roundf(x / d) (half away from zero),
+// d_x = binary16(d) rounded to nearest even.  All-zero blocks give d = 0, q = 0.
+// quant8_amax is called by all 8 lanes of a block (it shuffles among them).
+__device__ __forceinline__ float quant8_amax(const f32x4& v) {
+    float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 8));
+    return a;
+}
+
+// this lane's 4 quantized values (packed) and the block's binary16 d_x
+__device__ __forceinline__ void quant8_codes(const f32x4& v, float a, uint32_t& packed, uint16_t& h) {
+    const float dd = a / 127.0f;
+    packed = 0;
+    if (a != 0.0f) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) packed |= ((uint32_t)(uint8_t)(int8_t)(int)roundf(v[k] / dd)) << (8 * k);
+    }
+    h = __half_as_ushort(__float2half_rn(dd));
+}
+
+// Where the lane-per-row path gets the Q8_0 activation.  load(slot, c) runs
+// when chunk c's weight loads are issued (slot 0 or 1 follows the chunk
+// buffer), prepare(slot, c) when chunk c is consumed; q and d then give block
+// blk (b within the chunk) as scalar operands.
+//
+// ActGlobal: the planar buffer in global memory, through scalar loads.
+struct ActGlobal {
+    const MatDesc& m;
+    struct Prep {};
+    __device__ __forceinline__ void load(int, int) {}
+    __device__ __forceinline__ Prep prepare(int, int) { return {}; }
+    __device__ __forceinline__ u32x8 q(const Prep&, int t, int blk, int) const {
+        return act_q(m.xq, (int64_t)t * m.cols + (int64_t)blk * 32);
+    }
+    __device__ __forceinline__ float d(const Prep&, int t, int blk, int) const {
+        return act_d(m.xd, (int64_t)t * m.dstride + blk);
+    }
+};
+
+// ActQuant (the fused 1-row sweep): the wave quantizes the 256 fp32 values of
+// the chunk it is about to consume itself -- lane l holds values 4(l%8) ..
+// 4(l%8)+3 of block l/8, 8 lanes per Q8_0 block with the standalone
+// quantizer's arithmetic -- and broadcasts codes and scales with v_readlane.
+// The activation load travels with the chunk's weight loads, so no barrier or
+// prologue stands between the launch and the weight stream.  With `publish`
+// (the waves of row group 0) the codes are also written to x_q8.
+struct ActQuant {
+    const MatDesc& m;
+    bool publish;
+    f32x4 xs[2];
+    struct Prep {
+        uint32_t packed;  // this lane's 4 codes
+        uint32_t dbits;   // fp32 bits of its block's binary16 d_x
+    };
+    __device__ __forceinline__ void load(int slot, int c) {
+        const int lane = threadIdx.x & 63;
+        // clamped, so the load is unconditional; lanes past the row are zeroed in prepare
+        const int64_t i = min((int64_t)c * 256 + 4 * lane, (int64_t)m.cols - 4);
+        xs[slot] = *gp<f32x4>(m.x + i);
+    }
+    __device__ __forceinline__ Prep prepare(int slot, int c) {
+        const int lane = threadIdx.x & 63;
+        const int blk = c * kChunkBlocks + (lane >> 3);
+        const bool valid = blk < m.nb;  // uniform over the 8 lanes of a block
+        f32x4 v = xs[slot];
+        if (!valid) v = (f32x4){0.f, 0.f, 0.f, 0.f};
+        const float a = quant8_amax(v);
+        uint32_t packed;
+        uint16_t h;
+        quant8_codes(v, a, packed, h);
+        if (publish && valid) {
+            const int o = lane & 7;
+            *gwr<uint32_t>((void*)(m.xq + (int64_t)c * 256 + 4 * lane)) = packed;
+            if (o == 0) *gwr<uint16_t>((void*)(m.xd + blk)) = h;
+            if (blk == m.nb - 1 && o < m.dstride - m.nb) gwr<uint16_t>((void*)m.xd)[m.nb + o] = 0;
+        }
+        return {packed, __float_as_uint(__half2float(__ushort_as_half(h)))};
+    }
+    __device__ __forceinline__ u32x8 q(const Prep& p, int, int, int b) const {
+        u32x8 r;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) r[k] = __builtin_amdgcn_readlane(p.packed, 8 * b + k);
+        return r;
+    }
+    __device__ __forceinline__ float d(const Prep& p, int, int, int b) const {
+        return __uint_as_float(__builtin_amdgcn_readlane(p.dbits, 8 * b));
+    }
+};
+
+// Adds chunk `c` (held in ch) of the lane's row into the chains pa / pb.
+template <int N, class Act>
+__device__ __forceinline__ void chunk_fma(const MatDesc& m, int c, const Chunk& ch, float (&pa)[N],
+                                          float (&pb)[N], Act& act, int slot) {
+    const auto pr = act.prepare(slot, c);
+#pragma unroll
+    for (int b = 0; b < kChunkBlocks; ++b) {
+        // padding blocks of the last chunk have zero nibbles and scale; read a
+        // valid activation block for them
+        const int blk = min(c * kChunkBlocks + b, m.nb - 1);
+        const uint32_t sw = ch.scale[b >> 1];
+        const float dw16 = ((b & 1) ? half_hi(sw) : half_lo(sw)) * 0.0625f;
+        const Unpacked u = unpack(ch.nib[b]);
+#pragma unroll
+        for (int t = 0; t < N; ++t) {
+            const u32x8 q = act.q(pr, t, blk, b);
+            const int s16 = block_dot16(u, q);
+            const float dx = act.d(pr, t, blk, b);
+            float& p = (b < kChunkBlocks / 2) ? pa[t] : pb[t];
+            p = fmaf(dw16 * dx, (float)s16, p);
+        }
+    }
+}
+
+// One wave streams chunks [c0, c1) of row group g; lane = row.
+template <int N, class Act>
+__device__ __forceinline__ void wave_task(const MatDesc& m, int g, int c0, int c1, float (&acc)[N], Act& act) {
+    const int lane = threadIdx.x & 63;
+    float pa[N], pb[N];
+#pragma unroll
+    for (int t = 0; t < N; ++t) acc[t] = pa[t] = pb[t] = 0.0f;
+    if (g >= m.G || c0 >= c1) return;
+    const uint8_t* wp = m.w + ((size_t)g * m.C + c0) * kChunkBytes + lane * kBlockNibBytes;
+    auto seg_end = [&](int c) {  // after chunk c: close the segment if it ends here
+        if (c + 1 == c1 || (c + 1 - c0) % kSegChunks == 0) {
+#pragma unroll
+            for (int t = 0; t < N; ++t) {
+                acc[t] += pa[t] + pb[t];
+                pa[t] = pb[t] = 0.0f;
+            }
+        }
+    };
+    // The steady-state body prefetches unconditionally so that every path
+    // reaching a chunk's use has the same loads outstanding (a conditional
+    // prefetch makes the compiler wait for all loads, the prefetch included).
+    Chunk a, b;
+    load_chunk(a, wp);
+    act.load(0, c0);
+    int c = c0;
+    for (; c + 2 < c1; c += 2, wp += 2 * kChunkBytes) {
+        load_chunk(b, wp + kChunkBytes);
+        act.load(1, c + 1);
+        chunk_fma<N>(m, c, a, pa, pb, act, 0);
+        seg_end(c);
+        load_chunk(a, wp + 2 * kChunkBytes);
+        act.load(0, c + 2);
+        chunk_fma<N>(m, c + 1, b, pa, pb, act, 1);
+        seg_end(c + 1);
+    }
+    if (c + 1 < c1) {  // two chunks left
+        load_chunk(b, wp + kChunkBytes);
+        act.load(1, c + 1);
+        chunk_fma<N>(m, c, a, pa, pb, act, 0);
+        seg_end(c);
+        chunk_fma<N>(m, c + 1, b, pa, pb, act, 1);
+        seg_end(c + 1);
+    } else {           // one chunk left
+        chunk_fma<N>(m, c, a, pa, pb, act, 0);
+        seg_end(c);
+    }
+}
+
+}  // namespace
+}  // namespace q4s
