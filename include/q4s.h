@@ -425,6 +425,14 @@ q4s_status q4s_chain_run(q4s_chain* chain, void* stream);
 /* Synchronize `stream`; Q4S_ERR_WAIT if a wait of the last step gave up. */
 q4s_status q4s_chain_check(const q4s_chain* chain, void* stream);
 
+/*
+ * Polls a wait of later steps may spend before it gives up (default 2^20,
+ * about a second; 0: give up at the first read that is not ready yet).  A
+ * step whose wait gave up still runs to its end; its results are invalid and
+ * q4s_chain_check reports Q4S_ERR_WAIT.  The next step starts afresh.
+ */
+q4s_status q4s_chain_set_wait_limit(q4s_chain* chain, uint32_t polls);
+
 q4s_status q4s_chain_get_info(const q4s_chain* chain, q4s_chain_info* info);
 
 /*

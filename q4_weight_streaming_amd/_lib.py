@@ -101,6 +101,7 @@ def lib():
             "q4s_chain_destroy": ([p], None),
             "q4s_chain_trace_bytes": ([p], sz),
             "q4s_chain_set_trace": ([p, p, sz], i32),
+            "q4s_chain_set_wait_limit": ([p, ctypes.c_uint32], i32),
             "q4s_bench_read": ([p, sz, i32, i32, p, p], i32),
             "q4s_bench_copy": ([p, p, sz, p], i32),
             "q4s_bench_grid_barrier": ([i32, i32, i32, p, sz, p], i32),
@@ -409,6 +410,9 @@ class Chain:
         self._trace = torch.zeros(n, dtype=torch.int64, device=self.device)
         _check("q4s_chain_set_trace", lib().q4s_chain_set_trace(self._chain, self._trace.data_ptr(), n * 8))
         return self._trace
+
+    def set_wait_limit(self, polls: int) -> None:
+        _check("q4s_chain_set_wait_limit", lib().q4s_chain_set_wait_limit(self._chain, polls))
 
     def check(self) -> None:
         """Synchronize; raise Q4SError (status 7) if a bounded wait of the last step gave up."""

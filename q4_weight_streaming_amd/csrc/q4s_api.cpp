@@ -516,6 +516,7 @@ struct q4s_chain {
     uint32_t gen = 0;
     int64_t steps = 0;
     uint64_t* trace = nullptr;
+    uint32_t spin_limit = kChainDefaultSpin;
 };
 
 static bool chain_shape_ok(const q4s_chain_shape* s) {
@@ -702,7 +703,8 @@ q4s_status q4s_chain_run(q4s_chain* p, void* stream) {
     cp.n_phases = (int32_t)p->phase_end.size();
     cp.gen = p->gen;
     cp.trace = p->trace;
-    q4s_status s = hip_status(launch_chain(p->mode, cp, p->workgroups, (hipStream_t)stream), "chain launch");
+    q4s_status s =
+        hip_status(launch_chain(p->mode, cp, p->workgroups, p->spin_limit, (hipStream_t)stream), "chain launch");
     if (s == Q4S_OK) ++p->steps;
     return s;
 }
@@ -733,6 +735,12 @@ q4s_status q4s_chain_set_trace(q4s_chain* p, uint64_t* trace, size_t trace_bytes
         if (trace_bytes < need) return fail(Q4S_ERR_SHAPE, "trace holds %zu bytes, needs %zu", trace_bytes, need);
     }
     p->trace = trace;
+    return ok();
+}
+
+q4s_status q4s_chain_set_wait_limit(q4s_chain* p, uint32_t polls) {
+    if (!p) return fail(Q4S_ERR_NULL, "chain is NULL");
+    p->spin_limit = polls;
     return ok();
 }
 

@@ -34,10 +34,12 @@ struct ChainParams {
 
 // Phase synchronisation of the chained step.
 enum ChainSync { kChainCounter = 0, kChainTree = 1, kChainTagged = 2 };
-constexpr int kChainSyncWords = 32 * 18;  // error line, top-counter line, 16 sub-counter lines
+// error line (word 0 error flag, 1 release word, 3 poll limit), top-counter line, 16 sub-counter lines
+constexpr int kChainSyncWords = 32 * 18;
 
 // The chained decode step (one cooperative launch; grid = resident workgroups).
-hipError_t launch_chain(int sync_mode, const ChainParams& p, int workgroups, hipStream_t st);
+hipError_t launch_chain(int sync_mode, const ChainParams& p, int workgroups, uint32_t spin_limit, hipStream_t st);
+constexpr uint32_t kChainDefaultSpin = 1u << 20;
 hipError_t chain_max_workgroups(int sync_mode, int* n);
 
 }  // namespace q4s

@@ -36,11 +36,15 @@ namespace {
 //    this step's tag.  Each word is its own flag, so no fence is needed; this
 //    avoids the per-workgroup L2 write-back and invalidate that device-scope
 //    release and acquire cost on the multi-XCD chip.
-// Every wait is bounded: past the limit the error word is set, every other
-// wait then gives up within ~1000 polls, and the launch runs to its end with
-// whatever values it has.
+// Every wait is bounded: past the limit (2^20 polls unless the caller sets
+// another) the error word is set, every other wait then gives up within ~1000
+// polls, and the launch runs to its end with whatever values it has.
 
-constexpr int64_t kChainSpin = 1 << 20;
+// The poll limit of this launch: sync word 3, written by the clearing launch
+// before it (q4s_chain_set_wait_limit; 2^20 polls unless set).
+__device__ __forceinline__ int64_t chain_spin_limit(const uint32_t* sync) {
+    return (int64_t)*gp<uint32_t>(sync + 3);
+}
 
 __device__ __forceinline__ uint64_t tag_word(float v, uint32_t gen) {
     return ((uint64_t)gen << 32) | (uint64_t)__float_as_uint(v);
@@ -75,10 +79,11 @@ __device__ __forceinline__ void chain_fail(uint32_t* err) {
 template <int kSync>
 __device__ __forceinline__ float chain_value(const uint64_t* p, uint64_t w, uint32_t gen, uint32_t* err) {
     if constexpr (kSync == kChainTagged) {
+        const int64_t limit = chain_spin_limit(err);
         int64_t spins = 0;
         while ((uint32_t)(w >> 32) != gen) {
             // give up past the limit, or at once once any other wait has given up
-            if (++spins > kChainSpin || ((spins & 1023) == 0 && chain_failed(err))) {
+            if (++spins > limit || ((spins & 1023) == 0 && chain_failed(err))) {
                 chain_fail(err);
                 break;
             }
@@ -123,11 +128,12 @@ __device__ __forceinline__ void chain_batch(const uint64_t* x, int n, int b0, in
         return ok;
     };
     if constexpr (kSync == kChainTagged) {
+        const int64_t limit = chain_spin_limit(err);
         int64_t spins = 0;
         for (;;) {
             load_all();
             if (all_tagged()) break;
-            if (++spins > kChainSpin || ((spins & 1023) == 0 && chain_failed(err))) {
+            if (++spins > limit || ((spins & 1023) == 0 && chain_failed(err))) {
                 chain_fail(err);
                 break;
             }
@@ -363,9 +369,10 @@ __device__ __forceinline__ void chain_barrier(uint32_t* sync, uint32_t k) {
             watch = err + 1;
             target = k;
         }
+        const int64_t limit = chain_spin_limit(sync);
         int64_t spins = 0;
         while (__hip_atomic_load(watch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            if (++spins > kChainSpin || ((spins & 1023) == 0 && chain_failed(sync))) {
+            if (++spins > limit || ((spins & 1023) == 0 && chain_failed(sync))) {
                 __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
@@ -405,14 +412,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_chain(ChainParams P) {
     }
 }
 
-__global__ __launch_bounds__(256) void k_zero_words(uint32_t* w, int n) {
-    for (int i = threadIdx.x; i < n; i += 256) w[i] = 0;
+// Clears the sync words before a launch and sets its poll limit (word 3).
+__global__ __launch_bounds__(256) void k_chain_reset(uint32_t* w, int n, uint32_t spin_limit) {
+    for (int i = threadIdx.x; i < n; i += 256) w[i] = i == 3 ? spin_limit : 0u;
 }
 
 }  // namespace
 
-hipError_t launch_chain(int sync_mode, const ChainParams& p, int workgroups, hipStream_t st) {
-    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, st, p.sync, kChainSyncWords);
+hipError_t launch_chain(int sync_mode, const ChainParams& p, int workgroups, uint32_t spin_limit, hipStream_t st) {
+    hipLaunchKernelGGL(k_chain_reset, dim3(1), dim3(256), 0, st, p.sync, kChainSyncWords, spin_limit);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     ChainParams a = p;

@@ -162,3 +162,48 @@ def test_chain_trace_timeline(oracle, mode):
     ch.close()
     vals, _ = q.chain_values(acts[:q.chain_act_words(L, E, D, F, V)])
     _compare(ref_acts, ref_logits, vals.cpu().numpy(), logits.cpu().numpy(), L, E, D, F, "traced")
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_chain_wait_limit_zero_reports_and_recovers(oracle, mode):
+    """With a wait limit of 0 polls a wait that finds its input not yet ready gives up: the
+    step still ends (no hang), q4s_chain_check reports Q4S_ERR_WAIT; with the default limit
+    restored the next step is bit-exact again."""
+    require_gpu()
+    L, E, D, F, V = 4, 256, 64, 384, 320
+    shapes, ws, h0 = _inputs(46, L, E, D, F, V)
+    ref_acts, ref_logits = oracle.chain_step(ws, E, D, F, V, h0)
+    wp, h0d, acts, logits = _device(shapes, ws, h0, L, E, D, F, V)
+    ch = q.Chain(L, E, D, F, V, wp, h0d, acts, logits, sync_mode=mode, workgroups=0)
+    ch.set_wait_limit(0)
+    ch.run()
+    with pytest.raises(q.Q4SError) as e:
+        ch.check()
+    assert e.value.status == q.ERR_WAIT
+    ch.set_wait_limit(1 << 20)
+    ch.run()
+    ch.check()
+    ch.close()
+    vals, tags = q.chain_values(acts[:q.chain_act_words(L, E, D, F, V)])
+    assert (tags.cpu().numpy() == 2).all()
+    _compare(ref_acts, ref_logits, vals.cpu().numpy(), logits.cpu().numpy(), L, E, D, F, "after recovery")
+
+
+@pytest.fixture(scope="module")
+def qwen7b_chain(oracle):
+    require_gpu()
+    L, E, D, F, V = 28, 3584, 512, 18944, 152064
+    shapes, ws, h0 = _inputs(47, L, E, D, F, V)
+    ref = oracle.chain_step(ws, E, D, F, V, h0)
+    dv = _device(shapes, ws, h0, L, E, D, F, V)
+    del ws
+    return (L, E, D, F, V), ref, dv
+
+
+def test_chain_qwen7b_full_bit_exact(qwen7b_chain):
+    """The Qwen2.5-7B-shaped chain (28 layers, 3.98 GB), tagged sync: every vector and logit
+    equals the oracle's (ff 18944: four K splits of 18-19 chunks, two segments each)."""
+    (L, E, D, F, V), (ref_acts, ref_logits), (wp, h0d, acts, logits) = qwen7b_chain
+    vals, tags, lg, info = _run(wp, h0d, acts, logits, L, E, D, F, V, q.CHAIN_TAGGED, 0)
+    assert info["n_phases"] == 113 and (tags == 1).all() and np.isfinite(lg).all()
+    _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, "7B tagged")
