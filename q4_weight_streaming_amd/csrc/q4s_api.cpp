@@ -506,7 +506,9 @@ struct q4s_chain {
     uint64_t* acts = nullptr;
     int64_t act_words = 0;
     std::vector<ChainMat> mats;
-    std::vector<uint32_t> tiles;      // (matrix, group set), phase by phase, largest first within a phase
+    std::vector<std::vector<uint32_t>> phases;  // the matrices of each phase
+    int layout_wg = 0;                // the workgroup count the tile table was laid out for
+    std::vector<uint32_t> tiles;      // (matrix, tile word), phase by phase, largest first within a phase
     std::vector<uint32_t> phase_end;  // cumulative tile count per phase
     q4s_chain_info info{};
     // device image: [ChainMat x n][tiles][phase_end][sync words], 16-byte aligned parts
@@ -518,6 +520,60 @@ struct q4s_chain {
     uint64_t* trace = nullptr;
     uint32_t spin_limit = kChainDefaultSpin;
 };
+
+// The tile table for `wg` persistent workgroups.  Per phase, the finest layout
+// whose tile count fits the workgroups: one row group per tile with its chunks
+// spread over the 4 waves (matrices with one or two K splits), or two row
+// groups per tile with two waves each (one K split); else a group set per tile
+// (one wave per row group, or per K range).  The device image keeps room for the
+// largest table (one tile per row group).
+static void chain_layout(q4s_chain* p, int wg) {
+    struct Tile { uint32_t mat, word; int64_t bytes; };
+    p->tiles.clear();
+    p->phase_end.clear();
+    int64_t max_tiles = 0;
+    for (const std::vector<uint32_t>& members : p->phases) {
+        int64_t groups = 0;
+        bool splittable = true, narrow = true;
+        for (uint32_t i : members) {
+            groups += p->mats[i].m.G;
+            splittable = splittable && p->mats[i].m.ks <= 2;  // <= 16 chunks
+            narrow = narrow && p->mats[i].m.ks == 1;          // <= 8 chunks
+        }
+        max_tiles += groups;
+        const uint32_t mode = !splittable                          ? 0u
+                              : groups <= wg                       ? kChainSplit4
+                              : narrow && (groups + 1) / 2 <= wg   ? kChainSplit2
+                                                                   : 0u;
+        std::vector<Tile> phase;
+        for (uint32_t i : members) {
+            const MatDesc& m = p->mats[i].m;
+            const int gpt = mode == kChainSplit4 ? 1 : (mode == kChainSplit2 ? 2 : kWaves / m.ks);
+            for (int64_t t = 0; t * gpt < m.G; ++t) {
+                const int64_t n = std::min<int64_t>(gpt, m.G - t * gpt);
+                phase.push_back({i, (uint32_t)t | mode, n * m.C * kChunkBytes});
+            }
+        }
+        std::stable_sort(phase.begin(), phase.end(), [](const Tile& a, const Tile& b) { return a.bytes > b.bytes; });
+        for (const Tile& t : phase) {
+            p->tiles.push_back(t.mat);
+            p->tiles.push_back(t.word);
+        }
+        p->phase_end.push_back((uint32_t)(p->tiles.size() / 2));
+    }
+    auto up16 = [](size_t v) { return (v + 15) & ~(size_t)15; };
+    p->off_tiles = up16(p->mats.size() * sizeof(ChainMat));
+    p->off_phase = p->off_tiles + up16((size_t)max_tiles * 2 * sizeof(uint32_t));
+    p->off_sync = p->off_phase + up16(p->phase_end.size() * sizeof(uint32_t));
+    p->dev_bytes = p->off_sync + up16(kChainSyncWords * sizeof(uint32_t));
+    p->image.assign(p->dev_bytes, 0);
+    memcpy(p->image.data(), p->mats.data(), p->mats.size() * sizeof(ChainMat));
+    memcpy(p->image.data() + p->off_tiles, p->tiles.data(), p->tiles.size() * sizeof(uint32_t));
+    memcpy(p->image.data() + p->off_phase, p->phase_end.data(), p->phase_end.size() * sizeof(uint32_t));
+    p->info.n_tiles = (int64_t)p->tiles.size() / 2;
+    p->info.dev_bytes = (int64_t)p->dev_bytes;
+    p->layout_wg = wg;
+}
 
 static bool chain_shape_ok(const q4s_chain_shape* s) {
     // hidden and ff <= 32768 keep every wave's K range within its 32-chunk LDS slice
@@ -583,26 +639,14 @@ q4s_status q4s_chain_create(const q4s_chain_shape* shape, const void* const* w_p
         p->info.packed_bytes += (int64_t)packed_bytes(r, c);
         return cm;
     };
-    struct Tile { uint32_t mat, gset; int64_t bytes; };
-    std::vector<Tile> phase;
+    std::vector<uint32_t> members;  // matrices of the phase being built
     auto add = [&](const ChainMat& cm) {
-        const uint32_t i = (uint32_t)p->mats.size();
+        members.push_back((uint32_t)p->mats.size());
         p->mats.push_back(cm);
-        const int gpw = kWaves / cm.m.ks;
-        const int64_t ng = gsets_of(cm.m.G, cm.m.ks);
-        for (int64_t gs = 0; gs < ng; ++gs) {
-            const int64_t groups = std::min<int64_t>(gpw, cm.m.G - gs * gpw);
-            phase.push_back({i, (uint32_t)gs, groups * cm.m.C * kChunkBytes});
-        }
     };
     auto close = [&]() {
-        std::stable_sort(phase.begin(), phase.end(), [](const Tile& a, const Tile& b) { return a.bytes > b.bytes; });
-        for (const Tile& t : phase) {
-            p->tiles.push_back(t.mat);
-            p->tiles.push_back(t.gset);
-        }
-        p->phase_end.push_back((uint32_t)(p->tiles.size() / 2));
-        phase.clear();
+        p->phases.push_back(members);
+        members.clear();
     };
     for (int64_t l = 0; l < L; ++l) {
         const void* const* lw = w_packed + 7 * l;
@@ -643,20 +687,12 @@ q4s_status q4s_chain_create(const q4s_chain_shape* shape, const void* const* w_p
         add(cm);
         close();
     }
-    auto up16 = [](size_t v) { return (v + 15) & ~(size_t)15; };
-    p->off_tiles = up16(p->mats.size() * sizeof(ChainMat));
-    p->off_phase = p->off_tiles + up16(p->tiles.size() * sizeof(uint32_t));
-    p->off_sync = p->off_phase + up16(p->phase_end.size() * sizeof(uint32_t));
-    p->dev_bytes = p->off_sync + up16(kChainSyncWords * sizeof(uint32_t));
-    p->image.assign(p->dev_bytes, 0);
-    memcpy(p->image.data(), p->mats.data(), p->mats.size() * sizeof(ChainMat));
-    memcpy(p->image.data() + p->off_tiles, p->tiles.data(), p->tiles.size() * sizeof(uint32_t));
-    memcpy(p->image.data() + p->off_phase, p->phase_end.data(), p->phase_end.size() * sizeof(uint32_t));
+    // laid out for the requested workgroups (256 when left to the upload, which lays it out
+    // again for the count it resolves); dev_bytes does not depend on the count
+    chain_layout(p, workgroups ? workgroups : 256);
     p->info.n_mats = n_mats;
     p->info.n_phases = (int64_t)p->phase_end.size();
-    p->info.n_tiles = (int64_t)p->tiles.size() / 2;
     p->info.act_words = words;
-    p->info.dev_bytes = (int64_t)p->dev_bytes;
     *dev_bytes_needed = p->dev_bytes;
     *out = p;
     return ok();
@@ -678,6 +714,7 @@ q4s_status q4s_chain_upload(q4s_chain* p, void* dev_mem, size_t dev_bytes, void*
     const int wg = p->workgroups_req ? p->workgroups_req : std::min(cus, max_wg);
     if (wg < 1 || wg > max_wg)
         return fail(Q4S_ERR_SHAPE, "workgroups=%d out of [1, %d] (all must be resident at once)", wg, max_wg);
+    if (wg != p->layout_wg) chain_layout(p, wg);
     hipStream_t st = (hipStream_t)stream;
     if ((e = hipMemcpyAsync(dev_mem, p->image.data(), p->dev_bytes, hipMemcpyHostToDevice, st)) != hipSuccess)
         return hip_status(e, "chain upload");

@@ -40,6 +40,12 @@ constexpr int kChainSyncWords = 32 * 18;
 // The chained decode step (one cooperative launch; grid = resident workgroups).
 hipError_t launch_chain(int sync_mode, const ChainParams& p, int workgroups, uint32_t spin_limit, hipStream_t st);
 constexpr uint32_t kChainDefaultSpin = 1u << 20;
+// Tile word: the tile index in bits 0-29; bit 31: one row group whose chunks
+// are spread over the 4 waves; bit 30: two row groups, two waves each; neither:
+// a group set (one wave per row group, or per K range).
+constexpr uint32_t kChainSplit4 = 1u << 31;
+constexpr uint32_t kChainSplit2 = 1u << 30;
+constexpr uint32_t kChainTileIndex = kChainSplit2 - 1;
 hipError_t chain_max_workgroups(int sync_mode, int* n);
 
 }  // namespace q4s

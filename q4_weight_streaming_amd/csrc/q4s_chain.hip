@@ -130,6 +130,16 @@ __device__ __forceinline__ void chain_batch(const uint64_t* x, int n, int b0, in
     if constexpr (kSync == kChainTagged) {
         const int64_t limit = chain_spin_limit(err);
         int64_t spins = 0;
+        // light poll first: the lane's last word of the batch (one load per lane and
+        // round instead of the whole batch, so waiting waves do not crowd the
+        // producers' memory channels); then the whole batch, re-read until all tagged
+        {
+            const int i = min((b0 + cnt - 1) * 256 + 4 * lane, n - 4) + 3;
+            while ((uint32_t)(chain_ld<kSync>(x + i) >> 32) != gen) {
+                if (++spins > limit || ((spins & 1023) == 0 && chain_failed(err))) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
         for (;;) {
             load_all();
             if (all_tagged()) break;
@@ -226,12 +236,12 @@ __device__ __noinline__ void chain_stage(const void* x, const uint64_t* x2, int 
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
         s = sqrtf(p / (float)n + 1e-6f);
-        if (nc <= kChainBatch && c0 == 0 && c1 == nc) {  // the last batch was the whole range: reuse it
+        if (nc <= kChainBatch) {  // the one batch was the whole vector: quantize this wave's chunks from it
 #pragma unroll
             for (int cc = 0; cc < kChainBatch; ++cc)
-                if (cc < nc)
+                if (cc >= c0 && cc < c1)
                     chain_quant((f32x4){v[cc][0] / s, v[cc][1] / s, v[cc][2] / s, v[cc][3] / s}, cc, nb,
-                                slice + cc * 64);
+                                slice + (cc - c0) * 64);
             return;
         }
     }
@@ -340,6 +350,111 @@ __device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, flo
     }
 }
 
+// Row groups of a matrix with one or two K splits (at most 16 chunks) in a
+// phase small enough to give each row group 4 waves (wpg = 4: one group per
+// tile) or, for at most 8 chunks, 2 waves (wpg = 2: two groups per tile).  Wave lw of a group stages
+// and multiplies chunks [ceil(lw C/wpg), ceil((lw+1) C/wpg)) and leaves each
+// block's exact integer sum (as int16: |s| <= 32512) and its binary16 d_w in
+// the group's term table; then wave lw < ks of the group runs the fixed-order
+// fp32 chain of K range lw over those terms -- the same fmaf(d_w/16 * d_x,
+// 16 s, chain) per block, in the same order, as wave_task -- and the ranges are
+// added in order.  So the result is bit-identical to the one-wave-per-range
+// tile, with 1/wpg of the serial work per wave.
+constexpr int kChainSplitChunks = 16;  // chunks of a matrix with ks <= 2
+constexpr int kChainTermWords = kChainSplitChunks * kChunkBlocks * 64;  // one group's term table
+
+template <int kWpg>
+__device__ __forceinline__ int split_first(int w, int C) { return (w * C + kWpg - 1) / kWpg; }
+
+template <int kSync>
+__device__ __forceinline__ void chunk_terms(int c, const Chunk& ch, ActStaged<kSync>& act, Q4S_LDS uint32_t* terms) {
+    const int lane = threadIdx.x & 63;
+    const auto pr = act.prepare(0, c);
+#pragma unroll
+    for (int b = 0; b < kChunkBlocks; ++b) {
+        const uint32_t sw = ch.scale[b >> 1];
+        const uint32_t dw_bits = (b & 1) ? (sw >> 16) : (sw & 0xffffu);
+        const int s16 = block_dot16(unpack(ch.nib[b]), act.q(pr, 0, 0, b));
+        terms[(c * kChunkBlocks + b) * 64 + lane] = (uint32_t)(uint16_t)(int16_t)(s16 >> 4) | (dw_bits << 16);
+    }
+}
+
+template <int kSync, int kWpg>
+__device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t tile, float* red,
+                                                 Q4S_LDS u32x2* stage, Q4S_LDS uint32_t* terms, uint32_t gen,
+                                                 uint32_t* err, uint64_t* mark_start, uint64_t* mark_ready) {
+    if (mark_start && threadIdx.x == 0) gwr<uint64_t>(mark_start)[0] = __builtin_amdgcn_s_memrealtime();
+    const MatDesc& m = cm.m;
+    const int wave = wave_uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int C = m.C, ks = m.ks;
+    const int gi = wave / kWpg, lw = wave % kWpg;  // the wave's group within the tile, its place in the group
+    const int64_t g = tile * (kWaves / kWpg) + gi;
+    const bool live = g < m.G;
+    // one group's table takes all kChainTermWords (<= 16 chunks); two groups (<= 8 chunks each) halve it
+    Q4S_LDS uint32_t* gterms = terms + gi * (kChainTermWords / 2);
+    const int64_t row = g * kGroupRows + lane;
+    const int64_t rrow = min(row, (int64_t)m.rows - 1);
+    uint64_t rword = 0;
+    if (cm.res && !cm.res_plain && lw == 0 && live) rword = chain_ld<kSync>((const uint64_t*)cm.res + rrow);
+    // integer work of this wave's chunks
+    const int i0 = split_first<kWpg>(lw, C), i1 = split_first<kWpg>(lw + 1, C);
+    if (live && i0 < i1) {
+        Q4S_LDS u32x2* slice = stage + wave * (kChainMaxChunks * 64);
+        ActStaged<kSync> act{cm, g, i0, i1, gen, err, slice, false, wave == 0 ? mark_ready : nullptr};
+        const uint8_t* wp = m.w + ((size_t)g * m.C + i0) * kChunkBytes + lane * kBlockNibBytes;
+        Chunk a, b;
+        load_chunk(a, wp);
+        if (i0 + 1 < i1) load_chunk(b, wp + kChunkBytes);
+        for (int c = i0; c < i1; c += 2) {
+            chunk_terms<kSync>(c, a, act, gterms);
+            if (c + 2 < i1) load_chunk(a, wp + (size_t)(c + 2 - i0) * kChunkBytes);
+            if (c + 1 < i1) {
+                chunk_terms<kSync>(c + 1, b, act, gterms);
+                if (c + 3 < i1) load_chunk(b, wp + (size_t)(c + 3 - i0) * kChunkBytes);
+            }
+        }
+    }
+    __syncthreads();
+    // the fixed-order fp32 chains, one wave per K range (a range of <= 8 chunks is one segment)
+    if (live && lw < ks) {
+        const int c0 = (int)((int64_t)lw * C / ks), c1 = (int)((int64_t)(lw + 1) * C / ks);
+        // where the group's waves' slices start (wave w staged chunks [first[w], first[w + 1]))
+        int first[kWpg + 1];
+#pragma unroll
+        for (int w = 0; w <= kWpg; ++w) first[w] = split_first<kWpg>(w, C);
+        float pa = 0.0f, pb = 0.0f;
+        int w = 0;  // the wave of the group that staged chunk c
+        for (int c = c0; c < c1; ++c) {
+            while (c >= first[w + 1]) ++w;
+            const Q4S_LDS u32x2* st = stage + (gi * kWpg + w) * (kChainMaxChunks * 64) + (c - first[w]) * 64;
+#pragma unroll
+            for (int b = 0; b < kChunkBlocks; ++b) {
+                const uint32_t t = gterms[(c * kChunkBlocks + b) * 64 + lane];
+                const float dw16 = half_hi(t) * 0.0625f;
+                const float dx = __uint_as_float(st[8 * b][1]);
+                const float s16 = (float)((int)(int16_t)(t & 0xffffu) * 16);
+                float& p = b < kChunkBlocks / 2 ? pa : pb;
+                p = fmaf(dw16 * dx, s16, p);
+            }
+        }
+        float acc = 0.0f;
+        acc += pa + pb;
+        red[wave * 64 + lane] = acc;
+    }
+    __syncthreads();
+    if (!live || lw != 0 || row >= m.rows) return;
+    float v = red[wave * 64 + lane];
+    for (int j = 1; j < ks; ++j) v += red[(wave + j) * 64 + lane];
+    if (cm.y) chain_st<kSync>(cm.y + row, tag_word(v, gen));
+    if (cm.yf) gwr<float>(cm.yf)[row] = v;
+    if (cm.res) {
+        const float r = cm.res_plain ? ((const float*)cm.res)[row]
+                                     : chain_value<kSync>((const uint64_t*)cm.res + row, rword, gen, err);
+        chain_st<kSync>(cm.y2 + row, tag_word(r + v, gen));
+    }
+}
+
 // Phase barrier number k (1-based) of a launch; sync: [0] error word,
 // [32] top counter, [64 + 32 i] sub-counter i.  Counters start at 0 per launch.
 template <int kSync>
@@ -387,6 +502,7 @@ template <int kSync>
 __global__ __launch_bounds__(kThreads, 1) void k_chain(ChainParams P) {
     __shared__ float red[kWaves * 64];
     __shared__ u32x2 stage[kWaves * kChainMaxChunks * 64];
+    __shared__ uint32_t terms[kChainTermWords];
     const uint32_t nwg = gridDim.x, b = blockIdx.x;
     if (P.trace && threadIdx.x == 0)  // when this workgroup started, after the phase-end plane
         gwr<uint64_t>(P.trace)[(size_t)P.n_phases * nwg + b] = __builtin_amdgcn_s_memrealtime();
@@ -401,7 +517,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_chain(ChainParams P) {
             const size_t slot = (size_t)p * nwg + b, plane = (size_t)P.n_phases * nwg;
             uint64_t* ms = P.trace && j == j0 ? P.trace + plane + nwg + slot : nullptr;
             uint64_t* mr = P.trace && j == j0 ? P.trace + 2 * plane + nwg + slot : nullptr;
-            chain_tile<kSync>(cm, P.tiles[2 * (size_t)t + 1], red, (Q4S_LDS u32x2*)stage, P.gen, P.sync, ms, mr);
+            const uint32_t tw = P.tiles[2 * (size_t)t + 1];
+            if (tw & kChainSplit4)  // one row group, its chunks spread over the 4 waves
+                chain_tile_split<kSync, 4>(cm, tw & kChainTileIndex, red, (Q4S_LDS u32x2*)stage,
+                                           (Q4S_LDS uint32_t*)terms, P.gen, P.sync, ms, mr);
+            else if (tw & kChainSplit2)  // two row groups, two waves each
+                chain_tile_split<kSync, 2>(cm, tw & kChainTileIndex, red, (Q4S_LDS u32x2*)stage,
+                                           (Q4S_LDS uint32_t*)terms, P.gen, P.sync, ms, mr);
+            else  // a group set: one wave per row group (or K range)
+                chain_tile<kSync>(cm, tw, red, (Q4S_LDS u32x2*)stage, P.gen, P.sync, ms, mr);
             __syncthreads();
         }
         if (P.trace && threadIdx.x == 0)  // when this workgroup is done with the phase
