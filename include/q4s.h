@@ -444,8 +444,8 @@ q4s_status q4s_chain_get_info(const q4s_chain* chain, q4s_chain_info* info);
  *   trace[P * W + W + s]  when b started its first tile of phase p;
  *   trace[2 P W + W + s]  when that tile's activation prologue was done (its
  *                         input had arrived, been normalized and quantized).
- * The tile entries are left untouched for workgroups without a tile in a phase
- * (q4s_chain_set_trace zeroes the buffer once).  Times are the GPU's 100 MHz
+ * The tile entries are left untouched for workgroups without a tile in a phase,
+ * so the caller zeroes the buffer before setting it.  Times are the GPU's 100 MHz
  * constant clock.  trace: q4s_chain_trace_bytes bytes of device memory
  * (8-byte aligned; 0 before upload); NULL turns tracing off.  One thread per
  * workgroup stores the marks.
