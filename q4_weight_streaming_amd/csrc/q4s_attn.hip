@@ -153,16 +153,19 @@ __global__ __launch_bounds__(256) void k_attn_partial(AttnParams a) {
 
 // Workgroup (query head h, 16-dimension block), 1024 threads: thread (split
 // slice k, dimension) takes splits [k*S/64, (k+1)*S/64) in order, all of its
-// loads issued together; the 64 slices are then added in order.
+// loads issued together.  The 64 slices are reduced in a fixed tree: the 4
+// slices of a wave by an xor butterfly over lanes 16 and 32 apart, then the
+// 16 waves in order through LDS.
 constexpr int kCombSlices = 64;
 constexpr int kCombDims = 16;
+constexpr int kCombWaves = kCombSlices * kCombDims / 64;  // 16
 constexpr int kCombBatch = 8;  // splits per slice whose loads are in flight together
 __global__ __launch_bounds__(kCombSlices * kCombDims) void k_attn_combine(AttnParams a) {
-    __shared__ float mred[kCombSlices];
-    __shared__ float num[kCombSlices][kCombDims];
-    __shared__ float den[kCombSlices];
+    __shared__ float mred[kCombWaves];
+    __shared__ float num[kCombWaves][kCombDims];
+    __shared__ float den[kCombWaves];
     const int h = blockIdx.x, d0 = blockIdx.y * kCombDims;
-    const int t = threadIdx.x, dd = t % kCombDims, k = t / kCombDims;
+    const int t = threadIdx.x, dd = t % kCombDims, k = t / kCombDims, wv = t >> 6, lane = t & 63;
     const int64_t stride = attn_split_floats(a.n_q);
     const int64_t om = (int64_t)a.n_q * kHd, ol = om + a.n_q;  // offsets of m and l in a split
     const int s0 = (int)((int64_t)k * a.S / kCombSlices), s1 = (int)((int64_t)(k + 1) * a.S / kCombSlices);
@@ -183,10 +186,13 @@ __global__ __launch_bounds__(kCombSlices * kCombDims) void k_attn_combine(AttnPa
     for (int i = 0; i < kCombBatch; ++i)
         if (s0 + i < s1) mk = fmaxf(mk, mm[i]);
     for (int b = s0 + kCombBatch; b < s1; ++b) mk = fmaxf(mk, a.ws[b * stride + om + h]);
-    if (dd == 0) mred[k] = mk;
+    mk = fmaxf(mk, __shfl_xor(mk, 16, 64));
+    mk = fmaxf(mk, __shfl_xor(mk, 32, 64));
+    if (lane == 0) mred[wv] = mk;
     __syncthreads();
     float M = mred[0];
-    for (int i = 1; i < kCombSlices; ++i) M = fmaxf(M, mred[i]);
+#pragma unroll
+    for (int i = 1; i < kCombWaves; ++i) M = fmaxf(M, mred[i]);
     float nu = 0.0f, de = 0.0f;
     for (int b = s0; b < s1; b += kCombBatch) {
         if (b != s0) load_batch(b);
@@ -198,12 +204,17 @@ __global__ __launch_bounds__(kCombSlices * kCombDims) void k_attn_combine(AttnPa
             nu = fmaf(f, oo[i], nu);
         }
     }
-    num[k][dd] = nu;
-    if (dd == 0) den[k] = de;
+    nu += __shfl_xor(nu, 16, 64);
+    de += __shfl_xor(de, 16, 64);
+    nu += __shfl_xor(nu, 32, 64);
+    de += __shfl_xor(de, 32, 64);
+    if (lane < kCombDims) num[wv][dd] = nu;
+    if (lane == 0) den[wv] = de;
     __syncthreads();
-    if (k == 0) {
+    if (t < kCombDims) {
         float n = num[0][dd], d = den[0];
-        for (int i = 1; i < kCombSlices; ++i) {
+#pragma unroll
+        for (int i = 1; i < kCombWaves; ++i) {
             n += num[i][dd];
             d += den[i];
         }
