@@ -151,14 +151,14 @@ __global__ __launch_bounds__(256) void k_attn_partial(AttnParams a) {
     }
 }
 
-// Workgroup (query head h, 16-dimension block), 1024 threads: thread (split
+// Workgroup (query head h, 4-dimension block), 256 threads: thread (split
 // slice k, dimension) takes splits [k*S/64, (k+1)*S/64) in order, all of its
-// loads issued together.  The 64 slices are reduced in a fixed tree: the 4
-// slices of a wave by an xor butterfly over lanes 16 and 32 apart, then the
-// 16 waves in order through LDS.
+// loads issued together.  The 64 slices are reduced in a fixed tree: the 16
+// slices of a wave by an xor butterfly over lanes 4, 8, 16 and 32 apart, then
+// the 4 waves in order through LDS.
 constexpr int kCombSlices = 64;
-constexpr int kCombDims = 16;
-constexpr int kCombWaves = kCombSlices * kCombDims / 64;  // 16
+constexpr int kCombDims = 4;
+constexpr int kCombWaves = kCombSlices * kCombDims / 64;  // 4
 constexpr int kCombBatch = 8;  // splits per slice whose loads are in flight together
 __global__ __launch_bounds__(kCombSlices * kCombDims) void k_attn_combine(AttnParams a) {
     __shared__ float mred[kCombWaves];
@@ -186,8 +186,8 @@ __global__ __launch_bounds__(kCombSlices * kCombDims) void k_attn_combine(AttnPa
     for (int i = 0; i < kCombBatch; ++i)
         if (s0 + i < s1) mk = fmaxf(mk, mm[i]);
     for (int b = s0 + kCombBatch; b < s1; ++b) mk = fmaxf(mk, a.ws[b * stride + om + h]);
-    mk = fmaxf(mk, __shfl_xor(mk, 16, 64));
-    mk = fmaxf(mk, __shfl_xor(mk, 32, 64));
+#pragma unroll
+    for (int off = kCombDims; off < 64; off <<= 1) mk = fmaxf(mk, __shfl_xor(mk, off, 64));
     if (lane == 0) mred[wv] = mk;
     __syncthreads();
     float M = mred[0];
@@ -204,10 +204,11 @@ __global__ __launch_bounds__(kCombSlices * kCombDims) void k_attn_combine(AttnPa
             nu = fmaf(f, oo[i], nu);
         }
     }
-    nu += __shfl_xor(nu, 16, 64);
-    de += __shfl_xor(de, 16, 64);
-    nu += __shfl_xor(nu, 32, 64);
-    de += __shfl_xor(de, 32, 64);
+#pragma unroll
+    for (int off = kCombDims; off < 64; off <<= 1) {
+        nu += __shfl_xor(nu, off, 64);
+        de += __shfl_xor(de, off, 64);
+    }
     if (lane < kCombDims) num[wv][dd] = nu;
     if (lane == 0) den[wv] = de;
     __syncthreads();

@@ -196,6 +196,19 @@ __global__ __launch_bounds__(kThreads, N == 1 ? 1 : 2) void k_gemv(MatDesc m) {
     run_any<N>(m, blockIdx.x, l);
 }
 
+// 1-row GEMV of a matrix with one K split (at most 8 chunks): one wave per
+// workgroup and row group, the same wave task, so a lone large matrix (an
+// output head: 2374 row groups) spreads evenly over the CUs instead of in
+// tiles of 4 row groups, 2 or 3 per CU.
+__global__ __launch_bounds__(64) void k_gemv_wave(MatDesc m) {
+    float acc[1];
+    const int g = blockIdx.x;
+    ActGlobal act{m};
+    wave_task<1>(m, g, 0, m.C, acc, act);
+    const int64_t row = (int64_t)g * kGroupRows + (threadIdx.x & 63);
+    if (row < m.rows) gwr<float>(m.y)[row] = acc[0];
+}
+
 // The sweep: workgroup i takes tile i = (matrix, group set) of a table sorted
 // by tile size, largest first, so the hardware dispatcher's in-order
 // assignment to free slots is a longest-first list schedule.
@@ -441,6 +454,10 @@ static void gemv_n(const MatDesc& m, int64_t n_gsets, hipStream_t st) {
 
 hipError_t launch_gemv(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st) {
     if (n_gsets == 0 || n == 0) return hipSuccess;
+    if (n == 1 && m.ks == 1) {
+        hipLaunchKernelGGL(k_gemv_wave, dim3((unsigned)m.G), dim3(64), 0, st, m);
+        return hipGetLastError();
+    }
     if (n > kTokTile) {
         const int tt = (n + kTokTile - 1) / kTokTile;
         hipLaunchKernelGGL(k_gemv_tiled, dim3(tiled_grid(tt, n_gsets)), dim3(kThreads), 0, st, m, tt, n_gsets);

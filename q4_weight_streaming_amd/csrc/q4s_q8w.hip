@@ -233,6 +233,18 @@ __global__ __launch_bounds__(kThreads, N == 1 ? 1 : 2) void k_gemv_q8(MatDesc m)
         });
 }
 
+// 1-row GEMV of a matrix with one K split (at most 8 chunks): one wave per
+// workgroup and row group, the same wave task, so a lone large matrix (an
+// output head: 2374 row groups) spreads evenly over the CUs instead of in
+// tiles of 4 row groups, 2 or 3 per CU.
+__global__ __launch_bounds__(64) void k_gemv_q8_wave(MatDesc m) {
+    float acc[1];
+    const int g = blockIdx.x;
+    wave_task_q8<1>(m, g, 0, m.C, acc);
+    const int64_t row = (int64_t)g * kGroupRows + (threadIdx.x & 63);
+    if (row < m.rows) gwr<float>(m.y)[row] = acc[0];
+}
+
 // Test hook: the exact per-block sums, from the same loads and dot.
 template <int N>
 __global__ __launch_bounds__(kThreads) void k_block_sums_q8(MatDesc m, int32_t* __restrict__ s) {
@@ -361,6 +373,10 @@ static void gemv_q8_n(const MatDesc& m, int64_t n_gsets, hipStream_t st) {
 
 hipError_t launch_gemv_q8_0(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st) {
     if (n_gsets == 0 || n == 0) return hipSuccess;
+    if (n == 1 && m.ks == 1) {
+        hipLaunchKernelGGL(k_gemv_q8_wave, dim3((unsigned)m.G), dim3(64), 0, st, m);
+        return hipGetLastError();
+    }
     switch (n) {
         case 1: gemv_q8_n<1>(m, n_gsets, st); break;
         case 2: gemv_q8_n<2>(m, n_gsets, st); break;
