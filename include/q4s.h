@@ -320,7 +320,10 @@ q4s_status q4s_sweep_plan_upload(q4s_plan* plan, void* dev_mem, size_t dev_bytes
  * mega kernel of milestone M15 quantizes the activation inside its one kernel):
  * each wave quantizes the activation blocks of the chunks it streams, x_q8
  * still receives the Q8_0 bytes, and the results are bit-identical to the
- * two-launch form.  Calls on one plan must not overlap in
+ * two-launch form.  When n == 1 and no matrix has more than 8 chunks (a
+ * single K split), the GEMV launch runs one wave per (matrix, row group)
+ * instead of tiles of 4 row groups (same results), which spreads a plan of
+ * few large matrices evenly.  Calls on one plan must not overlap in
  * time (they share the plan's device tables only for reading, but write the
  * same y and x_q8 buffers).
  */

@@ -392,6 +392,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_sweep_fused(const MatDesc* __re
     });
 }
 
+// ---------------------------------------------------------------- 1-row sweeps of single-split matrices
+//
+// When every matrix of a 1-row sweep has one K split (at most 8 chunks), no
+// wave needs another: one wave per workgroup and table entry (matrix, row
+// group), so a sweep of few large matrices (an output head alone: 2374 row
+// groups) spreads evenly over the CUs.  Same wave task, so results are
+// bit-identical to the 4-wave tiles.
+__device__ __forceinline__ void store_row(const MatDesc& m, int g, float v) {
+    const int64_t row = (int64_t)g * kGroupRows + (threadIdx.x & 63);
+    if (row < m.rows) gwr<float>(m.y)[row] = v;
+}
+
+__global__ __launch_bounds__(64) void k_sweep_wave(const MatDesc* __restrict__ mats,
+                                                   const uint32_t* __restrict__ tiles) {
+    const MatDesc m = mats[tiles[2 * (size_t)blockIdx.x]];
+    const int g = (int)tiles[2 * (size_t)blockIdx.x + 1];
+    float acc[1];
+    ActGlobal act{m};
+    wave_task<1>(m, g, 0, m.C, acc, act);
+    store_row(m, g, acc[0]);
+}
+
+__global__ __launch_bounds__(64) void k_sweep_fused_wave(const MatDesc* __restrict__ mats,
+                                                         const uint32_t* __restrict__ tiles) {
+    const MatDesc m = mats[tiles[2 * (size_t)blockIdx.x]];
+    const int g = (int)tiles[2 * (size_t)blockIdx.x + 1];
+    float acc[1];
+    ActQuant act{m, g == 0, {}};
+    wave_task<1>(m, g, 0, m.C, acc, act);
+    store_row(m, g, acc[0]);
+}
+
 // ---------------------------------------------------------------- measurement
 
 template <int L>
@@ -502,6 +534,16 @@ hipError_t launch_sweep(const MatDesc* dev_mats, const uint32_t* dev_tiles, int6
         case 8: sweep_n<8>(dev_mats, dev_tiles, n_tiles, st); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_sweep_wave(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles, bool fused,
+                             hipStream_t st) {
+    if (n_tiles == 0) return hipSuccess;
+    if (fused)
+        hipLaunchKernelGGL(k_sweep_fused_wave, dim3((unsigned)n_tiles), dim3(64), 0, st, dev_mats, dev_tiles);
+    else
+        hipLaunchKernelGGL(k_sweep_wave, dim3((unsigned)n_tiles), dim3(64), 0, st, dev_mats, dev_tiles);
     return hipGetLastError();
 }
 
