@@ -7,6 +7,12 @@ method of the minfer README, milestone M15: one launch over a large buffer,
 several 16-byte loads in flight per thread).  A plain copy is timed as well.
 
   python -m q4_weight_streaming_amd.roofline [--gib 4] [--reps 5]
+  python -m q4_weight_streaming_amd.roofline --sizes 131,868 [--reps 20]
+
+--sizes times reads of the sizes the GEMV streams (MB, e.g. the 1.5B output head
+and the whole 1.5B sweep) the way the benchmark times its steps: launches back to
+back, four rotated buffers (past the Infinity Cache), over a small grid of loads
+in flight and workgroups.
 """
 from __future__ import annotations
 
@@ -22,7 +28,10 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gib", type=float, default=4.0)
     ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--sizes", default="", help="comma-separated MB: back-to-back reads of these sizes")
     args = ap.parse_args()
+    if args.sizes:
+        return by_size([int(v) for v in args.sizes.split(",")], max(args.reps, 10))
 
     import torch
 
@@ -61,6 +70,41 @@ def main() -> int:
     print(f"copy: {copy} GB/s (read + write)", file=sys.stderr)
     best = max(rows, key=lambda r: r["gb_s"])
     print(json.dumps({"buffer_bytes": nbytes, "best_read": best, "copy_gb_s": copy, "sweep": rows}))
+    return 0
+
+
+def by_size(sizes_mb, reps) -> int:
+    import torch
+
+    from q4_weight_streaming_amd import _lib as q
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    out = []
+    for mb in sizes_mb:
+        n = mb * 1000 * 1000 // 16 * 16
+        bufs = [torch.ones(n, dtype=torch.uint8, device=dev) for _ in range(4)]
+        rows = []
+        for lif in (4, 8):
+            for blocks in (2048, 4096, 8192, 16384):
+                for i in range(3):
+                    q.bench_read(bufs[i % 4], lif, blocks, sink)
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for i in range(reps):
+                    q.bench_read(bufs[i % 4], lif, blocks, sink)
+                b.record(stream)
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) * 1e3 / reps
+                rows.append({"loads_in_flight": lif, "workgroups": blocks, "us": round(us, 2),
+                             "gb_s": round(n / us / 1e3, 1)})
+                print(f"{mb} MB L={lif} wg={blocks:6d}: {us:7.1f} us {n / us / 1e3:8.1f} GB/s", file=sys.stderr,
+                      flush=True)
+        best = max(rows, key=lambda r: r["gb_s"])
+        out.append({"mb": mb, "bytes": n, "best": best, "grid": rows})
+        del bufs
+    print(json.dumps({"back_to_back_reads": out}))
     return 0
 
 
