@@ -59,7 +59,8 @@
  *     round-half-away-from-zero(x / d) with the fp32 d as divisor; stored
  *     d_x = binary16(d) (round to nearest even, subnormals kept).  An
  *     all-zero block stores d_x = +0, q = 0.  Inputs must be finite with
- *     |x| < 8e6 (so d_x stays finite).
+ *     |x| < 8e6 (so d_x stays finite); a block whose max|x| is nonzero but
+ *     below 127 * 2^-150 (d rounds to 0) gets unspecified q.
  *   Output y: fp32 [n][rows], row-major.
  *
  * Numerics: per block the kernel forms the exact integer s and the term

@@ -77,21 +77,75 @@ __device__ __forceinline__ int block_dot16(const Unpacked& u, const u32x8& q) {
 // 8 consecutive lanes quantize one block, 4 values each: d = max|x| / 127
 // (correctly rounded fp32 division), q = roundf(x / d) (half away from zero),
 // d_x = binary16(d) rounded to nearest even.  All-zero blocks give d = 0, q = 0.
-// quant8_amax is called by all 8 lanes of a block (it shuffles among them).
+// Inputs are finite.
+//
+// quant8_amax is called by all 8 lanes of a block.  The magnitudes are
+// compared as integers (for non-negative finite floats the bit patterns order
+// as the values do) and move between lanes by DPP: swap neighbours, swap
+// pairs, then the mirror within 8 lanes, which pairs each quad with the other.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kCtrl, 0xF, 0xF, true);
+}
+constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror: lane i <- lane 7-i within 8
 __device__ __forceinline__ float quant8_amax(const f32x4& v) {
-    float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    uint32_t a = 0;
 #pragma unroll
-    for (int off = 1; off < 8; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 8));
-    return a;
+    for (int k = 0; k < 4; ++k) a = max(a, __float_as_uint(v[k]) & 0x7FFFFFFFu);
+    a = max(a, dpp_move<kDppQuadSwap1>(a));
+    a = max(a, dpp_move<kDppQuadSwap2>(a));
+    a = max(a, dpp_move<kDppHalfMirror>(a));
+    return __uint_as_float(a);
 }
 
-// this lane's 4 quantized values (packed) and the block's binary16 d_x
+// d = RN(a / 127) without a division: q = RN(a * RN(1/127)) is within one ulp
+// of a/127, the residual a - 127 q is exact in one fma, and RN(q + r RN(1/127))
+// is then the correctly rounded quotient (Markstein's theorem).  Every step
+// scales exactly by powers of two while the operands stay normal, so checking
+// every a in [1, 2) covers the guarded range; outside it the division is done.
+__device__ __forceinline__ float quant8_scale(float a) {
+    if (!(a >= 0x1p-96f && a <= 0x1p96f)) return a / 127.0f;
+    constexpr float y = 1.0f / 127.0f;
+    const float q = a * y;
+    const float r = fmaf(-q, 127.0f, a);
+    return fmaf(r, y, q);
+}
+
+// this lane's 4 quantized values (packed) and the block's binary16 d_x.
+//
+// roundf(RN(x / d)) is taken from the exact product x * rcp(d).  With rcp
+// within one ulp of 1/d and |x/d| <= 127, the product is within 2^-16 of x/d
+// and RN(x/d) within 2^-18 of it, so where the product lies more than 2^-13
+// from every half-integer all three round to the same integer n.  One fma
+// adds 1.5 * 2^23 to the product and rounds to an integer: the sum is 1.5 *
+// 2^23 + n exactly, its low byte is n as a two's-complement byte, and a second
+// fma gives the product's distance from n.  Lanes with any value within 2^-13
+// of a half-integer, or with d too small or too large for rcp to stay normal,
+// redo their values with the correctly rounded division.
 __device__ __forceinline__ void quant8_codes(const f32x4& v, float a, uint32_t& packed, uint16_t& h) {
-    const float dd = a / 127.0f;
+    const float dd = quant8_scale(a);
     packed = 0;
     if (a != 0.0f) {
+        constexpr float kMagic = 0x1.8p23f;
+        const float rc = __builtin_amdgcn_rcpf(dd);
+        bool fast = dd >= 0x1p-125f && dd <= 0x1p125f;
+        uint32_t s[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) packed |= ((uint32_t)(uint8_t)(int8_t)(int)roundf(v[k] / dd)) << (8 * k);
+        for (int k = 0; k < 4; ++k) {
+            const float m = fmaf(v[k], rc, kMagic);
+            const float dist = fmaf(v[k], rc, -(m - kMagic));    // m - kMagic is exact
+            fast = fast && fabsf(dist) < 0.5f - 0x1p-13f;
+            s[k] = __float_as_uint(m);
+        }
+        packed = __builtin_amdgcn_perm(__builtin_amdgcn_perm(s[3], s[2], 0x0c0c0400u),
+                                       __builtin_amdgcn_perm(s[1], s[0], 0x0c0c0400u), 0x05040100u);
+        if (!fast) {
+            packed = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) packed |= ((uint32_t)(uint8_t)(int8_t)(int)roundf(v[k] / dd)) << (8 * k);
+        }
     }
     h = __half_as_ushort(__float2half_rn(dd));
 }

@@ -70,6 +70,40 @@ def test_quantize_near_ties_and_scales(oracle):
     assert np.array_equal(got, oracle.quantize_q8_0(xs))
 
 
+def test_quantize_extreme_scales(oracle):
+    """Block maxima at and around the ends of the kernel's division-free range
+    (a in [2^-96, 2^96] for the scale, d in [2^-125, 2^125] for the reciprocal),
+    subnormal maxima and values (down to d = 2^-149), and the largest allowed
+    magnitude; each block
+    holds its maximum, near-ties (k + 1/2) d nudged by an ulp, and random values."""
+    rng = np.random.default_rng(23)
+    f32 = np.float32
+    edges = [2.0 ** -97, 2.0 ** -96, 2.0 ** -95, 127 * 2.0 ** -126, 127 * 2.0 ** -125, 127 * 2.0 ** -124,
+             1e-36, 1e-38, 1e-40, 2.0 ** -142, 2.0 ** -140, 2.0 ** 22, 7.9e6]
+    amax = []
+    for e in edges:
+        e = f32(e)
+        amax += [np.nextafter(e, f32(0)), e, np.nextafter(e, f32(np.inf))]
+    amax = np.array([a for a in amax if a > 0], np.float32)
+    reps = 8
+    amax = np.repeat(amax, reps)
+    nblk = amax.size
+    d = (amax / f32(127)).astype(np.float32)
+    k = rng.integers(-126, 126, size=(nblk, 15)).astype(np.float32)
+    ties = ((k + f32(0.5)) * d[:, None]).astype(np.float32)
+    ties = np.where(rng.random(ties.shape) < 0.4, np.nextafter(ties, f32(np.inf)), ties)
+    ties = np.where(rng.random(ties.shape) < 0.4, np.nextafter(ties, f32(-np.inf)), ties)
+    rand = ((rng.random((nblk, 16)) * 2 - 1) * amax[:, None]).astype(np.float32)
+    x = np.clip(np.concatenate([ties, rand], 1), -amax[:, None], amax[:, None])
+    sign = np.where(rng.random((nblk, 1)) < 0.5, f32(-1), f32(1))
+    blocks = np.concatenate([amax[:, None] * sign, x], 1).astype(np.float32)
+    perm = rng.permuted(np.tile(np.arange(32), (nblk, 1)), axis=1)  # maximum anywhere in the block
+    blocks = np.take_along_axis(blocks, perm, 1)
+    xs = blocks.reshape(reps, -1)
+    got = q8_canonical(q.quantize_q8_0(to_dev(xs)), reps, xs.shape[1])
+    assert np.array_equal(got, oracle.quantize_q8_0(xs))
+
+
 def test_quantize_empty_is_noop():
     x = torch.empty((0, 64), dtype=torch.float32, device=dev())
     assert q.quantize_q8_0(x).numel() == 0
