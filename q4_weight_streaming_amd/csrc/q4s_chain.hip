@@ -264,6 +264,7 @@ __device__ __noinline__ void chain_stage(const void* x, const uint64_t* x2, int 
 // scales from LDS.
 template <int kSync>
 struct ActStaged {
+    static constexpr bool kLaneCodes = false;
     const ChainMat& cm;
     int64_t g;
     int c0, c1;

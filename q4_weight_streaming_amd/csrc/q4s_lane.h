@@ -62,6 +62,58 @@ __device__ __forceinline__ int block_dot16(const Unpacked& u, const u32x8& q) {
     return s;
 }
 
+// Codes held one dword per lane: where a wave quantizes a chunk itself, lane l
+// holds code dword l of the chunk (block l/8, values 4(l%8) .. 4(l%8)+3).
+// rows4 copies row j (lanes 16j .. 16j+15) of that register into every row of
+// y[j] with the lane-swap instructions: a 32-lane swap of the register with
+// itself gives [R0 R1 R0 R1] and [R2 R3 R2 R3], a 16-lane swap of each with
+// itself gives [R0 R0 R0 R0], [R1 R1 R1 R1] and so on.  A DPP row_newbcast:n
+// operand of y[j] then hands dword 16j + n to every lane, so block b's 8
+// dwords are y[b/2] at n = 8(b%2) .. 8(b%2)+7.
+__device__ __forceinline__ void rows4(uint32_t x, uint32_t (&y)[4]) {
+    const auto h = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    const auto a = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
+    y[0] = a[0];
+    y[1] = a[1];
+    y[2] = b[0];
+    y[3] = b[1];
+}
+
+// block_dot16 for the four blocks 4h .. 4h+3 of a chunk, their codes taken
+// from ya = rows4 register 2h (blocks 4h, 4h+1) and yb = register 2h+1 (blocks
+// 4h+2, 4h+3) by row_newbcast operands; s[X] is block 4h+X's sum.  The compiler
+// does not fold a DPP move into v_dot4c, so the 32 dots are written out.  A DPP
+// instruction reads all of its VGPR operands two wait states after a VALU
+// write becomes visible, the accumulator included: the four blocks' dots take
+// turns, so each accumulator is read again three instructions after it was
+// written, and the leading s_nop covers the operands the compiler wrote just
+// before.  Integer sums, so the order of the dots does not change them.
+#define Q4S_DOT_BCAST(acc, y, w, n) \
+    "v_dot4c_i32_i8_dpp %" #acc ", %" #y ", %" #w " row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n"
+#define Q4S_DOT_ROUND(wa, wb, wc, wd, n, n8) \
+    Q4S_DOT_BCAST(0, 4, wa, n) Q4S_DOT_BCAST(1, 4, wb, n8) Q4S_DOT_BCAST(2, 5, wc, n) Q4S_DOT_BCAST(3, 5, wd, n8)
+__device__ __forceinline__ void quad_dot16_rows(const Unpacked (&u)[4], uint32_t ya, uint32_t yb, int (&s)[4]) {
+    s[0] = s[1] = s[2] = s[3] = 0;
+    asm("s_nop 1\n"
+        Q4S_DOT_ROUND(6, 14, 22, 30, 0, 8) Q4S_DOT_ROUND(7, 15, 23, 31, 1, 9)
+        Q4S_DOT_ROUND(8, 16, 24, 32, 2, 10) Q4S_DOT_ROUND(9, 17, 25, 33, 3, 11)
+        Q4S_DOT_ROUND(10, 18, 26, 34, 4, 12) Q4S_DOT_ROUND(11, 19, 27, 35, 5, 13)
+        Q4S_DOT_ROUND(12, 20, 28, 36, 6, 14) Q4S_DOT_ROUND(13, 21, 29, 37, 7, 15)
+        : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3])
+        : "v"(ya), "v"(yb),
+          "v"(u[0].lo[0]), "v"(u[0].lo[1]), "v"(u[0].lo[2]), "v"(u[0].lo[3]),
+          "v"(u[0].hi[0]), "v"(u[0].hi[1]), "v"(u[0].hi[2]), "v"(u[0].hi[3]),
+          "v"(u[1].lo[0]), "v"(u[1].lo[1]), "v"(u[1].lo[2]), "v"(u[1].lo[3]),
+          "v"(u[1].hi[0]), "v"(u[1].hi[1]), "v"(u[1].hi[2]), "v"(u[1].hi[3]),
+          "v"(u[2].lo[0]), "v"(u[2].lo[1]), "v"(u[2].lo[2]), "v"(u[2].lo[3]),
+          "v"(u[2].hi[0]), "v"(u[2].hi[1]), "v"(u[2].hi[2]), "v"(u[2].hi[3]),
+          "v"(u[3].lo[0]), "v"(u[3].lo[1]), "v"(u[3].lo[2]), "v"(u[3].lo[3]),
+          "v"(u[3].hi[0]), "v"(u[3].hi[1]), "v"(u[3].hi[2]), "v"(u[3].hi[3]));
+}
+#undef Q4S_DOT_ROUND
+#undef Q4S_DOT_BCAST
+
 // ---------------------------------------------------------------- GEMV core
 
 // Summation order shared by every path.  A wave task streams chunks [c0, c1)
@@ -157,6 +209,7 @@ __device__ __forceinline__ void quant8_codes(const f32x4& v, float a, uint32_t& 
 //
 // ActGlobal: the planar buffer in global memory, through scalar loads.
 struct ActGlobal {
+    static constexpr bool kLaneCodes = false;
     const MatDesc& m;
     struct Prep {};
     __device__ __forceinline__ void load(int, int) {}
@@ -177,6 +230,7 @@ struct ActGlobal {
 // prologue stands between the launch and the weight stream.  With `publish`
 // (the waves of row group 0) the codes are also written to x_q8.
 struct ActQuant {
+    static constexpr bool kLaneCodes = true;   // Prep::packed is the lane's code dword
     const MatDesc& m;
     bool publish;
     f32x4 xs[2];
@@ -224,6 +278,28 @@ template <int N, class Act>
 __device__ __forceinline__ void chunk_fma(const MatDesc& m, int c, const Chunk& ch, float (&pa)[N],
                                           float (&pb)[N], Act& act, int slot) {
     const auto pr = act.prepare(slot, c);
+    if constexpr (Act::kLaneCodes) {
+        static_assert(N == 1, "lane-held codes carry one activation row");
+        uint32_t y[4];
+        rows4(pr.packed, y);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            Unpacked u[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) u[x] = unpack(ch.nib[4 * h + x]);
+            int s16[4];
+            quad_dot16_rows(u, y[2 * h], y[2 * h + 1], s16);
+            float& p = h == 0 ? pa[0] : pb[0];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int b = 4 * h + x;
+                const uint32_t sw = ch.scale[b >> 1];
+                const float dw16 = ((b & 1) ? half_hi(sw) : half_lo(sw)) * 0.0625f;
+                p = fmaf(dw16 * act.d(pr, 0, 0, b), (float)s16[x], p);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int b = 0; b < kChunkBlocks; ++b) {
         // padding blocks of the last chunk have zero nibbles and scale; read a
