@@ -264,7 +264,7 @@ __device__ __noinline__ void chain_stage(const void* x, const uint64_t* x2, int 
 // scales from LDS.
 template <int kSync>
 struct ActStaged {
-    static constexpr bool kLaneCodes = false;
+    static constexpr bool kLaneCodes = true;   // Prep::packed is the lane's code dword
     const ChainMat& cm;
     int64_t g;
     int c0, c1;
@@ -298,12 +298,6 @@ struct ActStaged {
         }
         const u32x2 e = slice[(c - c0) * 64 + (threadIdx.x & 63)];
         return {e[0], e[1]};
-    }
-    __device__ __forceinline__ u32x8 q(const Prep& p, int, int, int b) const {
-        u32x8 r;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) r[k] = __builtin_amdgcn_readlane(p.packed, 8 * b + k);
-        return r;
     }
     __device__ __forceinline__ float d(const Prep& p, int, int, int b) const {
         return __uint_as_float(__builtin_amdgcn_readlane(p.dbits, 8 * b));
@@ -371,12 +365,22 @@ template <int kSync>
 __device__ __forceinline__ void chunk_terms(int c, const Chunk& ch, ActStaged<kSync>& act, Q4S_LDS uint32_t* terms) {
     const int lane = threadIdx.x & 63;
     const auto pr = act.prepare(0, c);
+    uint32_t y[4];
+    rows4(pr.packed, y);
 #pragma unroll
-    for (int b = 0; b < kChunkBlocks; ++b) {
-        const uint32_t sw = ch.scale[b >> 1];
-        const uint32_t dw_bits = (b & 1) ? (sw >> 16) : (sw & 0xffffu);
-        const int s16 = block_dot16(unpack(ch.nib[b]), act.q(pr, 0, 0, b));
-        terms[(c * kChunkBlocks + b) * 64 + lane] = (uint32_t)(uint16_t)(int16_t)(s16 >> 4) | (dw_bits << 16);
+    for (int h = 0; h < 2; ++h) {
+        Unpacked u[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) u[x] = unpack(ch.nib[4 * h + x]);
+        int s16[4];
+        quad_dot16_rows(u, y[2 * h], y[2 * h + 1], s16);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int b = 4 * h + x;
+            const uint32_t sw = ch.scale[b >> 1];
+            const uint32_t dw_bits = (b & 1) ? (sw >> 16) : (sw & 0xffffu);
+            terms[(c * kChunkBlocks + b) * 64 + lane] = (uint32_t)(uint16_t)(int16_t)(s16[x] >> 4) | (dw_bits << 16);
+        }
     }
 }
 

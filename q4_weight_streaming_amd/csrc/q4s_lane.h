@@ -88,14 +88,15 @@ __device__ __forceinline__ void rows4(uint32_t x, uint32_t (&y)[4]) {
 // write becomes visible, the accumulator included: the four blocks' dots take
 // turns, so each accumulator is read again three instructions after it was
 // written, and the leading s_nop covers the operands the compiler wrote just
-// before.  Integer sums, so the order of the dots does not change them.
+// before (five wait states, which also covers a VALU write of EXEC).  Integer
+// sums, so the order of the dots does not change them.
 #define Q4S_DOT_BCAST(acc, y, w, n) \
     "v_dot4c_i32_i8_dpp %" #acc ", %" #y ", %" #w " row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n"
 #define Q4S_DOT_ROUND(wa, wb, wc, wd, n, n8) \
     Q4S_DOT_BCAST(0, 4, wa, n) Q4S_DOT_BCAST(1, 4, wb, n8) Q4S_DOT_BCAST(2, 5, wc, n) Q4S_DOT_BCAST(3, 5, wd, n8)
 __device__ __forceinline__ void quad_dot16_rows(const Unpacked (&u)[4], uint32_t ya, uint32_t yb, int (&s)[4]) {
     s[0] = s[1] = s[2] = s[3] = 0;
-    asm("s_nop 1\n"
+    asm("s_nop 4\n"
         Q4S_DOT_ROUND(6, 14, 22, 30, 0, 8) Q4S_DOT_ROUND(7, 15, 23, 31, 1, 9)
         Q4S_DOT_ROUND(8, 16, 24, 32, 2, 10) Q4S_DOT_ROUND(9, 17, 25, 33, 3, 11)
         Q4S_DOT_ROUND(10, 18, 26, 34, 4, 12) Q4S_DOT_ROUND(11, 19, 27, 35, 5, 13)
@@ -204,8 +205,10 @@ __device__ __forceinline__ void quant8_codes(const f32x4& v, float a, uint32_t& 
 
 // Where the lane-per-row path gets the Q8_0 activation.  load(slot, c) runs
 // when chunk c's weight loads are issued (slot 0 or 1 follows the chunk
-// buffer), prepare(slot, c) when chunk c is consumed; q and d then give block
-// blk (b within the chunk) as scalar operands.
+// buffer), prepare(slot, c) when chunk c is consumed; d gives block blk (b
+// within the chunk) a scalar d_x.  Without kLaneCodes, q gives its codes as
+// scalar operands; with it, Prep::packed holds the lane's code dword of the
+// chunk and the dots take the codes through rows4 and quad_dot16_rows.
 //
 // ActGlobal: the planar buffer in global memory, through scalar loads.
 struct ActGlobal {
@@ -225,7 +228,8 @@ struct ActGlobal {
 // ActQuant (the fused 1-row sweep): the wave quantizes the 256 fp32 values of
 // the chunk it is about to consume itself -- lane l holds values 4(l%8) ..
 // 4(l%8)+3 of block l/8, 8 lanes per Q8_0 block with the standalone
-// quantizer's arithmetic -- and broadcasts codes and scales with v_readlane.
+// quantizer's arithmetic -- and broadcasts the codes by lane swaps and DPP
+// operands (rows4, quad_dot16_rows) and the scales with v_readlane.
 // The activation load travels with the chunk's weight loads, so no barrier or
 // prologue stands between the launch and the weight stream.  With `publish`
 // (the waves of row group 0) the codes are also written to x_q8.
@@ -262,12 +266,6 @@ struct ActQuant {
         }
         return {packed, __float_as_uint(__half2float(__ushort_as_half(h)))};
     }
-    __device__ __forceinline__ u32x8 q(const Prep& p, int, int, int b) const {
-        u32x8 r;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) r[k] = __builtin_amdgcn_readlane(p.packed, 8 * b + k);
-        return r;
-    }
     __device__ __forceinline__ float d(const Prep& p, int, int, int b) const {
         return __uint_as_float(__builtin_amdgcn_readlane(p.dbits, 8 * b));
     }
@@ -298,23 +296,23 @@ __device__ __forceinline__ void chunk_fma(const MatDesc& m, int c, const Chunk& 
                 p = fmaf(dw16 * act.d(pr, 0, 0, b), (float)s16[x], p);
             }
         }
-        return;
-    }
+    } else {
 #pragma unroll
-    for (int b = 0; b < kChunkBlocks; ++b) {
-        // padding blocks of the last chunk have zero nibbles and scale; read a
-        // valid activation block for them
-        const int blk = min(c * kChunkBlocks + b, m.nb - 1);
-        const uint32_t sw = ch.scale[b >> 1];
-        const float dw16 = ((b & 1) ? half_hi(sw) : half_lo(sw)) * 0.0625f;
-        const Unpacked u = unpack(ch.nib[b]);
+        for (int b = 0; b < kChunkBlocks; ++b) {
+            // padding blocks of the last chunk have zero nibbles and scale; read a
+            // valid activation block for them
+            const int blk = min(c * kChunkBlocks + b, m.nb - 1);
+            const uint32_t sw = ch.scale[b >> 1];
+            const float dw16 = ((b & 1) ? half_hi(sw) : half_lo(sw)) * 0.0625f;
+            const Unpacked u = unpack(ch.nib[b]);
 #pragma unroll
-        for (int t = 0; t < N; ++t) {
-            const u32x8 q = act.q(pr, t, blk, b);
-            const int s16 = block_dot16(u, q);
-            const float dx = act.d(pr, t, blk, b);
-            float& p = (b < kChunkBlocks / 2) ? pa[t] : pb[t];
-            p = fmaf(dw16 * dx, (float)s16, p);
+            for (int t = 0; t < N; ++t) {
+                const u32x8 q = act.q(pr, t, blk, b);
+                const int s16 = block_dot16(u, q);
+                const float dx = act.d(pr, t, blk, b);
+                float& p = (b < kChunkBlocks / 2) ? pa[t] : pb[t];
+                p = fmaf(dw16 * dx, (float)s16, p);
+            }
         }
     }
 }
