@@ -322,9 +322,10 @@ q4s_status q4s_sweep_plan_upload(q4s_plan* plan, void* dev_mem, size_t dev_bytes
  * each wave quantizes the activation blocks of the chunks it streams, x_q8
  * still receives the Q8_0 bytes, and the results are bit-identical to the
  * two-launch form.  When n == 1 and no matrix has more than 8 chunks (a
- * single K split), the GEMV launch runs one wave per (matrix, row group)
- * instead of tiles of 4 row groups (same results), which spreads a plan of
- * few large matrices evenly.  Calls on one plan must not overlap in
+ * single K split), the GEMV launch runs one 8-wave workgroup per (matrix, row
+ * group), the row's chunks spread over its waves, instead of tiles of 4 row
+ * groups (same results), which keeps every weight load of a plan of few
+ * large matrices in flight early.  Calls on one plan must not overlap in
  * time (they share the plan's device tables only for reading, but write the
  * same y and x_q8 buffers).
  */

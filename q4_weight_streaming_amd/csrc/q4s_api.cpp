@@ -331,7 +331,7 @@ struct q4s_plan {
     std::vector<uint32_t> qtiles;    // (activation, first block) pairs, kQuantTileBlocks blocks each
     int64_t quant_blocks = 0;
     bool fused = false;              // n == 1, every matrix quantized by the GEMV launch itself
-    bool wave_tiles = false;         // n == 1, one K split everywhere: one wave per (matrix, row group)
+    bool split_tiles = false;        // n == 1, one K split everywhere: one workgroup per (matrix, row group)
     q4s_plan_info info{};
     // device image: [MatDesc x n_mats][QuantDesc x n_quant][tiles][quantize tiles], 16-byte aligned parts
     size_t off_mats = 0, off_quant = 0, off_tiles = 0, off_qtiles = 0, dev_bytes = 0;
@@ -390,10 +390,10 @@ q4s_status q4s_sweep_plan_create(const q4s_mat* mats, int n_mats, int n, size_t*
     struct Tile { uint32_t mat, gset; int64_t bytes; };
     std::vector<Tile> tiles;
     // one row, no matrix with more than 8 chunks (one K split): no wave needs another, so
-    // the GEMV launch runs one wave per (matrix, row group) instead of 4-group tiles
-    p->wave_tiles = n == 1;
-    for (int i = 0; i < n_mats && p->wave_tiles; ++i)
-        if (mats[i].rows > 0 && choose_ksplit(chunks_of(mats[i].cols)) != 1) p->wave_tiles = false;
+    // the GEMV launch runs one workgroup per (matrix, row group), its chunks over 8 waves, instead of 4-group tiles
+    p->split_tiles = n == 1;
+    for (int i = 0; i < n_mats && p->split_tiles; ++i)
+        if (mats[i].rows > 0 && choose_ksplit(chunks_of(mats[i].cols)) != 1) p->split_tiles = false;
     for (int i = 0; i < n_mats; ++i) {
         const q4s_mat& a = mats[i];
         MatDesc m = make_desc(a.w_packed, a.x_q8, a.y, a.rows, a.cols, n);
@@ -424,7 +424,7 @@ q4s_status q4s_sweep_plan_create(const q4s_mat* mats, int n_mats, int n, size_t*
         p->info.packed_bytes += (int64_t)packed_bytes(a.rows, a.cols);
         p->info.act_bytes += (int64_t)n * a.cols / 32 * 34;
         p->info.out_bytes += (int64_t)n * a.rows * 4;
-        if (p->wave_tiles) {
+        if (p->split_tiles) {
             for (int64_t gr = 0; gr < m.G; ++gr) tiles.push_back({(uint32_t)i, (uint32_t)gr, m.C * kChunkBytes});
             continue;
         }
@@ -481,8 +481,8 @@ q4s_status q4s_sweep_run(const q4s_plan* p, void* stream) {
     if (!p) return fail(Q4S_ERR_NULL, "plan is NULL");
     if (!p->dev) return fail(Q4S_ERR_PLAN, "plan was not uploaded");
     hipStream_t st = (hipStream_t)stream;
-    if (p->wave_tiles && p->fused)
-        return hip_status(launch_sweep_wave((const MatDesc*)(p->dev + p->off_mats),
+    if (p->split_tiles && p->fused)
+        return hip_status(launch_sweep_split((const MatDesc*)(p->dev + p->off_mats),
                                             (const uint32_t*)(p->dev + p->off_tiles), (int64_t)p->tiles.size() / 2,
                                             true, st),
                           "sweep launch");
@@ -497,8 +497,8 @@ q4s_status q4s_sweep_run(const q4s_plan* p, void* stream) {
                                              (int64_t)p->qtiles.size() / 2, st);
         if (e != hipSuccess) return hip_status(e, "sweep quantize launch");
     }
-    if (p->wave_tiles)
-        return hip_status(launch_sweep_wave((const MatDesc*)(p->dev + p->off_mats),
+    if (p->split_tiles)
+        return hip_status(launch_sweep_split((const MatDesc*)(p->dev + p->off_mats),
                                             (const uint32_t*)(p->dev + p->off_tiles), (int64_t)p->tiles.size() / 2,
                                             false, st),
                           "sweep launch");

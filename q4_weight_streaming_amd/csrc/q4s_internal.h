@@ -84,8 +84,8 @@ hipError_t launch_sweep(const MatDesc* dev_mats, const uint32_t* dev_tiles, int6
                         int n, hipStream_t st);
 hipError_t launch_block_sums(const MatDesc& m, int n, int32_t* s, hipStream_t st);
 // The 1-row sweep with the activation quantized by the GEMV waves themselves.
-// 1-row sweeps whose matrices all have one K split: one wave per (matrix, row group) entry.
-hipError_t launch_sweep_wave(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles, bool fused,
+// 1-row sweeps whose matrices all have one K split: one 8-wave workgroup per (matrix, row group) entry.
+hipError_t launch_sweep_split(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles, bool fused,
                              hipStream_t st);
 hipError_t launch_sweep_fused(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles,
                               hipStream_t st);

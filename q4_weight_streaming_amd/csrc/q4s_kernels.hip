@@ -196,19 +196,6 @@ __global__ __launch_bounds__(kThreads, N == 1 ? 1 : 2) void k_gemv(MatDesc m) {
     run_any<N>(m, blockIdx.x, l);
 }
 
-// 1-row GEMV of a matrix with one K split (at most 8 chunks): one wave per
-// workgroup and row group, the same wave task, so a lone large matrix (an
-// output head: 2374 row groups) spreads evenly over the CUs instead of in
-// tiles of 4 row groups, 2 or 3 per CU.
-__global__ __launch_bounds__(64) void k_gemv_wave(MatDesc m) {
-    float acc[1];
-    const int g = blockIdx.x;
-    ActGlobal act{m};
-    wave_task<1>(m, g, 0, m.C, acc, act);
-    const int64_t row = (int64_t)g * kGroupRows + (threadIdx.x & 63);
-    if (row < m.rows) gwr<float>(m.y)[row] = acc[0];
-}
-
 // The sweep: workgroup i takes tile i = (matrix, group set) of a table sorted
 // by tile size, largest first, so the hardware dispatcher's in-order
 // assignment to free slots is a longest-first list schedule.
@@ -392,36 +379,121 @@ __global__ __launch_bounds__(kThreads, 1) void k_sweep_fused(const MatDesc* __re
     });
 }
 
-// ---------------------------------------------------------------- 1-row sweeps of single-split matrices
+// ---------------------------------------------------------------- 1-row split tiles
 //
-// When every matrix of a 1-row sweep has one K split (at most 8 chunks), no
-// wave needs another: one wave per workgroup and table entry (matrix, row
-// group), so a sweep of few large matrices (an output head alone: 2374 row
-// groups) spreads evenly over the CUs.  Same wave task, so results are
-// bit-identical to the 4-wave tiles.
-__device__ __forceinline__ void store_row(const MatDesc& m, int g, float v) {
-    const int64_t row = (int64_t)g * kGroupRows + (threadIdx.x & 63);
-    if (row < m.rows) gwr<float>(m.y)[row] = v;
+// A 1-row GEMV or sweep whose matrices all have one K split (C <= 8 chunks):
+// each row group (a table entry: matrix, row group) gets its own workgroup of
+// kSplitWaves waves.  Wave w takes chunks [ceil(wC/W), ceil((w+1)C/W)) -- one
+// chunk at most with 8 waves -- issues its loads at once, and leaves each
+// block's exact integer sum (int16: |s| <= 32512) and binary16 d_w in LDS,
+// plus the chunk's d_x when it quantized the activation itself.  Waves 0 and 1
+// then run chains A (blocks 0-3) and B (blocks 4-7) over all chunks in order
+// with wave_task's fmaf, and wave 0 adds 0 + (A + B): bit-identical to a wave
+// task over the whole row, with every weight load of the row group in flight
+// from the start.  (A lone output head, 2374 row groups of 6 chunks, is too
+// small for waves that stream their chunks two at a time: one wave per row
+// group took 22.7 us as a plain GEMV and 23.1 us quantizing on the fly, 8 waves
+// take 22.6 and 22.2 us; 2 and 4 waves were slower.)
+constexpr int kSplitWaves = 8;
+struct SplitLds {
+    uint32_t terms[kChunkBlocks * kChunkBlocks * 64];  // [chunk][block][lane], C <= 8
+    uint32_t dx[kChunkBlocks * kChunkBlocks];          // fp32 bits of d_x per block
+    float chain_b[64];
+};
+
+template <bool kFused, int kW>
+__device__ __forceinline__ void split_group(const MatDesc& m, int g, SplitLds& l) {
+    static_assert(kW >= 2 && kW <= 8, "2 to 8 waves per row group");
+    constexpr int kPer = (kChunkBlocks + kW - 1) / kW;  // chunks per wave at most (C <= 8)
+    const int wave = wave_uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int C = m.C;
+    const int i0 = (wave * C + kW - 1) / kW, i1 = ((wave + 1) * C + kW - 1) / kW;
+    if (i0 < i1) {
+        const uint8_t* wp = m.w + ((size_t)g * C + i0) * kChunkBytes + lane * kBlockNibBytes;
+        Chunk ch[kPer];
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            if (i0 + k < i1) load_chunk(ch[k], wp + k * kChunkBytes);
+        ActQuantN<kPer> aq{m, g == 0, {}};
+        if constexpr (kFused) {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+                if (i0 + k < i1) aq.load(k, i0 + k);
+        }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int c = i0 + k;
+            if (c >= i1) break;
+            int s16[kChunkBlocks];
+            if constexpr (kFused) {
+                const auto pr = aq.prepare(k, c);
+                uint32_t y[4];
+                rows4(pr.packed, y);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    Unpacked u[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) u[x] = unpack(ch[k].nib[4 * h + x]);
+                    int sh[4];
+                    quad_dot16_rows(u, y[2 * h], y[2 * h + 1], sh);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) s16[4 * h + x] = sh[x];
+                }
+                if ((lane & 7) == 0) l.dx[c * kChunkBlocks + (lane >> 3)] = pr.dbits;
+            } else {
+#pragma unroll
+                for (int b = 0; b < kChunkBlocks; ++b) {
+                    // padding blocks of the last chunk have zero nibbles; read a valid block
+                    const int blk = min(c * kChunkBlocks + b, m.nb - 1);
+                    s16[b] = block_dot16(unpack(ch[k].nib[b]), act_q(m.xq, (int64_t)blk * 32));
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < kChunkBlocks; ++b) {
+                const uint32_t sw = ch[k].scale[b >> 1];
+                const uint32_t dw_bits = (b & 1) ? (sw >> 16) : (sw & 0xffffu);
+                l.terms[(c * kChunkBlocks + b) * 64 + lane] = (uint32_t)(uint16_t)(int16_t)(s16[b] >> 4) | (dw_bits << 16);
+            }
+        }
+    }
+    __syncthreads();
+    float p = 0.0f;
+    if (wave < 2) {
+        for (int c = 0; c < C; ++c) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int b = 4 * wave + x;
+                const uint32_t t = l.terms[(c * kChunkBlocks + b) * 64 + lane];
+                const float dw16 = half_hi(t) * 0.0625f;
+                const float dx = kFused ? __uint_as_float(l.dx[c * kChunkBlocks + b])
+                                        : act_d(m.xd, min(c * kChunkBlocks + b, m.nb - 1));
+                p = fmaf(dw16 * dx, (float)((int)(int16_t)(t & 0xffffu) * 16), p);
+            }
+        }
+        if (wave == 1) l.chain_b[lane] = p;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        float acc = 0.0f;
+        acc += p + l.chain_b[lane];
+        const int64_t row = (int64_t)g * kGroupRows + lane;
+        if (row < m.rows) gwr<float>(m.y)[row] = acc;
+    }
 }
 
-__global__ __launch_bounds__(64) void k_sweep_wave(const MatDesc* __restrict__ mats,
-                                                   const uint32_t* __restrict__ tiles) {
+template <bool kFused, int kW>
+__global__ __launch_bounds__(64 * kW) void k_sweep_split(const MatDesc* __restrict__ mats,
+                                                          const uint32_t* __restrict__ tiles) {
+    __shared__ SplitLds l;
     const MatDesc m = mats[tiles[2 * (size_t)blockIdx.x]];
-    const int g = (int)tiles[2 * (size_t)blockIdx.x + 1];
-    float acc[1];
-    ActGlobal act{m};
-    wave_task<1>(m, g, 0, m.C, acc, act);
-    store_row(m, g, acc[0]);
+    split_group<kFused, kW>(m, (int)tiles[2 * (size_t)blockIdx.x + 1], l);
 }
 
-__global__ __launch_bounds__(64) void k_sweep_fused_wave(const MatDesc* __restrict__ mats,
-                                                         const uint32_t* __restrict__ tiles) {
-    const MatDesc m = mats[tiles[2 * (size_t)blockIdx.x]];
-    const int g = (int)tiles[2 * (size_t)blockIdx.x + 1];
-    float acc[1];
-    ActQuant act{m, g == 0, {}};
-    wave_task<1>(m, g, 0, m.C, acc, act);
-    store_row(m, g, acc[0]);
+template <int kW>
+__global__ __launch_bounds__(64 * kW) void k_gemv_split(MatDesc m) {
+    __shared__ SplitLds l;
+    split_group<false, kW>(m, blockIdx.x, l);
 }
 
 // ---------------------------------------------------------------- measurement
@@ -487,7 +559,7 @@ static void gemv_n(const MatDesc& m, int64_t n_gsets, hipStream_t st) {
 hipError_t launch_gemv(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st) {
     if (n_gsets == 0 || n == 0) return hipSuccess;
     if (n == 1 && m.ks == 1) {
-        hipLaunchKernelGGL(k_gemv_wave, dim3((unsigned)m.G), dim3(64), 0, st, m);
+        hipLaunchKernelGGL(k_gemv_split<kSplitWaves>, dim3((unsigned)m.G), dim3(64 * kSplitWaves), 0, st, m);
         return hipGetLastError();
     }
     if (n > kTokTile) {
@@ -537,13 +609,13 @@ hipError_t launch_sweep(const MatDesc* dev_mats, const uint32_t* dev_tiles, int6
     return hipGetLastError();
 }
 
-hipError_t launch_sweep_wave(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles, bool fused,
+hipError_t launch_sweep_split(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles, bool fused,
                              hipStream_t st) {
     if (n_tiles == 0) return hipSuccess;
     if (fused)
-        hipLaunchKernelGGL(k_sweep_fused_wave, dim3((unsigned)n_tiles), dim3(64), 0, st, dev_mats, dev_tiles);
+        hipLaunchKernelGGL((k_sweep_split<true, kSplitWaves>), dim3((unsigned)n_tiles), dim3(64 * kSplitWaves), 0, st, dev_mats, dev_tiles);
     else
-        hipLaunchKernelGGL(k_sweep_wave, dim3((unsigned)n_tiles), dim3(64), 0, st, dev_mats, dev_tiles);
+        hipLaunchKernelGGL((k_sweep_split<false, kSplitWaves>), dim3((unsigned)n_tiles), dim3(64 * kSplitWaves), 0, st, dev_mats, dev_tiles);
     return hipGetLastError();
 }
 

@@ -233,11 +233,12 @@ struct ActGlobal {
 // The activation load travels with the chunk's weight loads, so no barrier or
 // prologue stands between the launch and the weight stream.  With `publish`
 // (the waves of row group 0) the codes are also written to x_q8.
-struct ActQuant {
+template <int kSlots>
+struct ActQuantN {
     static constexpr bool kLaneCodes = true;   // Prep::packed is the lane's code dword
     const MatDesc& m;
     bool publish;
-    f32x4 xs[2];
+    f32x4 xs[kSlots];
     struct Prep {
         uint32_t packed;  // this lane's 4 codes
         uint32_t dbits;   // fp32 bits of its block's binary16 d_x
@@ -270,6 +271,7 @@ struct ActQuant {
         return __uint_as_float(__builtin_amdgcn_readlane(p.dbits, 8 * b));
     }
 };
+using ActQuant = ActQuantN<2>;
 
 // Adds chunk `c` (held in ch) of the lane's row into the chains pa / pb.
 template <int N, class Act>

@@ -28,3 +28,42 @@ def test_gemv_equals_fixed_order_oracle(oracle, rows, cols, n):
     got = y.cpu().numpy()
     bad = np.argwhere(got != ref)
     assert bad.size == 0, f"{len(bad)} of {got.size} differ, first {bad[0]}: {got[tuple(bad[0])]!r} vs {ref[tuple(bad[0])]!r}"
+
+
+SINGLE_SPLIT = [(257, 1536), (64, 32), (130, 96), (70, 2048), (1, 800), (200, 288), (65, 640), (3, 1824)]
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_single_split_sweep_equals_fixed_order_oracle(oracle, fused):
+    """A 1-row sweep whose matrices all have one K split (at most 8 chunks) runs
+    one 4-wave workgroup per row group, the chunks spread over the waves and the
+    fp32 chains taken from exact block sums in LDS: chunk counts 1..8 (waves
+    without a chunk), padding blocks, ragged row groups; with the activation
+    quantized inside the launch or given as Q8_0."""
+    require_gpu()
+    mats, hw, hx = [], [], []
+    for i, (rows, cols) in enumerate(SINGLE_SPLIT):
+        w = synth.q4_0_weights(rows, cols, synth.generator(61, i, 0, 0))
+        x = synth.activation(1, cols, synth.generator(61, i, 0, 1))
+        m = {"w_packed": packed_weights(w, rows, cols),
+             "x_q8": torch.empty(q.q8_bytes(1, cols), dtype=torch.uint8, device=dev()),
+             "y": torch.full((1, rows), float("nan"), dtype=torch.float32, device=dev()),
+             "rows": rows, "cols": cols}
+        if fused:
+            m["x"] = to_dev(x)
+        else:
+            m["x_q8"] = q.quantize_q8_0(to_dev(x))
+        mats.append(m)
+        hw.append(w)
+        hx.append(x)
+    sw = q.Sweep(mats, 1)
+    assert sw.info()["fused_quantize"] == int(fused)
+    sw.run()
+    torch.cuda.synchronize()
+    for (rows, cols), m, w, x in zip(SINGLE_SPLIT, mats, hw, hx):
+        xq8 = oracle.quantize_q8_0(x)
+        assert np.array_equal(q8_canonical(m["x_q8"], 1, cols), xq8)
+        ref = oracle.gemv_f32(w, xq8, rows, cols, 1)
+        got = m["y"].cpu().numpy()
+        bad = np.argwhere(got.view(np.uint32) != ref.view(np.uint32))
+        assert bad.size == 0, f"{rows}x{cols}: {len(bad)} of {got.size} differ, first {bad[0]}"
