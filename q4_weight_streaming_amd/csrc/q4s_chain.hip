@@ -101,41 +101,52 @@ constexpr int kChainBatch = 6;       // chunks per prologue load batch (a 1536-w
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define Q4S_LDS __attribute__((address_space(3)))
 
-// Lane's words of chunks [b0, b0 + cnt) (cnt <= kChainBatch) of a tagged
-// activation, element 256c + 4 lane + k clamped to the vector; with tagged
-// phases every word is re-read until all carry this step's tag.
-template <int kSync>
-__device__ __forceinline__ void chain_batch(const uint64_t* x, int n, int b0, int cnt, uint32_t gen, uint32_t* err,
-                                            uint64_t (&w)[kChainBatch][4]) {
+// Lane's words of chunks [b0, b0 + cnt) (cnt <= kB) of a tagged activation x,
+// and of x2 when given (both in one round of loads), element 256c + 4 lane + k
+// clamped to the vector; with tagged phases every word is re-read until all
+// carry this step's tag.  With `light`, a single word per lane is polled first
+// (the lane's last word of the batch: one load per lane and round instead of
+// the whole batch, so waiting waves do not crowd the producers' memory
+// channels); a stage's later batches skip it, since their words were most
+// likely written by the time its first batch was.
+template <int kSync, int kB>
+__device__ __forceinline__ void chain_batch(const uint64_t* x, const uint64_t* x2, int n, int b0, int cnt,
+                                            uint32_t gen, uint32_t* err, bool light, uint64_t (&w)[kB][4],
+                                            uint64_t (&w2)[kB][4]) {
     const int lane = threadIdx.x & 63;
     auto load_all = [&]() {
 #pragma unroll
-        for (int cc = 0; cc < kChainBatch; ++cc)
+        for (int cc = 0; cc < kB; ++cc)
             if (cc < cnt) {
                 const int i = min((b0 + cc) * 256 + 4 * lane, n - 4);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) w[cc][k] = chain_ld<kSync>(x + i + k);
+                if (x2) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) w2[cc][k] = chain_ld<kSync>(x2 + i + k);
+                }
             }
     };
     auto all_tagged = [&]() {
         bool ok = true;
 #pragma unroll
-        for (int cc = 0; cc < kChainBatch; ++cc)
+        for (int cc = 0; cc < kB; ++cc)
             if (cc < cnt) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) ok = ok && (uint32_t)(w[cc][k] >> 32) == gen;
+                for (int k = 0; k < 4; ++k) {
+                    ok = ok && (uint32_t)(w[cc][k] >> 32) == gen;
+                    if (x2) ok = ok && (uint32_t)(w2[cc][k] >> 32) == gen;
+                }
             }
         return ok;
     };
     if constexpr (kSync == kChainTagged) {
         const int64_t limit = chain_spin_limit(err);
         int64_t spins = 0;
-        // light poll first: the lane's last word of the batch (one load per lane and
-        // round instead of the whole batch, so waiting waves do not crowd the
-        // producers' memory channels); then the whole batch, re-read until all tagged
-        {
+        if (light) {
+            const uint64_t* last = x2 ? x2 : x;
             const int i = min((b0 + cnt - 1) * 256 + 4 * lane, n - 4) + 3;
-            while ((uint32_t)(chain_ld<kSync>(x + i) >> 32) != gen) {
+            while ((uint32_t)(chain_ld<kSync>(last + i) >> 32) != gen) {
                 if (++spins > limit || ((spins & 1023) == 0 && chain_failed(err))) break;
                 __builtin_amdgcn_s_sleep(2);
             }
@@ -164,35 +175,30 @@ struct ChainSrc {
     int x_plain, n;
 };
 
-template <int kSync>
+template <int kSync, int kB>
 __device__ __forceinline__ void chain_values(const ChainSrc& cm, int b0, int cnt, uint32_t gen, uint32_t* err,
-                                             float (&v)[kChainBatch][4]) {
+                                             bool light, float (&v)[kB][4]) {
     const int lane = threadIdx.x & 63;
     const int n = cm.n;
     if (cm.x_plain) {
 #pragma unroll
-        for (int cc = 0; cc < kChainBatch; ++cc)
+        for (int cc = 0; cc < kB; ++cc)
             if (cc < cnt) {
                 const f32x4 f = *gp<f32x4>((const float*)cm.x + min((b0 + cc) * 256 + 4 * lane, n - 4));
 #pragma unroll
                 for (int k = 0; k < 4; ++k) v[cc][k] = f[k];
             }
-    } else {
-        uint64_t w[kChainBatch][4];
-        chain_batch<kSync>((const uint64_t*)cm.x, n, b0, cnt, gen, err, w);
-#pragma unroll
-        for (int cc = 0; cc < kChainBatch; ++cc)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) v[cc][k] = __uint_as_float((uint32_t)w[cc][k]);
+        return;
     }
-    if (cm.x2) {
-        uint64_t w[kChainBatch][4];
-        chain_batch<kSync>(cm.x2, n, b0, cnt, gen, err, w);
+    uint64_t w[kB][4], w2[kB][4];
+    chain_batch<kSync, kB>((const uint64_t*)cm.x, cm.x2, n, b0, cnt, gen, err, light, w, w2);
 #pragma unroll
-        for (int cc = 0; cc < kChainBatch; ++cc)
+    for (int cc = 0; cc < kB; ++cc)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) v[cc][k] = v[cc][k] * __uint_as_float((uint32_t)w[cc][k]);
-    }
+        for (int k = 0; k < 4; ++k) {
+            v[cc][k] = __uint_as_float((uint32_t)w[cc][k]);
+            if (cm.x2) v[cc][k] = v[cc][k] * __uint_as_float((uint32_t)w2[cc][k]);
+        }
 }
 
 // Quantizes chunk c (the lane's 4 values) into the wave's LDS slice entry.
@@ -220,13 +226,26 @@ __device__ __noinline__ void chain_stage(const void* x, const uint64_t* x2, int 
     const ChainSrc cm{x, x2, x_plain, n};
     const int nb = n / 32;
     const int nc = (nb + kChunkBlocks - 1) / kChunkBlocks;
+    if (x2) {  // an elementwise product (no norm): both factors in batches of half the size
+        constexpr int kB = kChainBatch / 2;
+        float v[kB][4];
+        for (int b0 = c0; b0 < c1; b0 += kB) {
+            const int cnt = min(kB, c1 - b0);
+            chain_values<kSync, kB>(cm, b0, cnt, gen, err, b0 == c0, v);
+#pragma unroll
+            for (int cc = 0; cc < kB; ++cc)
+                if (cc < cnt) chain_quant((f32x4){v[cc][0], v[cc][1], v[cc][2], v[cc][3]}, b0 + cc, nb,
+                                          slice + (b0 + cc - c0) * 64);
+        }
+        return;
+    }
     float v[kChainBatch][4];
     float s = 1.0f;
     if (norm) {
         float p = 0.0f;
         for (int b0 = 0; b0 < nc; b0 += kChainBatch) {
             const int cnt = min(kChainBatch, nc - b0);
-            chain_values<kSync>(cm, b0, cnt, gen, err, v);
+            chain_values<kSync, kChainBatch>(cm, b0, cnt, gen, err, b0 == 0, v);
 #pragma unroll
             for (int cc = 0; cc < kChainBatch; ++cc)
 #pragma unroll
@@ -247,7 +266,8 @@ __device__ __noinline__ void chain_stage(const void* x, const uint64_t* x2, int 
     }
     for (int b0 = c0; b0 < c1; b0 += kChainBatch) {
         const int cnt = min(kChainBatch, c1 - b0);
-        chain_values<kSync>(cm, b0, cnt, gen, err, v);
+        // after a norm pass every word has been seen tagged: no light poll
+        chain_values<kSync, kChainBatch>(cm, b0, cnt, gen, err, !norm && b0 == c0, v);
 #pragma unroll
         for (int cc = 0; cc < kChainBatch; ++cc)
             if (cc < cnt) {
