@@ -531,8 +531,12 @@ struct q4s_chain {
     std::vector<uint32_t> tiles;      // (matrix, tile word), phase by phase, largest first within a phase
     std::vector<uint32_t> phase_end;  // cumulative tile count per phase
     q4s_chain_info info{};
-    // device image: [ChainMat x n][tiles][phase_end][sync words], 16-byte aligned parts
-    size_t off_tiles = 0, off_phase = 0, off_sync = 0, dev_bytes = 0;
+    // per matrix: byte offset of its tagged Q8_0 product words (paired gate/up: written; down: read)
+    // within the Q8_0 area, or -1
+    std::vector<int64_t> q8_out, q8_in;
+    size_t q8_bytes = 0;
+    // device image: [ChainMat x n][tiles][phase_end][sync words][Q8_0 words], 16-byte aligned parts
+    size_t off_tiles = 0, off_phase = 0, off_sync = 0, off_q8 = 0, dev_bytes = 0;
     std::vector<uint8_t> image;
     uint8_t* dev = nullptr;
     uint32_t gen = 0;
@@ -552,25 +556,29 @@ static void chain_layout(q4s_chain* p, int wg) {
     p->tiles.clear();
     p->phase_end.clear();
     int64_t max_tiles = 0;
+    // a paired matrix (see ChainMat) has twice its row groups, and its tiles hold an even number
+    auto groups_of_mat = [&](uint32_t i) { return p->mats[i].m.G * (p->mats[i].w2 ? 2 : 1); };
     for (const std::vector<uint32_t>& members : p->phases) {
         int64_t groups = 0;
-        bool splittable = true, narrow = true;
+        bool splittable = true, narrow = true, paired = false;
         for (uint32_t i : members) {
-            groups += p->mats[i].m.G;
+            groups += groups_of_mat(i);
             splittable = splittable && p->mats[i].m.ks <= 2;  // <= 16 chunks
             narrow = narrow && p->mats[i].m.ks == 1;          // <= 8 chunks
+            paired = paired || p->mats[i].w2 != nullptr;      // only with ks <= 2
         }
         max_tiles += groups;
-        const uint32_t mode = !splittable                          ? 0u
-                              : groups <= wg                       ? kChainSplit4
-                              : narrow && (groups + 1) / 2 <= wg   ? kChainSplit2
-                                                                   : 0u;
+        const uint32_t mode = !splittable                               ? 0u
+                              : groups <= wg && !paired                 ? kChainSplit4
+                              : narrow && (groups + 1) / 2 <= wg        ? kChainSplit2
+                                                                        : 0u;
         std::vector<Tile> phase;
         for (uint32_t i : members) {
             const MatDesc& m = p->mats[i].m;
+            const int64_t G = groups_of_mat(i);
             const int gpt = mode == kChainSplit4 ? 1 : (mode == kChainSplit2 ? 2 : kWaves / m.ks);
-            for (int64_t t = 0; t * gpt < m.G; ++t) {
-                const int64_t n = std::min<int64_t>(gpt, m.G - t * gpt);
+            for (int64_t t = 0; t * gpt < G; ++t) {
+                const int64_t n = std::min<int64_t>(gpt, G - t * gpt);
                 phase.push_back({i, (uint32_t)t | mode, n * m.C * kChunkBytes});
             }
         }
@@ -585,7 +593,8 @@ static void chain_layout(q4s_chain* p, int wg) {
     p->off_tiles = up16(p->mats.size() * sizeof(ChainMat));
     p->off_phase = p->off_tiles + up16((size_t)max_tiles * 2 * sizeof(uint32_t));
     p->off_sync = p->off_phase + up16(p->phase_end.size() * sizeof(uint32_t));
-    p->dev_bytes = p->off_sync + up16(kChainSyncWords * sizeof(uint32_t));
+    p->off_q8 = p->off_sync + up16(kChainSyncWords * sizeof(uint32_t));
+    p->dev_bytes = p->off_q8 + up16(p->q8_bytes);
     p->image.assign(p->dev_bytes, 0);
     memcpy(p->image.data(), p->mats.data(), p->mats.size() * sizeof(ChainMat));
     memcpy(p->image.data() + p->off_tiles, p->tiles.data(), p->tiles.size() * sizeof(uint32_t));
@@ -663,6 +672,8 @@ q4s_status q4s_chain_create(const q4s_chain_shape* shape, const void* const* w_p
     auto add = [&](const ChainMat& cm) {
         members.push_back((uint32_t)p->mats.size());
         p->mats.push_back(cm);
+        p->q8_out.push_back(-1);
+        p->q8_in.push_back(-1);
     };
     auto close = [&]() {
         p->phases.push_back(members);
@@ -686,17 +697,32 @@ q4s_status q4s_chain_create(const q4s_chain_shape* shape, const void* const* w_p
             add(cm);
         }
         close();
-        for (int j = 0; j < 2; ++j) {  // gate, up: one activation of norm(h1)
-            ChainMat cm = base(lw[4 + j], F, E);
-            cm.x = word(l, oh1), cm.norm = 1, cm.y = word(l, j == 0 ? og : ou);
+        // gate, up: one activation of norm(h1).  With at most two K splits they run as one
+        // paired matrix whose tiles also leave g * u quantized for down (see ChainMat)
+        const bool pair = choose_ksplit(chunks_of(E)) <= 2;
+        const int64_t q8_at = (int64_t)p->q8_bytes;
+        if (pair) {
+            ChainMat cm = base(lw[4], F, E);
+            cm.w2 = (const uint8_t*)lw[5];
+            p->info.packed_bytes += (int64_t)packed_bytes(F, E);
+            cm.x = word(l, oh1), cm.norm = 1, cm.y = word(l, og), cm.y_b = word(l, ou);
             add(cm);
+            p->q8_out.back() = q8_at;
+            p->q8_bytes += (size_t)(F / 4 + F / 32) * 8;
+        } else {
+            for (int j = 0; j < 2; ++j) {
+                ChainMat cm = base(lw[4 + j], F, E);
+                cm.x = word(l, oh1), cm.norm = 1, cm.y = word(l, j == 0 ? og : ou);
+                add(cm);
+            }
         }
         close();
         {   // dn = Wd Q8(g * u); h2 = h1 + dn
             ChainMat cm = base(lw[6], E, F);
-            cm.x = word(l, og), cm.x2 = word(l, ou), cm.y = word(l, odn), cm.res = word(l, oh1),
-            cm.y2 = word(l, oh2);
+            if (!pair) cm.x = word(l, og), cm.x2 = word(l, ou);
+            cm.y = word(l, odn), cm.res = word(l, oh1), cm.y2 = word(l, oh2);
             add(cm);
+            if (pair) p->q8_in.back() = q8_at;
         }
         close();
     }
@@ -735,6 +761,13 @@ q4s_status q4s_chain_upload(q4s_chain* p, void* dev_mem, size_t dev_bytes, void*
     if (wg < 1 || wg > max_wg)
         return fail(Q4S_ERR_SHAPE, "workgroups=%d out of [1, %d] (all must be resident at once)", wg, max_wg);
     if (wg != p->layout_wg) chain_layout(p, wg);
+    // the Q8_0 product words live in dev_mem: point the matrices' copies in the image at them
+    // (the area itself is uploaded as zeros: tag 0, never written)
+    for (size_t i = 0; i < p->mats.size(); ++i) {
+        ChainMat* cm = (ChainMat*)p->image.data() + i;
+        if (p->q8_out[i] >= 0) cm->yq = (uint64_t*)((uint8_t*)dev_mem + p->off_q8 + p->q8_out[i]);
+        if (p->q8_in[i] >= 0) cm->xq = (const uint64_t*)((uint8_t*)dev_mem + p->off_q8 + p->q8_in[i]);
+    }
     hipStream_t st = (hipStream_t)stream;
     if ((e = hipMemcpyAsync(dev_mem, p->image.data(), p->dev_bytes, hipMemcpyHostToDevice, st)) != hipSuccess)
         return hip_status(e, "chain upload");

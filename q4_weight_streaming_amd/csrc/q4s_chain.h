@@ -9,14 +9,27 @@ namespace q4s {
 // One matrix of the chained decode step (one token).  Activations that cross
 // phases are 64-bit words: fp32 bits in the low half, the step's tag in the
 // high half, so a reader can tell this step's value from an older one.
+//
+// A paired matrix is two matrices of one shape and one activation (gate and
+// up) whose row groups alternate in the tile table: virtual row group 2i is
+// group i of the first matrix (w), 2i+1 group i of the second (w2).  A tile of
+// an even number of groups then holds whole pairs, and its epilogue writes the
+// product y * y_b already quantized, as tagged Q8_0 words (yq): the code word
+// of rows 4j..4j+3 at yq[j] (the codes' bytes in the low half), the fp32 bits
+// of block b's binary16 d_x at yq[rows/4 + b].  The consumer (down) reads them
+// through xq.
 struct ChainMat {
     MatDesc m;            // w and geometry (rows, cols, nb, G, C, ks, dstride), n = 1
     const void* x;        // activation: tagged words [cols], or fp32 when x_plain
     const uint64_t* x2;   // second factor of an elementwise product (tagged), or NULL
+    const uint64_t* xq;   // the activation as tagged Q8_0 words of a paired matrix's product, or NULL
     const void* res;      // residual input added to the output: tagged, or fp32 when res_plain; or NULL
     uint64_t* y;          // tagged output [rows], or NULL
     uint64_t* y2;         // tagged res + y [rows] when res
     float* yf;            // plain fp32 output [rows] (the logits), or NULL
+    const uint8_t* w2;    // paired: the second matrix's packed weights, else NULL
+    uint64_t* y_b;        // paired: tagged output of the second matrix [rows]
+    uint64_t* yq;         // paired: tagged Q8_0 words of y * y_b
     int32_t norm;         // RMS-normalize the activation before quantizing it
     int32_t x_plain, res_plain, pad_;
 };

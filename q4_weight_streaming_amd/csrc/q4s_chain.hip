@@ -46,9 +46,11 @@ __device__ __forceinline__ int64_t chain_spin_limit(const uint32_t* sync) {
     return (int64_t)*gp<uint32_t>(sync + 3);
 }
 
-__device__ __forceinline__ uint64_t tag_word(float v, uint32_t gen) {
-    return ((uint64_t)gen << 32) | (uint64_t)__float_as_uint(v);
+__device__ __forceinline__ uint64_t tag_bits(uint32_t bits, uint32_t gen) {
+    return ((uint64_t)gen << 32) | (uint64_t)bits;
 }
+
+__device__ __forceinline__ uint64_t tag_word(float v, uint32_t gen) { return tag_bits(__float_as_uint(v), gen); }
 
 template <int kSync>
 __device__ __forceinline__ uint64_t chain_ld(const uint64_t* p) {
@@ -212,6 +214,126 @@ __device__ __forceinline__ void chain_quant(f32x4 v, int c, int nb, Q4S_LDS u32x
     dst[lane] = (u32x2){packed, __float_as_uint(__half2float(__ushort_as_half(h)))};
 }
 
+// The Q8_0 codes and scales of chunks [c0, c1) of an activation given as a
+// paired matrix's tagged Q8_0 words (see ChainMat), polled like chain_batch,
+// into the wave's LDS slice: lane l of chunk c takes code word 64c + l (its
+// 4 values) and the d_x word of block 8c + l/8; lanes past the row take zeros,
+// as the quantizer gives them.
+template <int kSync>
+__device__ __forceinline__ void chain_stage_q8(const uint64_t* xq, int n, int c0, int c1, uint32_t gen,
+                                               uint32_t* err, Q4S_LDS u32x2* slice) {
+    const int lane = threadIdx.x & 63;
+    const int nb = n / 32;
+    for (int b0 = c0; b0 < c1; b0 += kChainBatch) {
+        const int cnt = min(kChainBatch, c1 - b0);
+        uint64_t wq[kChainBatch], wd[kChainBatch];
+        auto blk_of = [&](int cc) { return min((b0 + cc) * kChunkBlocks + (lane >> 3), nb - 1); };
+        auto load_all = [&]() {
+#pragma unroll
+            for (int cc = 0; cc < kChainBatch; ++cc)
+                if (cc < cnt) {
+                    const int blk = blk_of(cc);
+                    wq[cc] = chain_ld<kSync>(xq + blk * 8 + (lane & 7));
+                    wd[cc] = chain_ld<kSync>(xq + n / 4 + blk);
+                }
+        };
+        auto all_tagged = [&]() {
+            bool ok = true;
+#pragma unroll
+            for (int cc = 0; cc < kChainBatch; ++cc)
+                if (cc < cnt) ok = ok && (uint32_t)(wq[cc] >> 32) == gen && (uint32_t)(wd[cc] >> 32) == gen;
+            return ok;
+        };
+        if constexpr (kSync == kChainTagged) {
+            const int64_t limit = chain_spin_limit(err);
+            int64_t spins = 0;
+            if (b0 == c0) {  // light poll: the lane's last code word of the batch
+                const uint64_t* last = xq + blk_of(cnt - 1) * 8 + (lane & 7);
+                while ((uint32_t)(chain_ld<kSync>(last) >> 32) != gen) {
+                    if (++spins > limit || ((spins & 1023) == 0 && chain_failed(err))) break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            for (;;) {
+                load_all();
+                if (all_tagged()) break;
+                if (++spins > limit || ((spins & 1023) == 0 && chain_failed(err))) {
+                    chain_fail(err);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        } else {
+            load_all();
+            if (!all_tagged()) chain_fail(err);
+        }
+#pragma unroll
+        for (int cc = 0; cc < kChainBatch; ++cc)
+            if (cc < cnt) {
+                const bool valid = (b0 + cc) * kChunkBlocks + (lane >> 3) < nb;
+                slice[(b0 + cc - c0) * 64 + lane] =
+                    valid ? (u32x2){(uint32_t)wq[cc], (uint32_t)wd[cc]} : (u32x2){0u, 0u};
+            }
+    }
+}
+
+// A paired tile's product rows g*64 .. g*64+63 (lane = row, p = y * y_b) as
+// tagged Q8_0 words: two 32-row blocks, each quantized as the block quantizer
+// does (quant8_amax, quant8_scale, quant8_codes), one value per lane -- the
+// block maximum over its 32 lanes, d = RN(max/127), the code from p * rcp(d)
+// rounded through 1.5 * 2^23 where that is exact, else the correctly rounded
+// division -- then four lanes' codes per word.  Called by a whole wave.
+constexpr int kDppRowMirror = 0x140;  // row_mirror: lane i <- lane 15-i within 16
+template <int kSync>
+__device__ __forceinline__ void chain_store_q8(uint64_t* yq, int64_t rows, int64_t g, float p, uint32_t gen) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = g * kGroupRows + lane;
+    const bool valid = row < rows;  // rows is a multiple of 32: uniform over each block
+    if (!valid) p = 0.0f;
+    uint32_t ab = __float_as_uint(p) & 0x7FFFFFFFu;
+    ab = max(ab, dpp_move<kDppQuadSwap1>(ab));
+    ab = max(ab, dpp_move<kDppQuadSwap2>(ab));
+    ab = max(ab, dpp_move<kDppHalfMirror>(ab));
+    ab = max(ab, dpp_move<kDppRowMirror>(ab));
+    {   // 16-lane rows 2k and 2k+1 meet: the max of each 32-lane block
+        const auto sw = __builtin_amdgcn_permlane16_swap(ab, ab, false, false);
+        ab = max((uint32_t)sw[0], (uint32_t)sw[1]);
+    }
+    const float a = __uint_as_float(ab);
+    const float dd = quant8_scale(a);
+    uint32_t code = 0;
+    if (a != 0.0f) {
+        constexpr float kMagic = 0x1.8p23f;
+        const float rc = __builtin_amdgcn_rcpf(dd);
+        const float mg = fmaf(p, rc, kMagic);
+        const float dist = fmaf(p, rc, -(mg - kMagic));
+        if (dd >= 0x1p-125f && dd <= 0x1p125f && fabsf(dist) < 0.5f - 0x1p-13f)
+            code = __float_as_uint(mg) & 0xFFu;
+        else
+            code = (uint32_t)(uint8_t)(int8_t)(int)roundf(p / dd);
+    }
+    const uint32_t word = code | (__shfl_down(code, 1) << 8) | (__shfl_down(code, 2) << 16) |
+                          (__shfl_down(code, 3) << 24);
+    const uint32_t dbits = __float_as_uint(__half2float(__float2half_rn(dd)));
+    if (valid && (lane & 3) == 0) chain_st<kSync>(yq + row / 4, tag_bits(word, gen));
+    if (valid && (lane & 31) == 0) chain_st<kSync>(yq + rows / 4 + row / 32, tag_bits(dbits, gen));
+}
+
+// Row group vg of a tile's matrix: for a paired matrix group vg/2 of its first
+// (vg even) or second (vg odd) matrix, else group vg.
+__device__ __forceinline__ MatDesc chain_group(const ChainMat& cm, int64_t vg, int64_t& g, int& half) {
+    MatDesc m = cm.m;
+    if (cm.w2) {
+        half = (int)(vg & 1);
+        g = vg >> 1;
+        if (half) m.w = cm.w2;
+    } else {
+        half = 0;
+        g = vg;
+    }
+    return m;
+}
+
 // Prologue of a chained-step wave that streams chunks [c0, c1): waits for the
 // activation, takes the RMS norm of the whole vector when asked, and leaves
 // the Q8_0 codes and scales of its chunks in its LDS slice ([chunk][lane]).
@@ -220,8 +342,12 @@ __device__ __forceinline__ void chain_quant(f32x4 v, int c, int nb, Q4S_LDS u32x
 // butterfly 32, 16, ..., 1 -- every lane ends with the same ss, since each
 // step adds the same two values on both lanes.
 template <int kSync>
-__device__ __noinline__ void chain_stage(const void* x, const uint64_t* x2, int x_plain, int norm, int n, int c0,
-                                         int c1, uint32_t gen, uint32_t* err, Q4S_LDS u32x2* slice) {
+__device__ __noinline__ void chain_stage(const void* x, const uint64_t* x2, const uint64_t* xq, int x_plain, int norm,
+                                         int n, int c0, int c1, uint32_t gen, uint32_t* err, Q4S_LDS u32x2* slice) {
+    if (xq) {  // already quantized by the producing tiles
+        chain_stage_q8<kSync>(xq, n, c0, c1, gen, err, slice);
+        return;
+    }
     const int lane = threadIdx.x & 63;
     const ChainSrc cm{x, x2, x_plain, n};
     const int nb = n / 32;
@@ -286,6 +412,7 @@ template <int kSync>
 struct ActStaged {
     static constexpr bool kLaneCodes = true;   // Prep::packed is the lane's code dword
     const ChainMat& cm;
+    const uint8_t* w;  // the row group's matrix (the second one of a paired matrix's odd groups)
     int64_t g;
     int c0, c1;
     uint32_t gen;
@@ -307,11 +434,11 @@ struct ActStaged {
             uint32_t touch = 0;
             if constexpr (kSync == kChainTagged) {
                 const int lane = threadIdx.x & 63;
-                const uint8_t* w0 = cm.m.w + ((size_t)g * cm.m.C + c0 + 2) * kChunkBytes;
+                const uint8_t* w0 = w + ((size_t)g * cm.m.C + c0 + 2) * kChunkBytes;
                 const int lines = max(c1 - c0 - 2, 0) * (kChunkBytes / 128);
                 for (int i = lane; i < lines; i += 64) touch ^= *gp<uint32_t>(w0 + (size_t)i * 128);
             }
-            chain_stage<kSync>(cm.x, cm.x2, cm.x_plain, cm.norm, cm.m.cols, c0, c1, gen, err, slice);
+            chain_stage<kSync>(cm.x, cm.x2, cm.xq, cm.x_plain, cm.norm, cm.m.cols, c0, c1, gen, err, slice);
             if (gen == 0) err[2] = touch;  // never taken (tags start at 1); keeps the touches
             staged = true;
             if (mark && threadIdx.x == 0) gwr<uint64_t>(mark)[0] = __builtin_amdgcn_s_memrealtime();
@@ -330,12 +457,13 @@ template <int kSync>
 __device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, float* red, Q4S_LDS u32x2* stage,
                                            uint32_t gen, uint32_t* err, uint64_t* mark_start, uint64_t* mark_ready) {
     if (mark_start && threadIdx.x == 0) gwr<uint64_t>(mark_start)[0] = __builtin_amdgcn_s_memrealtime();
-    const MatDesc& m = cm.m;
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int ks = m.ks;
+    const int ks = cm.m.ks;
     const int gpw = kWaves / ks;
-    const int64_t g = gset * gpw + wave / ks;
+    int64_t g;
+    int half;
+    const MatDesc m = chain_group(cm, gset * gpw + wave / ks, g, half);
     const int sp = wave % ks;
     const int c0 = (int)((int64_t)sp * m.C / ks);
     const int c1 = (int)((int64_t)(sp + 1) * m.C / ks);
@@ -345,18 +473,25 @@ __device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, flo
     const int64_t rrow = min(row, (int64_t)m.rows - 1);
     uint64_t rword = 0;
     if (cm.res && !cm.res_plain && sp == 0 && g < m.G) rword = chain_ld<kSync>((const uint64_t*)cm.res + rrow);
-    ActStaged<kSync> act{cm, g, c0, c1, gen, err, stage + wave * (kChainMaxChunks * 64), false, mark_ready};
+    ActStaged<kSync> act{cm, m.w, g, c0, c1, gen, err, stage + wave * (kChainMaxChunks * 64), false, mark_ready};
     wave_task<1>(m, (int)g, c0, c1, acc, act);
     float v = acc[0];
-    if (ks > 1) {
+    if (ks > 1 || cm.w2) {
         red[wave * 64 + lane] = v;
         __syncthreads();
         if (sp != 0) return;
-        v = red[wave * 64 + lane];
-        for (int j = 1; j < ks; ++j) v += red[(wave + j) * 64 + lane];
+        // a row group's K ranges added in order; a pair's first half also forms its partner's
+        auto total = [&](int w0) {
+            float t = red[w0 * 64 + lane];
+            for (int j = 1; j < ks; ++j) t += red[(w0 + j) * 64 + lane];
+            return t;
+        };
+        v = total(wave);
+        if (cm.w2 && half == 0 && g < m.G) chain_store_q8<kSync>(cm.yq, m.rows, g, v * total(wave + ks), gen);
     }
     if (g >= m.G || row >= m.rows) return;
-    if (cm.y) chain_st<kSync>(cm.y + row, tag_word(v, gen));
+    uint64_t* y = half ? cm.y_b : cm.y;
+    if (y) chain_st<kSync>(y + row, tag_word(v, gen));
     if (cm.yf) gwr<float>(cm.yf)[row] = v;
     if (cm.res) {
         const float r = cm.res_plain ? ((const float*)cm.res)[row]
@@ -409,12 +544,13 @@ __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t til
                                                  Q4S_LDS u32x2* stage, Q4S_LDS uint32_t* terms, uint32_t gen,
                                                  uint32_t* err, uint64_t* mark_start, uint64_t* mark_ready) {
     if (mark_start && threadIdx.x == 0) gwr<uint64_t>(mark_start)[0] = __builtin_amdgcn_s_memrealtime();
-    const MatDesc& m = cm.m;
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int C = m.C, ks = m.ks;
     const int gi = wave / kWpg, lw = wave % kWpg;  // the wave's group within the tile, its place in the group
-    const int64_t g = tile * (kWaves / kWpg) + gi;
+    int64_t g;
+    int half;
+    const MatDesc m = chain_group(cm, tile * (kWaves / kWpg) + gi, g, half);
+    const int C = m.C, ks = m.ks;
     const bool live = g < m.G;
     // one group's table takes all kChainTermWords (<= 16 chunks); two groups (<= 8 chunks each) halve it
     Q4S_LDS uint32_t* gterms = terms + gi * (kChainTermWords / 2);
@@ -426,7 +562,7 @@ __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t til
     const int i0 = split_first<kWpg>(lw, C), i1 = split_first<kWpg>(lw + 1, C);
     if (live && i0 < i1) {
         Q4S_LDS u32x2* slice = stage + wave * (kChainMaxChunks * 64);
-        ActStaged<kSync> act{cm, g, i0, i1, gen, err, slice, false, wave == 0 ? mark_ready : nullptr};
+        ActStaged<kSync> act{cm, m.w, g, i0, i1, gen, err, slice, false, wave == 0 ? mark_ready : nullptr};
         const uint8_t* wp = m.w + ((size_t)g * m.C + i0) * kChunkBytes + lane * kBlockNibBytes;
         Chunk a, b;
         load_chunk(a, wp);
@@ -468,10 +604,18 @@ __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t til
         red[wave * 64 + lane] = acc;
     }
     __syncthreads();
-    if (!live || lw != 0 || row >= m.rows) return;
-    float v = red[wave * 64 + lane];
-    for (int j = 1; j < ks; ++j) v += red[(wave + j) * 64 + lane];
-    if (cm.y) chain_st<kSync>(cm.y + row, tag_word(v, gen));
+    if (!live || lw != 0) return;
+    // a row group's K ranges added in order; a pair's first half also forms its partner's
+    auto total = [&](int w0) {
+        float t = red[w0 * 64 + lane];
+        for (int j = 1; j < ks; ++j) t += red[(w0 + j) * 64 + lane];
+        return t;
+    };
+    const float v = total(wave);
+    if (cm.w2 && half == 0) chain_store_q8<kSync>(cm.yq, m.rows, g, v * total(wave + kWpg), gen);
+    if (row >= m.rows) return;
+    uint64_t* y = half ? cm.y_b : cm.y;
+    if (y) chain_st<kSync>(y + row, tag_word(v, gen));
     if (cm.yf) gwr<float>(cm.yf)[row] = v;
     if (cm.res) {
         const float r = cm.res_plain ? ((const float*)cm.res)[row]

@@ -3,7 +3,10 @@ and the logits equal the oracle's chained step (the fixed fp32 order of the
 milestone M16 reading, the Q8_0 quantizer and the RMS norm) bit for bit, in all
 three phase-synchronisation modes, at small, ragged and full Qwen2.5-1.5B
 shapes (28 layers, 868 MB), with the persistent workgroup count both one per
-compute unit and below the number of tiles of a phase."""
+compute unit and below the number of tiles of a phase.  Gate and up run as one
+paired matrix whose tiles hand g * u to down as Q8_0 words (every tile layout:
+two groups per tile, group sets of one and two K splits), and as two matrices
+when their rows have four K splits."""
 import numpy as np
 import pytest
 import torch
@@ -84,6 +87,21 @@ def test_chain_ragged_shapes(oracle, mode):
     vals, tags, lg, _ = _run(wp, h0d, acts, logits, L, E, D, F, V, mode, 3)
     assert (tags == 1).all()
     _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, "ragged")
+
+
+@pytest.mark.parametrize("mode", [q.CHAIN_TREE, q.CHAIN_TAGGED], ids=["tree", "tagged"])
+def test_chain_wide_hidden_unpaired(oracle, mode):
+    """hidden 4352 (17 chunks: four K splits), so gate and up cannot run as one paired
+    matrix and down quantizes g * u itself; ff 96 (one partial chunk)."""
+    require_gpu()
+    L, E, D, F, V = 1, 4352, 32, 96, 64
+    shapes, ws, h0 = _inputs(43, L, E, D, F, V, scale=0.05, outliers=0)
+    ref_acts, ref_logits = oracle.chain_step(ws, E, D, F, V, h0)
+    wp, h0d, acts, logits = _device(shapes, ws, h0, L, E, D, F, V)
+    vals, tags, lg, info = _run(wp, h0d, acts, logits, L, E, D, F, V, mode, 0)
+    assert info["n_phases"] == 4 * L + 1
+    assert (tags == 1).all()
+    _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, "wide hidden")
 
 
 def test_chain_head_only(oracle):
