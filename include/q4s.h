@@ -414,8 +414,11 @@ q4s_status q4s_chain_create(const q4s_chain_shape* shape, const void* const* w_p
 
 /*
  * Copy the chain's tables into dev_mem (16-byte aligned, caller-owned, kept
- * alive while the chain is used) and zero `acts`, both on `stream`.  Needs
- * the GPU: resolves and checks the workgroup count.
+ * alive while the chain is used) and zero `acts`, both on `stream`.  dev_mem
+ * also holds, past the tables, the step's quantized g * u words (written by
+ * the gate/up tiles and read by down when gate and up have at most two K
+ * splits, i.e. E <= 4096), which the upload zeroes.  Needs the GPU: resolves
+ * and checks the workgroup count.
  */
 q4s_status q4s_chain_upload(q4s_chain* chain, void* dev_mem, size_t dev_bytes, void* stream);
 
