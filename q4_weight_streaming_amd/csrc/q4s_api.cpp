@@ -685,16 +685,20 @@ q4s_status q4s_chain_create(const q4s_chain_shape* shape, const void* const* w_p
         const int hp = l == 0 ? 1 : 0;
         // q, k, v: one activation of norm(h)
         const int64_t qkv_rows[3] = {E, D, D}, qkv_off[3] = {oq, ok_, ov};
+        const int64_t q_q8 = (int64_t)p->q8_bytes;  // q's tiles also leave q quantized for o
+        p->q8_bytes += (size_t)(E / 4 + E / 32) * 8;
         for (int j = 0; j < 3; ++j) {
             ChainMat cm = base(lw[j], qkv_rows[j], E);
             cm.x = h, cm.x_plain = hp, cm.norm = 1, cm.y = word(l, qkv_off[j]);
             add(cm);
+            if (j == 0) p->q8_out.back() = q_q8;
         }
         close();
         {   // o = Wo Q8(q); h1 = h + o
             ChainMat cm = base(lw[3], E, E);
-            cm.x = word(l, oq), cm.y = word(l, oo), cm.res = h, cm.res_plain = hp, cm.y2 = word(l, oh1);
+            cm.y = word(l, oo), cm.res = h, cm.res_plain = hp, cm.y2 = word(l, oh1);
             add(cm);
+            p->q8_in.back() = q_q8;
         }
         close();
         // gate, up: one activation of norm(h1).  With at most two K splits they run as one

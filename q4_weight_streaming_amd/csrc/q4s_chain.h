@@ -17,7 +17,7 @@ namespace q4s {
 // product y * y_b already quantized, as tagged Q8_0 words (yq): the code word
 // of rows 4j..4j+3 at yq[j] (the codes' bytes in the low half), the fp32 bits
 // of block b's binary16 d_x at yq[rows/4 + b].  The consumer (down) reads them
-// through xq.
+// through xq.  q hands o its input the same way (yq without w2).
 struct ChainMat {
     MatDesc m;            // w and geometry (rows, cols, nb, G, C, ks, dstride), n = 1
     const void* x;        // activation: tagged words [cols], or fp32 when x_plain
@@ -29,7 +29,7 @@ struct ChainMat {
     float* yf;            // plain fp32 output [rows] (the logits), or NULL
     const uint8_t* w2;    // paired: the second matrix's packed weights, else NULL
     uint64_t* y_b;        // paired: tagged output of the second matrix [rows]
-    uint64_t* yq;         // paired: tagged Q8_0 words of y * y_b
+    uint64_t* yq;         // tagged Q8_0 words of y * y_b (paired) or of y (q, for o), or NULL
     int32_t norm;         // RMS-normalize the activation before quantizing it
     int32_t x_plain, res_plain, pad_;
 };

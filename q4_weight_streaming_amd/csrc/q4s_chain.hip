@@ -277,8 +277,9 @@ __device__ __forceinline__ void chain_stage_q8(const uint64_t* xq, int n, int c0
     }
 }
 
-// A paired tile's product rows g*64 .. g*64+63 (lane = row, p = y * y_b) as
-// tagged Q8_0 words: two 32-row blocks, each quantized as the block quantizer
+// Rows g*64 .. g*64+63 (lane = row) of a tile's output -- a paired tile's
+// product y * y_b, or the output itself (q, read by o) -- as tagged Q8_0
+// words: two 32-row blocks, each quantized as the block quantizer
 // does (quant8_amax, quant8_scale, quant8_codes), one value per lane -- the
 // block maximum over its 32 lanes, d = RN(max/127), the code from p * rcp(d)
 // rounded through 1.5 * 2^23 where that is exact, else the correctly rounded
@@ -489,6 +490,7 @@ __device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, flo
         v = total(wave);
         if (cm.w2 && half == 0 && g < m.G) chain_store_q8<kSync>(cm.yq, m.rows, g, v * total(wave + ks), gen);
     }
+    if (cm.yq && !cm.w2 && g < m.G) chain_store_q8<kSync>(cm.yq, m.rows, g, v, gen);  // the output itself
     if (g >= m.G || row >= m.rows) return;
     uint64_t* y = half ? cm.y_b : cm.y;
     if (y) chain_st<kSync>(y + row, tag_word(v, gen));
@@ -613,6 +615,7 @@ __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t til
     };
     const float v = total(wave);
     if (cm.w2 && half == 0) chain_store_q8<kSync>(cm.yq, m.rows, g, v * total(wave + kWpg), gen);
+    if (cm.yq && !cm.w2) chain_store_q8<kSync>(cm.yq, m.rows, g, v, gen);  // the output itself
     if (row >= m.rows) return;
     uint64_t* y = half ? cm.y_b : cm.y;
     if (y) chain_st<kSync>(y + row, tag_word(v, gen));
