@@ -405,6 +405,13 @@ __device__ __noinline__ void chain_stage(const void* x, const uint64_t* x2, cons
     }
 }
 
+// What a wave's LDS slice holds: the Q8_0 codes of chunks [c0, c1) of phase
+// `phase`'s activation (the matrices of a phase share one activation), so a
+// workgroup's later tiles of a phase skip the prologue the first one ran.
+struct StageKey {
+    int phase, c0, c1;
+};
+
 // The activation source of a chained-step wave (see ActQuant): on first use
 // the prologue stages the wave's whole range, after the first two chunks'
 // weight loads are already in flight; every chunk then reads its codes and
@@ -419,6 +426,8 @@ struct ActStaged {
     uint32_t gen;
     uint32_t* err;
     Q4S_LDS u32x2* slice;
+    StageKey& key;   // what the slice holds
+    int phase;
     bool staged;
     uint64_t* mark;  // NULL, or where to record when the first tile of the phase had its activation
     struct Prep {
@@ -427,6 +436,7 @@ struct ActStaged {
     };
     __device__ __forceinline__ void load(int, int) {}
     __device__ __forceinline__ Prep prepare(int, int c) {
+        if (!staged && key.phase == phase && key.c0 == c0 && key.c1 == c1) staged = true;
         if (!staged) {
             // With tagged phases the wave usually waits here for the activation: touch the
             // weight chunks after the two already in flight (one dword per 128-byte line) so
@@ -442,6 +452,7 @@ struct ActStaged {
             chain_stage<kSync>(cm.x, cm.x2, cm.xq, cm.x_plain, cm.norm, cm.m.cols, c0, c1, gen, err, slice);
             if (gen == 0) err[2] = touch;  // never taken (tags start at 1); keeps the touches
             staged = true;
+            key = {phase, c0, c1};
             if (mark && threadIdx.x == 0) gwr<uint64_t>(mark)[0] = __builtin_amdgcn_s_memrealtime();
         }
         const u32x2 e = slice[(c - c0) * 64 + (threadIdx.x & 63)];
@@ -456,7 +467,8 @@ struct ActStaged {
 // then the epilogue stores (tagged output, residual sum, plain logits).
 template <int kSync>
 __device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, float* red, Q4S_LDS u32x2* stage,
-                                           uint32_t gen, uint32_t* err, uint64_t* mark_start, uint64_t* mark_ready) {
+                                           StageKey& key, int phase, uint32_t gen, uint32_t* err,
+                                           uint64_t* mark_start, uint64_t* mark_ready) {
     if (mark_start && threadIdx.x == 0) gwr<uint64_t>(mark_start)[0] = __builtin_amdgcn_s_memrealtime();
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -474,7 +486,8 @@ __device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, flo
     const int64_t rrow = min(row, (int64_t)m.rows - 1);
     uint64_t rword = 0;
     if (cm.res && !cm.res_plain && sp == 0 && g < m.G) rword = chain_ld<kSync>((const uint64_t*)cm.res + rrow);
-    ActStaged<kSync> act{cm, m.w, g, c0, c1, gen, err, stage + wave * (kChainMaxChunks * 64), false, mark_ready};
+    ActStaged<kSync> act{cm, m.w, g, c0, c1, gen, err, stage + wave * (kChainMaxChunks * 64), key, phase, false,
+                         mark_ready};
     wave_task<1>(m, (int)g, c0, c1, acc, act);
     float v = acc[0];
     if (ks > 1 || cm.w2) {
@@ -543,8 +556,9 @@ __device__ __forceinline__ void chunk_terms(int c, const Chunk& ch, ActStaged<kS
 
 template <int kSync, int kWpg>
 __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t tile, float* red,
-                                                 Q4S_LDS u32x2* stage, Q4S_LDS uint32_t* terms, uint32_t gen,
-                                                 uint32_t* err, uint64_t* mark_start, uint64_t* mark_ready) {
+                                                 Q4S_LDS u32x2* stage, Q4S_LDS uint32_t* terms, StageKey& key,
+                                                 int phase, uint32_t gen, uint32_t* err, uint64_t* mark_start,
+                                                 uint64_t* mark_ready) {
     if (mark_start && threadIdx.x == 0) gwr<uint64_t>(mark_start)[0] = __builtin_amdgcn_s_memrealtime();
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -564,7 +578,7 @@ __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t til
     const int i0 = split_first<kWpg>(lw, C), i1 = split_first<kWpg>(lw + 1, C);
     if (live && i0 < i1) {
         Q4S_LDS u32x2* slice = stage + wave * (kChainMaxChunks * 64);
-        ActStaged<kSync> act{cm, m.w, g, i0, i1, gen, err, slice, false, wave == 0 ? mark_ready : nullptr};
+        ActStaged<kSync> act{cm, m.w, g, i0, i1, gen, err, slice, key, phase, false, wave == 0 ? mark_ready : nullptr};
         const uint8_t* wp = m.w + ((size_t)g * m.C + i0) * kChunkBytes + lane * kBlockNibBytes;
         Chunk a, b;
         load_chunk(a, wp);
@@ -679,6 +693,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chain(ChainParams P) {
     if (P.trace && threadIdx.x == 0)  // when this workgroup started, after the phase-end plane
         gwr<uint64_t>(P.trace)[(size_t)P.n_phases * nwg + b] = __builtin_amdgcn_s_memrealtime();
     uint32_t begin = 0;
+    StageKey key{-1, 0, 0};  // this wave's LDS slice holds nothing yet
     for (int p = 0; p < P.n_phases; ++p) {
         const uint32_t end = P.phase_end[p];
         const uint32_t j0 = (b + nwg - begin % nwg) % nwg;  // phase tiles start on workgroup begin mod nwg
@@ -692,12 +707,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_chain(ChainParams P) {
             const uint32_t tw = P.tiles[2 * (size_t)t + 1];
             if (tw & kChainSplit4)  // one row group, its chunks spread over the 4 waves
                 chain_tile_split<kSync, 4>(cm, tw & kChainTileIndex, red, (Q4S_LDS u32x2*)stage,
-                                           (Q4S_LDS uint32_t*)terms, P.gen, P.sync, ms, mr);
+                                           (Q4S_LDS uint32_t*)terms, key, p, P.gen, P.sync, ms, mr);
             else if (tw & kChainSplit2)  // two row groups, two waves each
                 chain_tile_split<kSync, 2>(cm, tw & kChainTileIndex, red, (Q4S_LDS u32x2*)stage,
-                                           (Q4S_LDS uint32_t*)terms, P.gen, P.sync, ms, mr);
+                                           (Q4S_LDS uint32_t*)terms, key, p, P.gen, P.sync, ms, mr);
             else  // a group set: one wave per row group (or K range)
-                chain_tile<kSync>(cm, tw, red, (Q4S_LDS u32x2*)stage, P.gen, P.sync, ms, mr);
+                chain_tile<kSync>(cm, tw, red, (Q4S_LDS u32x2*)stage, key, p, P.gen, P.sync, ms, mr);
             __syncthreads();
         }
         if (P.trace && threadIdx.x == 0)  // when this workgroup is done with the phase
