@@ -87,7 +87,7 @@
 extern "C" {
 #endif
 
-#define Q4S_ABI_VERSION 3
+#define Q4S_ABI_VERSION 4
 #define Q4S_MAX_N 24   /* activation rows per Q4_0 product (one weight pass) */
 #define Q4S_MAX_N_Q8 8 /* activation rows per Q8_0-weight product */
 
@@ -214,6 +214,20 @@ q4s_status q4s_repack_q8_0(const void* w_q8_0, void* w_packed, int64_t rows, int
  */
 q4s_status q4s_gemv_q8_0(const void* w_packed, const void* x_q8, float* y, int64_t rows,
                          int64_t cols, int n, void* stream);
+
+/*
+ * The 1-row Q8_0-weight GEMV from an fp32 activation: x (fp32 [cols], 16-byte
+ * aligned) is quantized into x_q8 (planar Q8_0 of one row, 16-byte aligned,
+ * receives exactly what q4s_quantize_q8_0 writes) and y = q4s_gemv_q8_0 of it
+ * (bit-identical).  When cols <= 2048 (one K split) both happen in one launch,
+ * each wave quantizing the activation of the chunk it streams (the mega
+ * kernel of milestone M15 quantizes inside its one kernel); wider matrices
+ * take a quantize launch and the GEMV.  x, x_q8 and y must not overlap each
+ * other or w_packed.  rows == 0 writes nothing.  Needs no workspace.  Source: as q4s_gemv_q8_0, and the
+ * activation quantization of M3.5 / M14.
+ */
+q4s_status q4s_gemv_q8_0_f32(const void* w_packed, const float* x, void* x_q8, float* y, int64_t rows,
+                             int64_t cols, void* stream);
 
 /*
  * Test hook: exact per-block sums s[t][r][b] = sum_j w_{r,b,j} * q_{t,b,j},

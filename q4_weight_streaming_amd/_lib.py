@@ -82,6 +82,7 @@ def lib():
             "q4s_packed_q8_0_bytes": ([i64, i64], sz),
             "q4s_repack_q8_0": ([p, p, i64, i64, p], i32),
             "q4s_gemv_q8_0": ([p, p, p, i64, i64, i32, p], i32),
+            "q4s_gemv_q8_0_f32": ([p, p, p, p, i64, i64, p], i32),
             "q4s_block_sums_q8_0": ([p, p, p, i64, i64, i32, p], i32),
             "q4s_requant_q8_0_to_q4_0": ([p, p, i64, i64, p], i32),
             "q4s_attn_workspace_bytes": ([i32, i64], sz),
@@ -112,7 +113,7 @@ def lib():
             f = getattr(L, name)
             f.argtypes = args
             f.restype = res
-        if L.q4s_abi_version() != 3:
+        if L.q4s_abi_version() != 4:
             raise RuntimeError("libq4stream ABI version mismatch")
         _lib = L
     return _lib
@@ -248,6 +249,22 @@ def gemv_q8_0(w_packed: torch.Tensor, x_q8: torch.Tensor, rows: int, cols: int, 
                                                  _dev(out, "out", torch.float32), rows, cols, n,
                                                  _stream(w_packed.device)))
     return out
+
+
+def gemv_q8_0_f32(w_packed: torch.Tensor, x: torch.Tensor, rows: int, cols: int,
+                  out: torch.Tensor | None = None, x_q8: torch.Tensor | None = None):
+    """1-row Q8_0-weight GEMV from an fp32 activation x [cols] (or [1][cols]): returns (y fp32 [1][rows],
+    x_q8, its planar Q8_0 bytes), in one launch when cols <= 2048."""
+    if out is None:
+        out = torch.empty((1, rows), dtype=torch.float32, device=w_packed.device)
+    if x_q8 is None:
+        x_q8 = torch.empty(q8_bytes(1, cols), dtype=torch.uint8, device=w_packed.device)
+    _check("q4s_gemv_q8_0_f32", lib().q4s_gemv_q8_0_f32(_dev(w_packed, "w_packed", torch.uint8),
+                                                         _dev(x, "x", torch.float32),
+                                                         _dev(x_q8, "x_q8", torch.uint8),
+                                                         _dev(out, "out", torch.float32), rows, cols,
+                                                         _stream(w_packed.device)))
+    return out, x_q8
 
 
 def block_sums_q8_0(w_packed: torch.Tensor, x_q8: torch.Tensor, rows: int, cols: int, n: int) -> torch.Tensor:

@@ -267,6 +267,26 @@ q4s_status q4s_gemv_q8_0(const void* w_packed, const void* x_q8, float* y, int64
     return hip_status(launch_gemv_q8_0(m, n, gsets_of(m.G, m.ks), (hipStream_t)stream), "gemv launch");
 }
 
+q4s_status q4s_gemv_q8_0_f32(const void* w_packed, const float* x, void* x_q8, float* y, int64_t rows,
+                             int64_t cols, void* stream) {
+    q4s_status s = check_gemv(w_packed, x_q8, y, rows, cols, 1, true);
+    if (s) return s;
+    const size_t xb = rows > 0 ? (size_t)cols * 4 : 0;
+    if ((s = check_ptr(x, xb, 16, "x"))) return s;
+    const size_t qb = rows > 0 ? q8_bytes(1, cols) : 0;
+    if (overlap(x, xb, x_q8, qb) || overlap(x, xb, y, (size_t)rows * 4) ||
+        overlap(x, xb, w_packed, packed_q8_bytes(rows, cols)) || overlap(x_q8, qb, w_packed, packed_q8_bytes(rows, cols)))
+        return fail(Q4S_ERR_ALIAS, "x, x_q8, y and w_packed must not overlap");
+    if (rows == 0) return ok();
+    MatDesc m = make_desc(w_packed, x_q8, y, rows, cols, 1);
+    if (m.ks == 1) {  // one launch: the waves quantize the chunks they stream
+        m.x = x;
+        return hip_status(launch_gemv_q8_0_fused(m, (hipStream_t)stream), "gemv launch");
+    }
+    if ((s = q4s_quantize_q8_0(x, x_q8, 1, cols, stream))) return s;
+    return hip_status(launch_gemv_q8_0(m, 1, gsets_of(m.G, m.ks), (hipStream_t)stream), "gemv launch");
+}
+
 q4s_status q4s_block_sums_q8_0(const void* w_packed, const void* x_q8, int32_t* sums, int64_t rows,
                                int64_t cols, int n, void* stream) {
     return block_sums_any(w_packed, x_q8, sums, rows, cols, n, stream, true);

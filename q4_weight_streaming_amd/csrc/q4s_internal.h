@@ -93,6 +93,8 @@ hipError_t launch_sweep_fused(const MatDesc* dev_mats, const uint32_t* dev_tiles
 hipError_t launch_repack_q8_0(const uint8_t* w, uint8_t* packed, int64_t rows, int64_t cols,
                               hipStream_t st);
 hipError_t launch_gemv_q8_0(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st);
+// 1-row GEMV of a single-split Q8_0 matrix (C <= 8) quantizing m.x into m.xq / m.xd in the same launch.
+hipError_t launch_gemv_q8_0_fused(const MatDesc& m, hipStream_t st);
 hipError_t launch_block_sums_q8_0(const MatDesc& m, int n, int32_t* s, hipStream_t st);
 hipError_t launch_requant_q8_0_to_q4_0(const uint8_t* w8, uint8_t* w4, int64_t n_blocks, hipStream_t st);
 // Decode attention (q4s_attn.hip): split-KV partials over 64-position splits, then the combine.

@@ -14,7 +14,7 @@
 // 32 int8 weights of a lane's row meet the wave-uniform activation in 8
 // v_dot4 steps.  Chain A takes the even blocks of a chunk and chain B the odd
 // ones, so the matrix-core path can pair blocks 2i and 2i+1 of one piece.
-#include "q4s_device.h"
+#include "q4s_lane.h"
 
 namespace q4s {
 namespace {
@@ -233,16 +233,111 @@ __global__ __launch_bounds__(kThreads, N == 1 ? 1 : 2) void k_gemv_q8(MatDesc m)
         });
 }
 
-// 1-row GEMV of a matrix with one K split (at most 8 chunks): one wave per
-// workgroup and row group, the same wave task, so a lone large matrix (an
-// output head: 2374 row groups) spreads evenly over the CUs instead of in
-// tiles of 4 row groups, 2 or 3 per CU.
-__global__ __launch_bounds__(64) void k_gemv_q8_wave(MatDesc m) {
-    float acc[1];
-    const int g = blockIdx.x;
-    wave_task_q8<1>(m, g, 0, m.C, acc);
-    const int64_t row = (int64_t)g * kGroupRows + (threadIdx.x & 63);
-    if (row < m.rows) gwr<float>(m.y)[row] = acc[0];
+// ---------------------------------------------------------------- 1-row split tiles
+//
+// A 1-row GEMV of a Q8_0 matrix with one K split (C <= 8 chunks), as the Q4_0
+// split tiles: each 64-row group gets an 8-wave workgroup, wave w the chunks
+// [ceil(wC/8), ceil((w+1)C/8)) -- one at most, both pieces loaded at once --
+// whose exact block sums (int32) and binary16 d_w go to LDS, with the chunk's
+// d_x when the wave quantized the activation itself (kFused: the sweep's
+// in-wave quantizer, codes to every lane by lane swaps and DPP dot operands;
+// 8-bit weights need no unpack, so the 32 raw int8 weights of a block meet the
+// codes as they are).  Waves 0 and 1 then run chains A (even blocks) and B (odd
+// blocks) over all chunks in order with wave_task_q8's fmaf, and wave 0 adds
+// 0 + (A + B): bit-identical to wave_task_q8.  (For the 151936 x 1536 head:
+// 38.2 us quantizing on the fly, against 39.6 us for one wave per row group
+// over a quantized activation plus 2.5 us for the quantize launch.)
+constexpr int kSplitWavesQ8 = 8;
+struct SplitLdsQ8 {
+    int32_t s[kChunkBlocks * kChunkBlocks * 64];   // [chunk][block][lane], C <= 8
+    uint16_t dw[kChunkBlocks * kChunkBlocks * 64];
+    uint32_t dx[kChunkBlocks * kChunkBlocks];      // fp32 bits of d_x per block (kFused)
+    float chain_b[64];
+};
+
+template <bool kFused>
+__device__ __forceinline__ void split_group_q8(const MatDesc& m, int g, SplitLdsQ8& l) {
+    const int wave = wave_uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int C = m.C;
+    const int c = (wave * C + kSplitWavesQ8 - 1) / kSplitWavesQ8;
+    if (c < ((wave + 1) * C + kSplitWavesQ8 - 1) / kSplitWavesQ8) {  // the wave's one chunk
+        const uint8_t* wp = m.w + ((size_t)g * C + c) * kQ8ChunkBytes;
+        Piece pc[2];
+        load_piece(pc[0], wp, lane);
+        load_piece(pc[1], wp + kQ8PieceBytes, lane);
+        ActQuant aq{m, g == 0, {}};
+        if constexpr (kFused) aq.load(0, c);
+        int s[kChunkBlocks];
+        if constexpr (kFused) {
+            const auto pr = aq.prepare(0, c);
+            uint32_t y[4];
+            rows4(pr.packed, y);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {  // piece k: blocks 4k .. 4k+3
+                Unpacked u[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        u[x].lo[j] = pc[k].q[2 * x][j];
+                        u[x].hi[j] = pc[k].q[2 * x + 1][j];
+                    }
+                int sh[4];
+                quad_dot16_rows(u, y[2 * k], y[2 * k + 1], sh);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) s[4 * k + x] = sh[x];
+            }
+            if ((lane & 7) == 0) l.dx[c * kChunkBlocks + (lane >> 3)] = pr.dbits;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int b = 0; b < kQ8PieceBlocks; ++b) {
+                    // padding blocks of the last chunk have zero weights; read a valid block
+                    const int blk = min(c * kChunkBlocks + k * kQ8PieceBlocks + b, m.nb - 1);
+                    s[4 * k + b] = block_dot_q8(pc[k].q[2 * b], pc[k].q[2 * b + 1], act_q(m.xq, (int64_t)blk * 32));
+                }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int b = 0; b < kQ8PieceBlocks; ++b) {
+                const int i = (c * kChunkBlocks + k * kQ8PieceBlocks + b) * 64 + lane;
+                const uint32_t sw = pc[k].scale[b >> 1];
+                l.s[i] = s[4 * k + b];
+                l.dw[i] = (uint16_t)((b & 1) ? (sw >> 16) : (sw & 0xffffu));
+            }
+    }
+    __syncthreads();
+    float p = 0.0f;
+    if (wave < 2) {  // wave 0: chain A, the even blocks; wave 1: chain B, the odd ones
+        for (int cc = 0; cc < C; ++cc) {
+#pragma unroll
+            for (int j = 0; j < kChunkBlocks / 2; ++j) {
+                const int b = 2 * j + wave;
+                const int i = (cc * kChunkBlocks + b) * 64 + lane;
+                const float dw = __half2float(__ushort_as_half(l.dw[i]));
+                const float dx = kFused ? __uint_as_float(l.dx[cc * kChunkBlocks + b])
+                                        : act_d(m.xd, min(cc * kChunkBlocks + b, m.nb - 1));
+                p = fmaf(dw * dx, (float)l.s[i], p);
+            }
+        }
+        if (wave == 1) l.chain_b[lane] = p;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        float acc = 0.0f;
+        acc += p + l.chain_b[lane];
+        const int64_t row = (int64_t)g * kGroupRows + lane;
+        if (row < m.rows) gwr<float>(m.y)[row] = acc;
+    }
+}
+
+template <bool kFused>
+__global__ __launch_bounds__(64 * kSplitWavesQ8) void k_gemv_q8_split(MatDesc m) {
+    __shared__ SplitLdsQ8 l;
+    split_group_q8<kFused>(m, blockIdx.x, l);
 }
 
 // Test hook: the exact per-block sums, from the same loads and dot.
@@ -374,7 +469,7 @@ static void gemv_q8_n(const MatDesc& m, int64_t n_gsets, hipStream_t st) {
 hipError_t launch_gemv_q8_0(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st) {
     if (n_gsets == 0 || n == 0) return hipSuccess;
     if (n == 1 && m.ks == 1) {
-        hipLaunchKernelGGL(k_gemv_q8_wave, dim3((unsigned)m.G), dim3(64), 0, st, m);
+        hipLaunchKernelGGL(k_gemv_q8_split<false>, dim3((unsigned)m.G), dim3(64 * kSplitWavesQ8), 0, st, m);
         return hipGetLastError();
     }
     switch (n) {
@@ -388,6 +483,12 @@ hipError_t launch_gemv_q8_0(const MatDesc& m, int n, int64_t n_gsets, hipStream_
         case 8: gemv_q8_n<8>(m, n_gsets, st); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_q8_0_fused(const MatDesc& m, hipStream_t st) {
+    if (m.G == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_gemv_q8_split<true>, dim3((unsigned)m.G), dim3(64 * kSplitWavesQ8), 0, st, m);
     return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ def test_exports_every_declared_function(L):
     assert len(names) >= 23
     for n in names:
         assert hasattr(L, n), n
-    assert L.q4s_abi_version() == 3
+    assert L.q4s_abi_version() == 4
 
 
 def test_status_strings(L):
@@ -98,6 +98,17 @@ def test_other_entry_points_validate(L):
     assert L.q4s_repack_q8_0(FAKE, FAKE, 64, 64, None) == 4
     assert L.q4s_block_sums_q8_0(FAKE, FAKE + (1 << 28), FAKE + 2, 64, 64, 1, None) == 3
     assert L.q4s_requant_q8_0_to_q4_0(FAKE, FAKE + 1, 64, 64, None) == 3
+    # Q8_0 weights from an fp32 activation (quantized in the launch)
+    f = L.q4s_gemv_q8_0_f32
+    W, X, XQ, Y = FAKE, FAKE + (1 << 24), FAKE + (1 << 26), FAKE + (1 << 28)
+    assert f(W, X, XQ, Y, 64, 33, None) == 2                             # cols % 32
+    assert f(W, X + 4, XQ, Y, 64, 64, None) == 3                         # x needs 16 bytes
+    assert f(W, X, XQ + 8, Y, 64, 64, None) == 3                         # x_q8 needs 16 bytes
+    assert f(W, None, XQ, Y, 64, 64, None) == 1
+    assert f(W, X, XQ, X + 64, 64, 64, None) == 4                        # y overlaps x
+    assert f(W, X, W + 16, Y, 64, 64, None) == 4                         # x_q8 overlaps w_packed
+    assert f(W, XQ, XQ, Y, 64, 64, None) == 4                            # x overlaps x_q8
+    assert f(None, None, None, None, 0, 64, None) == 0
     assert L.q4s_requant_q8_0_to_q4_0(FAKE, FAKE + 64, 64, 64, None) == 4
     assert L.q4s_requant_q8_0_to_q4_0(None, FAKE, 64, 64, None) == 1
     assert L.q4s_requant_q8_0_to_q4_0(None, None, 0, 64, None) == 0

@@ -92,6 +92,24 @@ def test_gemv_q8_rows_independent_of_n_and_deterministic(rows, cols):
             assert np.array_equal(a[t], singles[t]), (n, t)
 
 
+@pytest.mark.parametrize("rows,cols", [(1536, 1536), (257, 1536), (64, 32), (130, 96), (70, 2048), (3, 1824),
+                                       (1, 288), (130, 4128), (100, 2304)])
+def test_gemv_q8_from_f32_equals_two_launches(oracle, rows, cols):
+    """q4s_gemv_q8_0_f32: one launch quantizing inside (cols <= 2048: every chunk count 1..8,
+    padding blocks, ragged row groups), or a quantize launch and the GEMV (wider): x_q8 equals
+    the oracle's quantizer byte for byte and y the two-launch form bit for bit."""
+    w8, x = _inputs(rows, cols, 1, tag=3)
+    wp = _packed(w8, rows, cols)
+    xq_fill = torch.full((q.q8_bytes(1, cols),), 0xA5, dtype=torch.uint8, device=dev())  # every byte written
+    y, xq = q.gemv_q8_0_f32(wp, to_dev(x), rows, cols, x_q8=xq_fill)
+    xq_two = q.quantize_q8_0(to_dev(x))
+    y_two = q.gemv_q8_0(wp, xq_two, rows, cols, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(q8_canonical(xq, 1, cols), oracle.quantize_q8_0(x))
+    assert torch.equal(xq, xq_two)                                   # padded d_x entries included
+    assert torch.equal(y, y_two)
+
+
 def test_gemv_q8_unit_weights_exact():
     # every weight 1 with d_w = 1, integer activations whose blocks hold +-127:
     # d_x = 1, q = x, so y = sum(x) exactly for every row
@@ -125,6 +143,22 @@ def test_gemv_q8_lm_head_full(oracle, n):
     x = synth.activation(n, cols, synth.generator(3, 196, 0, 1), outliers=0)
     y, y_ref, S, _ = _run(w8, x, rows, cols, n, oracle)
     assert_within(y, y_ref, S, what=f"q8 lm_head n={n}")
+
+
+def test_gemv_q8_from_f32_lm_head_full(oracle):
+    # the one-launch form at the benchmark's 151936 x 1536 head: against the oracle, and the
+    # two-launch form bit for bit
+    rows, cols = 151936, 1536
+    w8 = synth.q8_0_weights(rows, cols, synth.generator(3, 196, 0, 0))
+    x = synth.activation(1, cols, synth.generator(3, 196, 0, 1), outliers=0)
+    wp = _packed(w8, rows, cols)
+    y, xq = q.gemv_q8_0_f32(wp, to_dev(x), rows, cols)
+    y_two = q.gemv_q8_0(wp, q.quantize_q8_0(to_dev(x)), rows, cols, 1)
+    assert torch.equal(y, y_two)
+    xq_ref = oracle.quantize_q8_0(x)
+    assert np.array_equal(q8_canonical(xq, 1, cols), xq_ref)
+    y_ref, S = oracle.q8w_gemv(w8, xq_ref, rows, cols, 1)
+    assert_within(y.cpu().numpy(), y_ref, S, what="q8 lm_head from f32")
 
 
 # --------------------------------------------------------------- requant
