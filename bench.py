@@ -209,15 +209,15 @@ def run_q8_head(args, dev, stream) -> int:
         return lambda: q.gemv_q8_0(c["wp"], c["xq"], rows, cols, n, out=c["y"])
 
     if args.profile_only:
-        for c in copies:
-            step(c)()
+        for i in range(10):
+            step(copies[i % ncopies])()
         for i in range(10):
             gemv_only(copies[i % ncopies])()
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         q.bench_copy(src, dst)
         torch.cuda.synchronize()
-        log(f"profile run done: 10 Q8_0 GEMVs of {launch_bytes} algorithmic bytes, one 1 GiB copy")
+        log(f"profile run done: 10 Q8_0 steps and 10 GEMVs of {launch_bytes} algorithmic bytes, one 1 GiB copy")
         return 0
 
     ms = time_steps([step(c) for c in copies], args.steps, args.warmup, stream)
