@@ -581,7 +581,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic,
-                     "kernel": step_kernel if fused else "k_sweep (GEMV launch of the sweep)",
+                     "kernel": step_kernel if fused else ("k_sweep_one" if n == 1 else f"k_sweep<{n}>")
+                     + " (GEMV launch of the sweep)",
                      "algorithmic_bytes_per_launch": launch_bytes},
     }
 

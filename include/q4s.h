@@ -490,6 +490,19 @@ q4s_status q4s_bench_read(const void* buf, size_t bytes, int loads_in_flight, in
                           uint32_t* sink, void* stream);
 
 /*
+ * Streaming read in the GEMV's own pattern: wave i of the launch reads unit i,
+ * `unit_bytes` contiguous bytes (a positive multiple of 1024, at most 1 GiB),
+ * with 1 KB wave-wide loads (16 bytes per lane), nine in flight, one
+ * workgroup of 4 waves per 4 units; the floor(bytes / unit_bytes) whole units
+ * of `buf` (16-byte aligned) are read, a tail shorter than a unit is not.
+ * This is the achievable-bandwidth reference for the weight stream (the
+ * grid-stride q4s_bench_read puts its loads in flight at power-of-two
+ * strides, which some grid sizes serve far more slowly).  `sink` as for
+ * q4s_bench_read.
+ */
+q4s_status q4s_bench_read_units(const void* buf, size_t bytes, size_t unit_bytes, uint32_t* sink, void* stream);
+
+/*
  * Grid-barrier microbenchmark (the phase barriers of a chained decode step):
  * one persistent cooperative launch of n_workgroups x 256 threads (1..the
  * number resident at once, see below) that passes `phases` grid barriers.

@@ -104,6 +104,7 @@ def lib():
             "q4s_chain_set_trace": ([p, p, sz], i32),
             "q4s_chain_set_wait_limit": ([p, ctypes.c_uint32], i32),
             "q4s_bench_read": ([p, sz, i32, i32, p, p], i32),
+            "q4s_bench_read_units": ([p, sz, sz, p, p], i32),
             "q4s_bench_copy": ([p, p, sz, p], i32),
             "q4s_bench_grid_barrier": ([i32, i32, i32, p, sz, p], i32),
             "q4s_bench_grid_barrier_scratch_bytes": ([i32], sz),
@@ -456,6 +457,14 @@ def bench_read(buf: torch.Tensor, loads_in_flight: int = 4, n_blocks: int = 0,
     _check("q4s_bench_read", lib().q4s_bench_read(_dev(buf, "buf"), buf.numel() * buf.element_size(),
                                                    loads_in_flight, n_blocks, _dev(sink, "sink"),
                                                    _stream(buf.device)))
+
+
+def bench_read_units(buf: torch.Tensor, unit_bytes: int, sink: torch.Tensor | None = None) -> None:
+    """Read buf's whole units of unit_bytes (a multiple of 1024), one wave per unit."""
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check("q4s_bench_read_units", lib().q4s_bench_read_units(_dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                                               unit_bytes, _dev(sink, "sink"), _stream(buf.device)))
 
 
 def bench_copy(src: torch.Tensor, dst: torch.Tensor) -> None:

@@ -444,7 +444,8 @@ q4s_status q4s_sweep_plan_create(const q4s_mat* mats, int n_mats, int n, size_t*
         p->info.packed_bytes += (int64_t)packed_bytes(a.rows, a.cols);
         p->info.act_bytes += (int64_t)n * a.cols / 32 * 34;
         p->info.out_bytes += (int64_t)n * a.rows * 4;
-        if (p->split_tiles) {
+        // one workgroup per row group: the split kernels, and the single-split matrices of other 1-row sweeps
+        if (p->split_tiles || (n == 1 && m.ks == 1)) {
             for (int64_t gr = 0; gr < m.G; ++gr) tiles.push_back({(uint32_t)i, (uint32_t)gr, m.C * kChunkBytes});
             continue;
         }
@@ -880,6 +881,17 @@ q4s_status q4s_bench_read(const void* buf, size_t bytes, int loads_in_flight, in
     if ((s = check_ptr(sink, bytes ? 4 : 0, 4, "sink"))) return s;
     return hip_status(launch_bench_read(buf, bytes, loads_in_flight, n_blocks, sink, (hipStream_t)stream),
                       "bench_read launch");
+}
+
+q4s_status q4s_bench_read_units(const void* buf, size_t bytes, size_t unit_bytes, uint32_t* sink, void* stream) {
+    if (unit_bytes == 0 || unit_bytes % 1024 || unit_bytes > ((size_t)1 << 30))
+        return fail(Q4S_ERR_SHAPE, "unit_bytes must be a positive multiple of 1024, at most 1 GiB");
+    if (bytes / unit_bytes > ((size_t)1 << 33)) return fail(Q4S_ERR_SHAPE, "too many units");
+    q4s_status s;
+    if ((s = check_ptr(buf, bytes, 16, "buf"))) return s;
+    if ((s = check_ptr(sink, bytes ? 4 : 0, 4, "sink"))) return s;
+    return hip_status(launch_bench_read_units(buf, bytes, unit_bytes, sink, (hipStream_t)stream),
+                      "bench_read_units launch");
 }
 
 size_t q4s_bench_grid_barrier_scratch_bytes(int n_workgroups) {

@@ -80,13 +80,14 @@ constexpr int kQuantTileBlocks = 32;   // Q8_0 blocks per workgroup of the batch
 hipError_t launch_quantize_batch(const QuantDesc* dev_descs, const uint32_t* dev_tiles, int64_t n_tiles,
                                  hipStream_t st);
 hipError_t launch_gemv(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st);
+// Tiles are (matrix, group set) pairs; with n == 1 a single-split matrix's tiles are its row groups.
 hipError_t launch_sweep(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles,
                         int n, hipStream_t st);
 hipError_t launch_block_sums(const MatDesc& m, int n, int32_t* s, hipStream_t st);
-// The 1-row sweep with the activation quantized by the GEMV waves themselves.
 // 1-row sweeps whose matrices all have one K split: one 8-wave workgroup per (matrix, row group) entry.
 hipError_t launch_sweep_split(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles, bool fused,
                              hipStream_t st);
+// The 1-row sweep with the activation quantized by the GEMV waves themselves (tiles as launch_sweep's at n == 1).
 hipError_t launch_sweep_fused(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles,
                               hipStream_t st);
 // Q8_0 weights (q4s_q8w.hip).
@@ -111,6 +112,8 @@ hipError_t launch_grid_barrier(int kind, int n_wg, int phases, uint32_t* scratch
 hipError_t grid_barrier_max_workgroups(int* n);
 hipError_t launch_bench_read(const void* buf, size_t bytes, int lif, int n_blocks,
                              uint32_t* sink, hipStream_t st);
+// Reads floor(bytes / unit_bytes) whole units (unit_bytes a multiple of 1024) in the GEMV's wave pattern.
+hipError_t launch_bench_read_units(const void* buf, size_t bytes, size_t unit_bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 
 }  // namespace q4s

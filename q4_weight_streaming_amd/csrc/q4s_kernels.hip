@@ -360,25 +360,6 @@ __global__ __launch_bounds__(256) void k_quantize_batch(const QuantDesc* __restr
     quant_local(qd, lb, lb < total);
 }
 
-// ---------------------------------------------------------------- fused 1-row sweep
-//
-// With one activation row the sweep quantizes inside the GEMV launch (the
-// pages' mega kernel quantizes the activation once per step inside its single
-// kernel, milestone M15): every wave quantizes the chunks it streams (see
-// ActQuant), so the bytes -- and the results -- equal those of a separate
-// quantize launch, and the group-0 waves publish them to x_q8.
-__global__ __launch_bounds__(kThreads, 1) void k_sweep_fused(const MatDesc* __restrict__ mats,
-                                                            const uint32_t* __restrict__ tiles) {
-    __shared__ float red[kWaves * 64];
-    const uint32_t mi = tiles[2 * (size_t)blockIdx.x];
-    const uint32_t gs = tiles[2 * (size_t)blockIdx.x + 1];
-    const MatDesc m = mats[mi];
-    run_tile_with<1>(m, gs, red, [&](int g, int c0, int c1, float (&acc)[1]) {
-        ActQuant act{m, g == 0, {}};
-        wave_task<1>(m, g, c0, c1, acc, act);
-    });
-}
-
 // ---------------------------------------------------------------- 1-row split tiles
 //
 // A 1-row GEMV or sweep whose matrices all have one K split (C <= 8 chunks):
@@ -496,6 +477,57 @@ __global__ __launch_bounds__(64 * kW) void k_gemv_split(MatDesc m) {
     split_group<false, kW>(m, blockIdx.x, l);
 }
 
+// ---------------------------------------------------------------- fused 1-row sweep
+//
+// With one activation row the sweep quantizes inside the GEMV launch (the
+// pages' mega kernel quantizes the activation once per step inside its single
+// kernel, milestone M15): every wave quantizes the chunks it streams (see
+// ActQuant), so the bytes -- and the results -- equal those of a separate
+// quantize launch, and the group-0 waves publish them to x_q8.
+//
+// A tile entry names a row group of a single-split matrix (C <= 8), whose
+// chunks spread over the 4 waves as split tiles (split_group: exact block sums
+// in LDS, then chains A and B in the fixed order), or a group set of a
+// multi-split matrix (the ks waves of a row group stream contiguous chunk
+// ranges).  Short tiles matter at the end of the launch: with 4 row groups of 6
+// chunks per workgroup every wave streams 6 chunks in turn, and the last
+// workgroups leave HBM under-fed while they finish (a replay of this tile plan
+// as plain reads took 133 us with a fixed per-chunk delay, 124 us with one row
+// group per workgroup).
+union FusedLds {
+    SplitLds split;
+    float red[kWaves * 64];
+};
+
+template <bool kFused>
+__device__ __forceinline__ void sweep_row1(const MatDesc& m, uint32_t t, FusedLds& l) {
+    if (m.ks == 1) {
+        split_group<kFused, kWaves>(m, (int)t, l.split);
+        return;
+    }
+    if constexpr (kFused) {
+        run_tile_with<1>(m, t, l.red, [&](int g, int c0, int c1, float (&acc)[1]) {
+            ActQuant act{m, g == 0, {}};
+            wave_task<1>(m, g, c0, c1, acc, act);
+        });
+    } else {
+        run_tile<1>(m, t, l.red);
+    }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_sweep_fused(const MatDesc* __restrict__ mats,
+                                                            const uint32_t* __restrict__ tiles) {
+    __shared__ FusedLds l;
+    sweep_row1<true>(mats[tiles[2 * (size_t)blockIdx.x]], tiles[2 * (size_t)blockIdx.x + 1], l);
+}
+
+// The same tiles over activations quantized beforehand.
+__global__ __launch_bounds__(kThreads, 1) void k_sweep_one(const MatDesc* __restrict__ mats,
+                                                          const uint32_t* __restrict__ tiles) {
+    __shared__ FusedLds l;
+    sweep_row1<false>(mats[tiles[2 * (size_t)blockIdx.x]], tiles[2 * (size_t)blockIdx.x + 1], l);
+}
+
 // ---------------------------------------------------------------- measurement
 
 template <int L>
@@ -512,6 +544,30 @@ __global__ __launch_bounds__(256) void k_bench_read(const u32x4* __restrict__ bu
         for (int k = 0; k < L; ++k) acc ^= v[k];
     }
     for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(buf + i);
+    const uint32_t h = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (h == 0x9E3779B9u && acc.x == 0x7F4A7C15u) sink[0] = h;  // practically never
+}
+
+// The GEMV's read pattern without its arithmetic: wave i of the launch reads
+// unit i (unit_kb contiguous KB) with 1 KB wave loads, 9 in flight (one chunk's
+// worth), one workgroup of 4 waves per 4 units.
+__global__ __launch_bounds__(256) void k_bench_read_units(const u32x4* __restrict__ buf, int64_t n_units,
+                                                          int64_t unit_kb, uint32_t* __restrict__ sink) {
+    const int lane = threadIdx.x & 63;
+    const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    if (u < n_units) {
+        const u32x4* p = buf + u * unit_kb * 64 + lane;
+        int64_t i = 0;
+        for (; i + 9 <= unit_kb; i += 9) {
+            u32x4 v[9];
+#pragma unroll
+            for (int k = 0; k < 9; ++k) v[k] = __builtin_nontemporal_load(p + (i + k) * 64);
+#pragma unroll
+            for (int k = 0; k < 9; ++k) acc ^= v[k];
+        }
+        for (; i < unit_kb; ++i) acc ^= __builtin_nontemporal_load(p + i * 64);
+    }
     const uint32_t h = acc.x ^ acc.y ^ acc.z ^ acc.w;
     if (h == 0x9E3779B9u && acc.x == 0x7F4A7C15u) sink[0] = h;  // practically never
 }
@@ -596,7 +652,9 @@ hipError_t launch_sweep(const MatDesc* dev_mats, const uint32_t* dev_tiles, int6
         return hipGetLastError();
     }
     switch (n) {
-        case 1: sweep_n<1>(dev_mats, dev_tiles, n_tiles, st); break;
+        case 1:  // tiles of single-split matrices are row groups (split tiles)
+            hipLaunchKernelGGL(k_sweep_one, dim3((unsigned)n_tiles), dim3(kThreads), 0, st, dev_mats, dev_tiles);
+            break;
         case 2: sweep_n<2>(dev_mats, dev_tiles, n_tiles, st); break;
         case 3: sweep_n<3>(dev_mats, dev_tiles, n_tiles, st); break;
         case 4: sweep_n<4>(dev_mats, dev_tiles, n_tiles, st); break;
@@ -673,6 +731,15 @@ hipError_t launch_bench_read(const void* buf, size_t bytes, int lif, int n_block
         case 8: hipLaunchKernelGGL(k_bench_read<8>, dim3(n_blocks), dim3(256), 0, st, p, n16, sink); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_bench_read_units(const void* buf, size_t bytes, size_t unit_bytes, uint32_t* sink, hipStream_t st) {
+    const int64_t unit_kb = (int64_t)(unit_bytes / 1024);
+    const int64_t n_units = unit_kb > 0 ? (int64_t)(bytes / unit_bytes) : 0;  // whole units only
+    if (n_units == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_bench_read_units, dim3((unsigned)((n_units + 3) / 4)), dim3(256), 0, st, (const u32x4*)buf,
+                       n_units, unit_kb, sink);
     return hipGetLastError();
 }
 

@@ -7,12 +7,16 @@ method of the minfer README, milestone M15: one launch over a large buffer,
 several 16-byte loads in flight per thread).  A plain copy is timed as well.
 
   python -m q4_weight_streaming_amd.roofline [--gib 4] [--reps 5]
-  python -m q4_weight_streaming_amd.roofline --sizes 131,868 [--reps 20]
+  python -m q4_weight_streaming_amd.roofline --sizes 131,868 [--reps 20] [--wg 2048,4096] [--lif 4,8]
 
 --sizes times reads of the sizes the GEMV streams (MB, e.g. the 1.5B output head
 and the whole 1.5B sweep) the way the benchmark times its steps: launches back to
 back, four rotated buffers (past the Infinity Cache), over a small grid of loads
-in flight and workgroups.
+in flight and workgroups, and in the GEMV's own pattern (q4s_bench_read_units:
+each wave streams one contiguous unit -- a 9216-byte chunk, a row group of 6 or
+9 chunks -- with 1 KB wave loads).  The unit pattern is the reference: the
+grid-stride kernel's loads in flight sit a power-of-two stride apart, which
+some grid sizes serve far more slowly.
 """
 from __future__ import annotations
 
@@ -29,9 +33,12 @@ def main() -> int:
     ap.add_argument("--gib", type=float, default=4.0)
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--sizes", default="", help="comma-separated MB: back-to-back reads of these sizes")
+    ap.add_argument("--wg", default="2048,4096,8192,16384", help="workgroup counts for --sizes")
+    ap.add_argument("--lif", default="4,8", help="loads in flight (1, 2, 4 or 8) for --sizes")
     args = ap.parse_args()
     if args.sizes:
-        return by_size([int(v) for v in args.sizes.split(",")], max(args.reps, 10))
+        return by_size([int(v) for v in args.sizes.split(",")], max(args.reps, 10),
+                       [int(v) for v in args.wg.split(",")], [int(v) for v in args.lif.split(",")])
 
     import torch
 
@@ -73,7 +80,7 @@ def main() -> int:
     return 0
 
 
-def by_size(sizes_mb, reps) -> int:
+def by_size(sizes_mb, reps, wgs, lifs) -> int:
     import torch
 
     from q4_weight_streaming_amd import _lib as q
@@ -85,8 +92,8 @@ def by_size(sizes_mb, reps) -> int:
         n = mb * 1000 * 1000 // 16 * 16
         bufs = [torch.ones(n, dtype=torch.uint8, device=dev) for _ in range(4)]
         rows = []
-        for lif in (4, 8):
-            for blocks in (2048, 4096, 8192, 16384):
+        for lif in lifs:
+            for blocks in wgs:
                 for i in range(3):
                     q.bench_read(bufs[i % 4], lif, blocks, sink)
                 torch.cuda.synchronize()
@@ -101,8 +108,24 @@ def by_size(sizes_mb, reps) -> int:
                              "gb_s": round(n / us / 1e3, 1)})
                 print(f"{mb} MB L={lif} wg={blocks:6d}: {us:7.1f} us {n / us / 1e3:8.1f} GB/s", file=sys.stderr,
                       flush=True)
+        units = []
+        for ub in (9216, 6 * 9216, 9 * 9216):
+            nb = n // ub * ub
+            for i in range(3):
+                q.bench_read_units(bufs[i % 4], ub, sink)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(reps):
+                q.bench_read_units(bufs[i % 4], ub, sink)
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / reps
+            units.append({"unit_bytes": ub, "bytes_read": nb, "us": round(us, 2), "gb_s": round(nb / us / 1e3, 1)})
+            print(f"{mb} MB units of {ub} B: {us:7.1f} us {nb / us / 1e3:8.1f} GB/s", file=sys.stderr, flush=True)
         best = max(rows, key=lambda r: r["gb_s"])
-        out.append({"mb": mb, "bytes": n, "best": best, "grid": rows})
+        out.append({"mb": mb, "bytes": n, "best": best, "grid": rows, "units": units,
+                    "best_units": max(units, key=lambda r: r["gb_s"])})
         del bufs
     print(json.dumps({"back_to_back_reads": out}))
     return 0

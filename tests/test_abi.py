@@ -83,6 +83,10 @@ def test_other_entry_points_validate(L):
     assert L.q4s_bench_read(FAKE, 24, 4, 0, FAKE + (1 << 30), None) == 2
     assert L.q4s_bench_read(FAKE, 32, 3, 0, FAKE + (1 << 30), None) == 2
     assert L.q4s_bench_copy(FAKE, FAKE + 16, 64, None) == 4
+    assert L.q4s_bench_read_units(FAKE, 1 << 20, 1000, FAKE + (1 << 30), None) == 2   # unit not a multiple of 1 KB
+    assert L.q4s_bench_read_units(FAKE, 1 << 20, 0, FAKE + (1 << 30), None) == 2
+    assert L.q4s_bench_read_units(FAKE + 4, 1 << 20, 9216, FAKE + (1 << 30), None) == 3
+    assert L.q4s_bench_read_units(None, 0, 9216, None, None) == 0                      # nothing to read
     assert L.q4s_sweep_run(None, None) == 1
     assert L.q4s_bench_grid_barrier(0, 4, 0, FAKE, 1 << 20, None) == 2      # phases >= 1
     assert L.q4s_bench_grid_barrier(10, 4, 10, FAKE, 1 << 20, None) == 2     # unknown kind
@@ -154,10 +158,23 @@ def test_sweep_plan_host_side(L):
     d = info.as_dict()
     assert d["n_mats"] == 197
     assert d["weight_bytes"] == 868_257_792 == d["packed_bytes"]
-    # group sets: q,o 6; k,v 1; gate,up 35; down 24 (4-way K split) per layer; lm_head 594
-    assert d["n_tiles"] == 28 * (6 + 1 + 1 + 6 + 35 + 35 + 24) + 594
+    # at n = 1 a single-split matrix (at most 8 chunks) has one tile per row group: q,o 24; k,v 4;
+    # gate,up 140; down 24 group sets of one row group (4-way K split) per layer; lm_head 2374
+    assert d["n_tiles"] == 28 * (24 + 4 + 4 + 24 + 140 + 140 + 24) + 2374
     assert d["n_quant_blocks"] == 0 and d["dev_bytes"] == need and d["fused_quantize"] == 0
     assert d["out_bytes"] == 4 * sum(s.rows for s in shapes)
+    L.q4s_sweep_plan_destroy(plan)
+    # at n = 2 every tile is a group set: q,o 6; k,v 1; gate,up 35; down 24 per layer; lm_head 594
+    mats2, base2 = [], base
+    for s in shapes:
+        w = base2; base2 += (q.packed_bytes(s.rows, s.cols) + 4095) // 4096 * 4096
+        x = base2; base2 += (q.q8_bytes(2, s.cols) + 4095) // 4096 * 4096
+        y = base2; base2 += (8 * s.rows + 4095) // 4096 * 4096
+        mats2.append((w, None, x, y, s.rows, s.cols))
+    st, plan, _ = _plan(L, mats2, 2)
+    assert st == 0, _err(L)
+    assert L.q4s_sweep_plan_info(plan, ctypes.byref(info)) == 0
+    assert info.n_tiles == 28 * (6 + 1 + 1 + 6 + 35 + 35 + 24) + 594
     L.q4s_sweep_plan_destroy(plan)
     # with fp32 activations at n = 1 the plan quantizes inside the GEMV launch
     fx = base
