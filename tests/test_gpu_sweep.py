@@ -69,7 +69,7 @@ def test_sweep_fused_quantize_equals_two_launches(oracle):
     require_gpu()
     shapes = [synth.MatShape("a", 257, 1536), synth.MatShape("b", 64, 8960), synth.MatShape("c", 1, 32),
               synth.MatShape("d", 130, 4128), synth.MatShape("e", 90, 96), synth.MatShape("f", 70, 18944),
-              synth.MatShape("g", 3, 33792)]
+              synth.MatShape("g", 3, 33792), synth.MatShape("h", 200, 3072)]
     _, hx, mats = _stack(78, shapes, 1)
     for m in mats:
         m["x_q8"].fill_(0xA5)                                # every byte must be written
@@ -86,6 +86,49 @@ def test_sweep_fused_quantize_equals_two_launches(oracle):
                               oracle.quantize_q8_0(x)[0, :, 2:].reshape(-1))
         y = q.gemv_q4_0(m["w_packed"], xq, m["rows"], m["cols"], 1)
         assert torch.equal(y, m["y"])
+
+
+def _one_row_tiles(shapes):
+    """Tiles of a 1-row plan: a row group each for matrices of at most 8 chunks, else group sets."""
+    n = 0
+    for sh in shapes:
+        if sh.rows == 0 or sh.cols == 0:
+            continue
+        g, c = -(-sh.rows // 64), -(-(sh.cols // 32) // 8)
+        ks = 1 if c <= 8 else (2 if c <= 16 else 4)
+        n += g if ks == 1 else -(-g // (4 // ks))
+    return n
+
+
+def test_sweep_one_row_prequantized_mixed_equals_standalone(oracle):
+    # n = 1 over activations quantized by the sweep's own quantize launch (one matrix brings its
+    # x_q8 already quantized, so the plan is not fused): matrices of at most 8 chunks run as
+    # split tiles, the others (2 and 4 K splits) as group sets, in one GEMV launch; every y
+    # equals the standalone GEMV bit for bit
+    require_gpu()
+    shapes = [synth.MatShape("a", 257, 1536), synth.MatShape("b", 64, 8960), synth.MatShape("c", 1, 32),
+              synth.MatShape("d", 130, 4128), synth.MatShape("e", 90, 96), synth.MatShape("f", 200, 3072),
+              synth.MatShape("g", 3, 33792), synth.MatShape("h", 65, 2048)]
+    hw, hx, mats = _stack(80, shapes, 1)
+    mats[7]["x_q8"] = q.quantize_q8_0(mats[7].pop("x"))
+    for m in mats:
+        m["y"].fill_(float("nan"))
+    sw = q.Sweep(mats, 1)
+    info = sw.info()
+    assert info["fused_quantize"] == 0
+    assert info["n_tiles"] == _one_row_tiles(shapes)
+    sw.run()
+    sw.run()
+    torch.cuda.synchronize()
+    for m, x, sh in zip(mats, hx, shapes):
+        xq = q.quantize_q8_0(to_dev(x))
+        assert torch.equal(xq, m["x_q8"]), sh.name
+        y = q.gemv_q4_0(m["w_packed"], xq, m["rows"], m["cols"], 1)
+        assert torch.equal(y, m["y"]), sh.name
+    # and against the oracle's fixed-order GEMV for one single-split and one split-K matrix
+    for i in (0, 5):
+        y_ref, S = oracle.gemv(hw[i], oracle.quantize_q8_0(hx[i]), shapes[i].rows, shapes[i].cols, 1)
+        assert_within(mats[i]["y"].cpu().numpy(), y_ref, S, what=shapes[i].name)
 
 
 def test_sweep_not_fused_with_a_prequantized_activation():
