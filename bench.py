@@ -2,14 +2,20 @@
 """Benchmark: Q4_0 x Q8_0 weight-streaming GEMV sweep on one MI355X.
 
 A step is one pass of the whole hot path over one decode token's projections:
-one launch quantizes every matrix's fresh fp32 activation to Q8_0, one launch
-streams every Q4_0 matrix once and writes every output.  Weights are synthetic,
-seeded, Qwen2.5-shaped; consecutive steps alternate between seeded copies of the
-weight set so no step finds the previous step's bytes in the 256 MB Infinity
-Cache.  Prints one JSON line.
+every matrix's fresh fp32 activation quantized to Q8_0 and every Q4_0 matrix
+streamed once with its output written -- one launch at N=1 (the GEMV waves
+quantize what they stream), a quantize launch and a GEMV launch at N >= 2.
+Weights are synthetic, seeded, Qwen2.5-shaped; consecutive steps alternate
+between seeded copies of the weight set so no step finds the previous step's
+bytes in the 256 MB Infinity Cache.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload qwen2.5-1.5b|qwen2.5-7b|lm_head] [--n N]
+  python bench.py [--steps K] [--warmup W] [--workload qwen2.5-1.5b|qwen2.5-7b|lm_head|gemv1536] [--n N]
+  python bench.py --workload lm_head_q8|attn [...]
   python bench.py --workload chain [--chain-model 1.5b|7b] [--sync all|tagged|tree|counter]
+
+gemv1536 is the single 1536x1536 GEMV: 405 seeded copies (537 MB, past the
+Infinity Cache) as one sweep launch, plus each GEMV as its own launch
+bracketed by events (latency-bound: ~1.3 MB per launch).
 """
 from __future__ import annotations
 
@@ -50,6 +56,8 @@ def workload_shapes(name: str):
         return synth.qwen25_7b(), 4, 1
     if name == "lm_head":
         return [synth.MatShape("lm_head", 151936, 1536)], 2, 4
+    if name == "gemv1536":
+        return [synth.MatShape(f"w{i}", 1536, 1536) for i in range(405)], 0, 1
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -472,7 +480,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen2.5-1.5b",
-                    choices=["qwen2.5-1.5b", "qwen2.5-7b", "lm_head", "lm_head_q8", "attn", "chain"])
+                    choices=["qwen2.5-1.5b", "qwen2.5-7b", "lm_head", "gemv1536", "lm_head_q8", "attn", "chain"])
     ap.add_argument("--chain-model", default="1.5b", choices=["1.5b", "7b"], help="stack of --workload chain")
     ap.add_argument("--sync", default="all", choices=["all", *CHAIN_MODES], help="phase sync of --workload chain")
     ap.add_argument("--chain-workgroups", type=int, default=0, help="persistent workgroups (0: one per CU)")
@@ -606,6 +614,23 @@ def main() -> int:
             log(f"n={nv} step {msv * 1e3:.1f} us, ratio {msv / ms:.3f}")
             del plans
         out["verify"] = verify
+
+    if args.workload == "gemv1536":
+        # each GEMV as its own launch over its quantized activation, bracketed by events on the stream
+        m0 = copies[0]
+        outs = [torch.empty((n, s.rows), dtype=torch.float32, device=dev) for s in shapes]
+        fns = [lambda mm=mm, o=o: q.gemv_q4_0(mm["w_packed"], mm["x_q8"], mm["rows"], mm["cols"], n, out=o)
+               for mm, o in zip(m0, outs)]
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        s_avg, s_med, s_min = time_kernel(fns, len(fns), stream)
+        per = shapes[0].rows * (shapes[0].cols // 32) * 18
+        out["single_gemv"] = {"launches": len(fns), "us_bracketed_avg": round(s_avg * 1e3, 2),
+                              "us_bracketed_median": round(s_med * 1e3, 2), "us_bracketed_min": round(s_min * 1e3, 2),
+                              "weight_gb_s_at_median": round(per / (s_med * 1e-3) / 1e9, 1),
+                              "note": "one 1536x1536 GEMV per launch; the bracket holds the dispatch latency"}
+        log(f"single GEMV launch: median {s_med * 1e3:.2f} us, min {s_min * 1e3:.2f} us")
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(host0, shapes, n, args.cpu_budget)
