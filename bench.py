@@ -582,7 +582,7 @@ def main() -> int:
                    "launches_per_step": 1 if fused else 2, "quantize": "fused" if fused else "own launch",
                    "accumulate": "f32", "gemv_tiles": info["n_tiles"]},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
-        "tok_s": round(1000.0 / ms, 1) if n == 1 else None,
+        "tok_s": round(1000.0 / ms, 1) if n == 1 and args.workload.startswith("qwen") else None,
         "gemv_only": {"us_back_to_back": round(k_b2b * 1e3, 2), "us_bracketed_avg": round(k_avg * 1e3, 2),
                       "us_bracketed_median": round(k_med * 1e3, 2), "us_bracketed_min": round(k_min * 1e3, 2),
                       "weight_gb_s": round(weight_bytes / (k_b2b * 1e-3) / 1e9, 1)},
