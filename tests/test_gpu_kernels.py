@@ -236,3 +236,15 @@ def test_gemv_empty_and_zero_width():
     q.gemv_q4_0(wp, xq, 40, 0, 20, out=y)                      # and on the wide path
     assert (y == 0).all()
     q.gemv_q4_0(wp, xq, 0, 64, 1, out=torch.empty((1, 0), device=dev()))   # no rows: no-op
+
+
+def test_measurement_reads_stay_in_their_buffers():
+    # the read benchmarks (no outputs besides the sink): whole units only, a tail shorter than a
+    # unit untouched; each returns cleanly and leaves the sink as it was
+    sink = torch.zeros(4, dtype=torch.int32, device=dev())
+    buf = torch.ones(3 * 9216 + 5000, dtype=torch.uint8, device=dev())
+    q.bench_read_units(buf, 9216, sink)
+    q.bench_read_units(buf, 55296, sink)                       # no whole unit: nothing to read
+    q.bench_read(buf[: (buf.numel() // 16) * 16], 4, 8, sink)
+    torch.cuda.synchronize()
+    assert (sink == 0).all()
