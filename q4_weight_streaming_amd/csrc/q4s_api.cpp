@@ -556,8 +556,11 @@ struct q4s_chain {
     // within the Q8_0 area, or -1
     std::vector<int64_t> q8_out, q8_in;
     size_t q8_bytes = 0;
-    // device image: [ChainMat x n][tiles][phase_end][sync words][Q8_0 words], 16-byte aligned parts
-    size_t off_tiles = 0, off_phase = 0, off_sync = 0, off_q8 = 0, dev_bytes = 0;
+    // per matrix: byte offset of its K-range words (see ChainMat::kpart) within that area, or -1
+    std::vector<int64_t> kp_off;
+    size_t kp_bytes = 0;
+    // device image: [ChainMat x n][tiles][phase_end][sync words][Q8_0 words][K-range words], 16-byte aligned
+    size_t off_tiles = 0, off_phase = 0, off_sync = 0, off_q8 = 0, off_kp = 0, dev_bytes = 0;
     std::vector<uint8_t> image;
     uint8_t* dev = nullptr;
     uint32_t gen = 0;
@@ -570,8 +573,11 @@ struct q4s_chain {
 // whose tile count fits the workgroups: one row group per tile with its chunks
 // spread over the 4 waves (matrices with one or two K splits), or two row
 // groups per tile with two waves each (one K split); else a group set per tile
-// (one wave per row group, or per K range).  The device image keeps room for the
-// largest table (one tile per row group).
+// (one wave per row group, or per K range).  With tagged phases a phase whose
+// one matrix has K-range words (four K splits of <= 16 chunks: down) runs one
+// tile per (K range, row group) instead, ranges 1..3 first and range 0 last,
+// whatever the workgroup count.  The device image keeps room for the largest
+// table (one tile per row group, or per K range and row group).
 static void chain_layout(q4s_chain* p, int wg) {
     struct Tile { uint32_t mat, word; int64_t bytes; };
     p->tiles.clear();
@@ -587,6 +593,20 @@ static void chain_layout(q4s_chain* p, int wg) {
             splittable = splittable && p->mats[i].m.ks <= 2;  // <= 16 chunks
             narrow = narrow && p->mats[i].m.ks == 1;          // <= 8 chunks
             paired = paired || p->mats[i].w2 != nullptr;      // only with ks <= 2
+        }
+        if (members.size() == 1 && p->kp_off[members[0]] >= 0) {
+            const uint32_t i = members[0];
+            const MatDesc& m = p->mats[i].m;
+            max_tiles += m.G * m.ks;
+            for (int sp = 1; sp <= m.ks; ++sp) {
+                const int r = sp % m.ks;  // ranges 1 .. ks-1, then 0
+                for (int64_t g = 0; g < m.G; ++g) {
+                    p->tiles.push_back(i);
+                    p->tiles.push_back((uint32_t)(r * m.G + g) | kChainRange);
+                }
+            }
+            p->phase_end.push_back((uint32_t)(p->tiles.size() / 2));
+            continue;
         }
         max_tiles += groups;
         const uint32_t mode = !splittable                               ? 0u
@@ -615,7 +635,8 @@ static void chain_layout(q4s_chain* p, int wg) {
     p->off_phase = p->off_tiles + up16((size_t)max_tiles * 2 * sizeof(uint32_t));
     p->off_sync = p->off_phase + up16(p->phase_end.size() * sizeof(uint32_t));
     p->off_q8 = p->off_sync + up16(kChainSyncWords * sizeof(uint32_t));
-    p->dev_bytes = p->off_q8 + up16(p->q8_bytes);
+    p->off_kp = p->off_q8 + up16(p->q8_bytes);
+    p->dev_bytes = p->off_kp + up16(p->kp_bytes);
     p->image.assign(p->dev_bytes, 0);
     memcpy(p->image.data(), p->mats.data(), p->mats.size() * sizeof(ChainMat));
     memcpy(p->image.data() + p->off_tiles, p->tiles.data(), p->tiles.size() * sizeof(uint32_t));
@@ -695,6 +716,7 @@ q4s_status q4s_chain_create(const q4s_chain_shape* shape, const void* const* w_p
         p->mats.push_back(cm);
         p->q8_out.push_back(-1);
         p->q8_in.push_back(-1);
+        p->kp_off.push_back(-1);
     };
     auto close = [&]() {
         p->phases.push_back(members);
@@ -748,6 +770,11 @@ q4s_status q4s_chain_create(const q4s_chain_shape* shape, const void* const* w_p
             cm.y = word(l, odn), cm.res = word(l, oh1), cm.y2 = word(l, oh2);
             add(cm);
             if (pair) p->q8_in.back() = q8_at;
+            // with tagged phases, four K splits of <= 16 chunks each run as K-range tiles
+            if (sync_mode == Q4S_CHAIN_TAGGED && cm.m.ks == 4 && cm.m.C <= 4 * kChainRangeChunks) {
+                p->kp_off.back() = (int64_t)p->kp_bytes;
+                p->kp_bytes += (size_t)(cm.m.ks - 1) * (size_t)cm.m.G * 64 * 8;
+            }
         }
         close();
     }
@@ -786,12 +813,13 @@ q4s_status q4s_chain_upload(q4s_chain* p, void* dev_mem, size_t dev_bytes, void*
     if (wg < 1 || wg > max_wg)
         return fail(Q4S_ERR_SHAPE, "workgroups=%d out of [1, %d] (all must be resident at once)", wg, max_wg);
     if (wg != p->layout_wg) chain_layout(p, wg);
-    // the Q8_0 product words live in dev_mem: point the matrices' copies in the image at them
-    // (the area itself is uploaded as zeros: tag 0, never written)
+    // the Q8_0 product words and the K-range words live in dev_mem: point the matrices' copies in
+    // the image at them (the areas themselves are uploaded as zeros: tag 0, never written)
     for (size_t i = 0; i < p->mats.size(); ++i) {
         ChainMat* cm = (ChainMat*)p->image.data() + i;
         if (p->q8_out[i] >= 0) cm->yq = (uint64_t*)((uint8_t*)dev_mem + p->off_q8 + p->q8_out[i]);
         if (p->q8_in[i] >= 0) cm->xq = (const uint64_t*)((uint8_t*)dev_mem + p->off_q8 + p->q8_in[i]);
+        if (p->kp_off[i] >= 0) cm->kpart = (uint64_t*)((uint8_t*)dev_mem + p->off_kp + p->kp_off[i]);
     }
     hipStream_t st = (hipStream_t)stream;
     if ((e = hipMemcpyAsync(dev_mem, p->image.data(), p->dev_bytes, hipMemcpyHostToDevice, st)) != hipSuccess)

@@ -30,6 +30,7 @@ struct ChainMat {
     const uint8_t* w2;    // paired: the second matrix's packed weights, else NULL
     uint64_t* y_b;        // paired: tagged output of the second matrix [rows]
     uint64_t* yq;         // tagged Q8_0 words of y * y_b (paired) or of y (q, for o), or NULL
+    uint64_t* kpart;      // K-range tiles: tagged fp32 results of K ranges 1..3 [range - 1][G][64], or NULL
     int32_t norm;         // RMS-normalize the activation before quantizing it
     int32_t x_plain, res_plain, pad_;
 };
@@ -53,12 +54,17 @@ constexpr int kChainSyncWords = 32 * 18;
 // The chained decode step (one cooperative launch; grid = resident workgroups).
 hipError_t launch_chain(int sync_mode, const ChainParams& p, int workgroups, uint32_t spin_limit, hipStream_t st);
 constexpr uint32_t kChainDefaultSpin = 1u << 20;
-// Tile word: the tile index in bits 0-29; bit 31: one row group whose chunks
-// are spread over the 4 waves; bit 30: two row groups, two waves each; neither:
-// a group set (one wave per row group, or per K range).
+// Tile word: the tile index in bits 0-28; bit 31: one row group whose chunks
+// are spread over the 4 waves; bit 30: two row groups, two waves each; bit 29:
+// one K range of one row group (index = range * G + group) of a matrix with
+// four K splits of at most 16 chunks, its chunks spread over the 4 waves, the
+// ranges meeting through kpart (tagged phases only); none: a group set (one
+// wave per row group, or per K range).
 constexpr uint32_t kChainSplit4 = 1u << 31;
 constexpr uint32_t kChainSplit2 = 1u << 30;
-constexpr uint32_t kChainTileIndex = kChainSplit2 - 1;
+constexpr uint32_t kChainRange = 1u << 29;
+constexpr uint32_t kChainTileIndex = kChainRange - 1;
+constexpr int kChainRangeChunks = 16;  // a K-range tile's chunks (its term table)
 hipError_t chain_max_workgroups(int sync_mode, int* n);
 
 }  // namespace q4s

@@ -527,12 +527,16 @@ __device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, flo
 // tile, with 1/wpg of the serial work per wave.
 constexpr int kChainSplitChunks = 16;  // chunks of a matrix with ks <= 2
 constexpr int kChainTermWords = kChainSplitChunks * kChunkBlocks * 64;  // one group's term table
+static_assert(kChainRangeChunks <= kChainSplitChunks, "a K-range tile's chunks fit the term table");
+static_assert(kChainRangeChunks <= kSegChunks, "a K-range tile's chunks are one segment");
 
 template <int kWpg>
 __device__ __forceinline__ int split_first(int w, int C) { return (w * C + kWpg - 1) / kWpg; }
 
+// Chunk c's exact block sums and binary16 d_w into entry tc of the term table.
 template <int kSync>
-__device__ __forceinline__ void chunk_terms(int c, const Chunk& ch, ActStaged<kSync>& act, Q4S_LDS uint32_t* terms) {
+__device__ __forceinline__ void chunk_terms(int c, int tc, const Chunk& ch, ActStaged<kSync>& act,
+                                            Q4S_LDS uint32_t* terms) {
     const int lane = threadIdx.x & 63;
     const auto pr = act.prepare(0, c);
     uint32_t y[4];
@@ -549,7 +553,7 @@ __device__ __forceinline__ void chunk_terms(int c, const Chunk& ch, ActStaged<kS
             const int b = 4 * h + x;
             const uint32_t sw = ch.scale[b >> 1];
             const uint32_t dw_bits = (b & 1) ? (sw >> 16) : (sw & 0xffffu);
-            terms[(c * kChunkBlocks + b) * 64 + lane] = (uint32_t)(uint16_t)(int16_t)(s16[x] >> 4) | (dw_bits << 16);
+            terms[(tc * kChunkBlocks + b) * 64 + lane] = (uint32_t)(uint16_t)(int16_t)(s16[x] >> 4) | (dw_bits << 16);
         }
     }
 }
@@ -584,10 +588,10 @@ __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t til
         load_chunk(a, wp);
         if (i0 + 1 < i1) load_chunk(b, wp + kChunkBytes);
         for (int c = i0; c < i1; c += 2) {
-            chunk_terms<kSync>(c, a, act, gterms);
+            chunk_terms<kSync>(c, c, a, act, gterms);
             if (c + 2 < i1) load_chunk(a, wp + (size_t)(c + 2 - i0) * kChunkBytes);
             if (c + 1 < i1) {
-                chunk_terms<kSync>(c + 1, b, act, gterms);
+                chunk_terms<kSync>(c + 1, c + 1, b, act, gterms);
                 if (c + 3 < i1) load_chunk(b, wp + (size_t)(c + 3 - i0) * kChunkBytes);
             }
         }
@@ -633,6 +637,101 @@ __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t til
     if (row >= m.rows) return;
     uint64_t* y = half ? cm.y_b : cm.y;
     if (y) chain_st<kSync>(y + row, tag_word(v, gen));
+    if (cm.yf) gwr<float>(cm.yf)[row] = v;
+    if (cm.res) {
+        const float r = cm.res_plain ? ((const float*)cm.res)[row]
+                                     : chain_value<kSync>((const uint64_t*)cm.res + row, rword, gen, err);
+        chain_st<kSync>(cm.y2 + row, tag_word(r + v, gen));
+    }
+}
+
+// One K range of one row group of a matrix with four K splits (ranges of at most
+// kChainRangeChunks chunks) on its own workgroup, with tagged phases: the
+// range's chunks are spread over the 4 waves as in chain_tile_split (exact
+// block sums and d_w in the term table), waves 0 and 1 run the range's
+// fixed-order chains A and B (one segment) and wave 0 forms 0 + (A + B), as the
+// one-wave-per-range tile does.  Ranges 1..3 store that value as tagged words in kpart; range 0, whose
+// tiles come last in the phase's table (so a workgroup never waits on a tile it
+// has yet to run), polls them and adds the ranges in order -- ((r0 + r1) + r2)
+// + r3, the group set's order -- then runs the epilogue.  So the result is
+// bit-identical to the group-set tile, with the row group's chunks on 16 waves
+// instead of 4.
+template <int kSync>
+__device__ __forceinline__ void chain_tile_range(const ChainMat& cm, int64_t idx, float* red, Q4S_LDS u32x2* stage,
+                                                 Q4S_LDS uint32_t* terms, StageKey& key, int phase, uint32_t gen,
+                                                 uint32_t* err, uint64_t* mark_start, uint64_t* mark_ready) {
+    if (mark_start && threadIdx.x == 0) gwr<uint64_t>(mark_start)[0] = __builtin_amdgcn_s_memrealtime();
+    const int wave = wave_uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const MatDesc& m = cm.m;
+    const int64_t G = m.G;
+    const int64_t g = idx % G;
+    const int sp = (int)(idx / G);
+    const int ks = m.ks;
+    const int c0 = (int)((int64_t)sp * m.C / ks), c1 = (int)((int64_t)(sp + 1) * m.C / ks);
+    const int n = c1 - c0;
+    const int64_t row = g * kGroupRows + lane;
+    const int64_t rrow = min(row, (int64_t)m.rows - 1);
+    uint64_t rword = 0;
+    if (cm.res && !cm.res_plain && sp == 0 && wave == 0) rword = chain_ld<kSync>((const uint64_t*)cm.res + rrow);
+    // integer work of this wave's chunks of the range
+    const int i0 = c0 + split_first<4>(wave, n), i1 = c0 + split_first<4>(wave + 1, n);
+    if (i0 < i1) {
+        Q4S_LDS u32x2* slice = stage + wave * (kChainMaxChunks * 64);
+        ActStaged<kSync> act{cm, m.w, g, i0, i1, gen, err, slice, key, phase, false, wave == 0 ? mark_ready : nullptr};
+        const uint8_t* wp = m.w + ((size_t)g * m.C + i0) * kChunkBytes + lane * kBlockNibBytes;
+        Chunk a, b;
+        load_chunk(a, wp);
+        if (i0 + 1 < i1) load_chunk(b, wp + kChunkBytes);
+        for (int c = i0; c < i1; c += 2) {
+            chunk_terms<kSync>(c, c - c0, a, act, terms);
+            if (c + 2 < i1) load_chunk(a, wp + (size_t)(c + 2 - i0) * kChunkBytes);
+            if (c + 1 < i1) {
+                chunk_terms<kSync>(c + 1, c + 1 - c0, b, act, terms);
+                if (c + 3 < i1) load_chunk(b, wp + (size_t)(c + 3 - i0) * kChunkBytes);
+            }
+        }
+    }
+    __syncthreads();
+    // the range's fixed-order fp32 chains (at most kChainRangeChunks chunks: one segment):
+    // wave 0 chain A (blocks 0-3 of each chunk), wave 1 chain B (blocks 4-7)
+    float p = 0.0f;
+    if (wave < 2) {
+        int first[5];
+#pragma unroll
+        for (int w = 0; w <= 4; ++w) first[w] = c0 + split_first<4>(w, n);
+        int w = 0;  // the wave that staged chunk c
+        for (int c = c0; c < c1; ++c) {
+            while (c >= first[w + 1]) ++w;
+            const Q4S_LDS u32x2* st = stage + w * (kChainMaxChunks * 64) + (c - first[w]) * 64;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int bk = 4 * wave + x;
+                const uint32_t t = terms[((c - c0) * kChunkBlocks + bk) * 64 + lane];
+                const float dw16 = half_hi(t) * 0.0625f;
+                const float dx = __uint_as_float(st[8 * bk][1]);
+                const float s16 = (float)((int)(int16_t)(t & 0xffffu) * 16);
+                p = fmaf(dw16 * dx, s16, p);
+            }
+        }
+        if (wave == 1) red[lane] = p;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float acc = 0.0f;
+    acc += p + red[lane];
+    if (sp != 0) {
+        chain_st<kSync>(cm.kpart + ((int64_t)(sp - 1) * G + g) * 64 + lane, tag_word(acc, gen));
+        return;
+    }
+    float v = acc;
+    for (int j = 1; j < ks; ++j) {
+        const uint64_t* pw = cm.kpart + ((int64_t)(j - 1) * G + g) * 64 + lane;
+        v += chain_value<kSync>(pw, chain_ld<kSync>(pw), gen, err);
+    }
+    if (cm.yq) chain_store_q8<kSync>(cm.yq, m.rows, g, v, gen);
+    if (row >= m.rows) return;
+    if (cm.y) chain_st<kSync>(cm.y + row, tag_word(v, gen));
     if (cm.yf) gwr<float>(cm.yf)[row] = v;
     if (cm.res) {
         const float r = cm.res_plain ? ((const float*)cm.res)[row]
@@ -711,6 +810,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_chain(ChainParams P) {
             else if (tw & kChainSplit2)  // two row groups, two waves each
                 chain_tile_split<kSync, 2>(cm, tw & kChainTileIndex, red, (Q4S_LDS u32x2*)stage,
                                            (Q4S_LDS uint32_t*)terms, key, p, P.gen, P.sync, ms, mr);
+            else if (kSync == kChainTagged && (tw & kChainRange))  // one K range of a row group
+                chain_tile_range<kSync>(cm, tw & kChainTileIndex, red, (Q4S_LDS u32x2*)stage,
+                                        (Q4S_LDS uint32_t*)terms, key, p, P.gen, P.sync, ms, mr);
             else  // a group set: one wave per row group (or K range)
                 chain_tile<kSync>(cm, tw, red, (Q4S_LDS u32x2*)stage, key, p, P.gen, P.sync, ms, mr);
             __syncthreads();

@@ -229,16 +229,21 @@ def test_chain_host_side(L):
     assert d["n_mats"] == 197 and d["n_phases"] == 113 and d["workgroups"] == 0 and d["steps"] == 0
     assert d["packed_bytes"] == 868_257_792 and d["dev_bytes"] == need
     # laid out for 256 workgroups: q/k/v (32 row groups) and o (24): one row group per tile;
-    # gate + up (280 groups): two per tile (140); down (four K splits): one tile per row group;
-    # the head (2374 groups): group sets of 4 (594)
-    assert d["n_tiles"] == 28 * (32 + 24 + 140 + 24) + 594
+    # gate + up (280 groups): two per tile (140); down (four K splits of <= 16 chunks, tagged
+    # phases): one tile per K range and row group (96); the head (2374 groups): group sets of 4 (594)
+    assert d["n_tiles"] == 28 * (32 + 24 + 140 + 96) + 594
     assert L.q4s_chain_run(h, None) == 5                  # not uploaded
     L.q4s_chain_destroy(h)
     # for 64 workgroups gate + up fall back to group sets of 4; the device image does not change
     st, h, need64 = _chain(L, shape, ws, h0, acts, logits, wg=64)
     assert st == 0 and need64 == need
     assert L.q4s_chain_get_info(h, ctypes.byref(info)) == 0
-    assert info.n_tiles == 28 * (32 + 24 + 70 + 24) + 594
+    assert info.n_tiles == 28 * (32 + 24 + 70 + 96) + 594
+    L.q4s_chain_destroy(h)
+    # with barriers between phases down keeps one tile per row group (its four K ranges on 4 waves)
+    st, h, _ = _chain(L, shape, ws, h0, acts, logits, mode=q.CHAIN_TREE)
+    assert st == 0 and L.q4s_chain_get_info(h, ctypes.byref(info)) == 0
+    assert info.n_tiles == 28 * (32 + 24 + 140 + 24) + 594
     L.q4s_chain_destroy(h)
     # bad shapes, modes, counts, pointers and aliasing
     for bad in (q.ChainShape(2, 100, 64, 256, 10), q.ChainShape(2, 128, 0, 256, 10),

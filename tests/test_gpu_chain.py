@@ -104,6 +104,21 @@ def test_chain_wide_hidden_unpaired(oracle, mode):
     _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, "wide hidden")
 
 
+@pytest.mark.parametrize("workgroups", [0, 5], ids=["per_cu", "wg5"])
+def test_chain_k_range_tiles_bit_exact(oracle, workgroups):
+    """Tagged phases: down with four K splits of <= 16 chunks runs one tile per (K range, row
+    group), ranges 1..3 handing their sums to range 0 as tagged words.  With 5 workgroups each
+    runs several such tiles in turn (range 0 last).  Results equal the oracle's bit for bit."""
+    require_gpu()
+    L, E, D, F, V = 2, 256, 64, 4608, 320      # down: 18 chunks, K ranges of 4-5 chunks
+    shapes, ws, h0 = _inputs(47, L, E, D, F, V)
+    ref_acts, ref_logits = oracle.chain_step(ws, E, D, F, V, h0)
+    wp, h0d, acts, logits = _device(shapes, ws, h0, L, E, D, F, V)
+    vals, tags, lg, info = _run(wp, h0d, acts, logits, L, E, D, F, V, q.CHAIN_TAGGED, workgroups, steps=2)
+    assert (tags == 2).all()
+    _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, f"K-range tiles, {workgroups} workgroups")
+
+
 def test_chain_head_only(oracle):
     require_gpu()
     L, E, D, F, V = 0, 128, 64, 64, 200
