@@ -429,10 +429,13 @@ q4s_status q4s_chain_create(const q4s_chain_shape* shape, const void* const* w_p
 /*
  * Copy the chain's tables into dev_mem (16-byte aligned, caller-owned, kept
  * alive while the chain is used) and zero `acts`, both on `stream`.  dev_mem
- * also holds, past the tables, the step's quantized g * u words (written by
- * the gate/up tiles and read by down when gate and up have at most two K
- * splits, i.e. E <= 4096), which the upload zeroes.  Needs the GPU: resolves
- * and checks the workgroup count.
+ * also holds, past the tables, the step's quantized g * u and q words (written
+ * by the gate/up and q tiles, read by down and o; gate and up pair when they
+ * have at most two K splits, i.e. E <= 4096) and, with Q4S_CHAIN_TAGGED, the
+ * words through which down's K ranges meet when each runs on its own
+ * workgroup (four K splits of at most 16 chunks, i.e. 4128 <= F <= 16384);
+ * the upload zeroes both.  Needs the GPU: resolves and checks the workgroup
+ * count.
  */
 q4s_status q4s_chain_upload(q4s_chain* chain, void* dev_mem, size_t dev_bytes, void* stream);
 
