@@ -64,7 +64,7 @@ constexpr uint32_t kChainSplit4 = 1u << 31;
 constexpr uint32_t kChainSplit2 = 1u << 30;
 constexpr uint32_t kChainRange = 1u << 29;
 constexpr uint32_t kChainTileIndex = kChainRange - 1;
-constexpr int kChainRangeChunks = 16;  // a K-range tile's chunks (its term table)
+constexpr int kChainRangeChunks = 32;  // a K-range tile's chunks at most (its term table)
 hipError_t chain_max_workgroups(int sync_mode, int* n);
 
 }  // namespace q4s

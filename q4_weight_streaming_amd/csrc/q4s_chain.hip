@@ -527,8 +527,10 @@ __device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, flo
 // tile, with 1/wpg of the serial work per wave.
 constexpr int kChainSplitChunks = 16;  // chunks of a matrix with ks <= 2
 constexpr int kChainTermWords = kChainSplitChunks * kChunkBlocks * 64;  // one group's term table
-static_assert(kChainRangeChunks <= kChainSplitChunks, "a K-range tile's chunks fit the term table");
-static_assert(kChainRangeChunks <= kSegChunks, "a K-range tile's chunks are one segment");
+// the workgroup's term table: a split tile's group(s), or a K-range tile's range
+constexpr int kChainTableWords =
+    (kChainRangeChunks > kChainSplitChunks ? kChainRangeChunks : kChainSplitChunks) * kChunkBlocks * 64;
+static_assert(kChainRangeChunks <= 4 * kSegChunks, "a K-range tile's segments fit the hand-off buffer");
 
 template <int kWpg>
 __device__ __forceinline__ int split_first(int w, int C) { return (w * C + kWpg - 1) / kWpg; }
@@ -649,7 +651,8 @@ __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t til
 // kChainRangeChunks chunks) on its own workgroup, with tagged phases: the
 // range's chunks are spread over the 4 waves as in chain_tile_split (exact
 // block sums and d_w in the term table), waves 0 and 1 run the range's
-// fixed-order chains A and B (one segment) and wave 0 forms 0 + (A + B), as the
+// fixed-order chains A and B, and wave 0 adds each segment's A + B into the
+// range's accumulator (segments of kSegChunks chunks), as the
 // one-wave-per-range tile does.  Ranges 1..3 store that value as tagged words in kpart; range 0, whose
 // tiles come last in the phase's table (so a workgroup never waits on a tile it
 // has yet to run), polls them and adds the ranges in order -- ((r0 + r1) + r2)
@@ -693,14 +696,20 @@ __device__ __forceinline__ void chain_tile_range(const ChainMat& cm, int64_t idx
         }
     }
     __syncthreads();
-    // the range's fixed-order fp32 chains (at most kChainRangeChunks chunks: one segment):
-    // wave 0 chain A (blocks 0-3 of each chunk), wave 1 chain B (blocks 4-7)
-    float p = 0.0f;
+    // the range's fixed-order fp32 chains: wave 0 chain A (blocks 0-3 of each chunk), wave 1
+    // chain B (blocks 4-7), each closed at every segment end; wave 1 leaves its segment values
+    // in red, wave 0 keeps its own
+    constexpr int kMaxSeg = (kChainRangeChunks + kSegChunks - 1) / kSegChunks;
+    float pseg[kMaxSeg];
+#pragma unroll
+    for (int k = 0; k < kMaxSeg; ++k) pseg[k] = 0.0f;
     if (wave < 2) {
         int first[5];
 #pragma unroll
         for (int w = 0; w <= 4; ++w) first[w] = c0 + split_first<4>(w, n);
         int w = 0;  // the wave that staged chunk c
+        float p = 0.0f;
+        int seg = 0;
         for (int c = c0; c < c1; ++c) {
             while (c >= first[w + 1]) ++w;
             const Q4S_LDS u32x2* st = stage + w * (kChainMaxChunks * 64) + (c - first[w]) * 64;
@@ -713,13 +722,23 @@ __device__ __forceinline__ void chain_tile_range(const ChainMat& cm, int64_t idx
                 const float s16 = (float)((int)(int16_t)(t & 0xffffu) * 16);
                 p = fmaf(dw16 * dx, s16, p);
             }
+            if (c + 1 == c1 || (c + 1 - c0) % kSegChunks == 0) {  // segment end
+                if (wave == 1) red[seg * 64 + lane] = p;
+#pragma unroll
+                for (int k = 0; k < kMaxSeg; ++k)
+                    if (k == seg) pseg[k] = p;
+                p = 0.0f;
+                ++seg;
+            }
         }
-        if (wave == 1) red[lane] = p;
     }
     __syncthreads();
     if (wave != 0) return;
     float acc = 0.0f;
-    acc += p + red[lane];
+    const int nseg = (n + kSegChunks - 1) / kSegChunks;
+#pragma unroll
+    for (int k = 0; k < kMaxSeg; ++k)
+        if (k < nseg) acc += pseg[k] + red[k * 64 + lane];
     if (sp != 0) {
         chain_st<kSync>(cm.kpart + ((int64_t)(sp - 1) * G + g) * 64 + lane, tag_word(acc, gen));
         return;
@@ -787,7 +806,7 @@ template <int kSync>
 __global__ __launch_bounds__(kThreads, 1) void k_chain(ChainParams P) {
     __shared__ float red[kWaves * 64];
     __shared__ u32x2 stage[kWaves * kChainMaxChunks * 64];
-    __shared__ uint32_t terms[kChainTermWords];
+    __shared__ uint32_t terms[kChainTableWords];
     const uint32_t nwg = gridDim.x, b = blockIdx.x;
     if (P.trace && threadIdx.x == 0)  // when this workgroup started, after the phase-end plane
         gwr<uint64_t>(P.trace)[(size_t)P.n_phases * nwg + b] = __builtin_amdgcn_s_memrealtime();

@@ -104,13 +104,15 @@ def test_chain_wide_hidden_unpaired(oracle, mode):
     _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, "wide hidden")
 
 
-@pytest.mark.parametrize("workgroups", [0, 5], ids=["per_cu", "wg5"])
-def test_chain_k_range_tiles_bit_exact(oracle, workgroups):
-    """Tagged phases: down with four K splits of <= 16 chunks runs one tile per (K range, row
-    group), ranges 1..3 handing their sums to range 0 as tagged words.  With 5 workgroups each
-    runs several such tiles in turn (range 0 last).  Results equal the oracle's bit for bit."""
+@pytest.mark.parametrize("F,workgroups", [(4608, 0), (4608, 5), (17408, 0), (17408, 5)],
+                         ids=["ranges4_per_cu", "ranges4_wg5", "ranges17_per_cu", "ranges17_wg5"])
+def test_chain_k_range_tiles_bit_exact(oracle, F, workgroups):
+    """Tagged phases: down with four K splits runs one tile per (K range, row group), ranges
+    1..3 handing their sums to range 0 as tagged words.  F = 4608: ranges of 4-5 chunks; F =
+    17408: 17 chunks, two fp32 segments per range.  With 5 workgroups each runs several such
+    tiles in turn (range 0 last).  Results equal the oracle's bit for bit."""
     require_gpu()
-    L, E, D, F, V = 2, 256, 64, 4608, 320      # down: 18 chunks, K ranges of 4-5 chunks
+    L, E, D, V = 2, 256, 64, 320
     shapes, ws, h0 = _inputs(47, L, E, D, F, V)
     ref_acts, ref_logits = oracle.chain_step(ws, E, D, F, V, h0)
     wp, h0d, acts, logits = _device(shapes, ws, h0, L, E, D, F, V)
