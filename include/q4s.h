@@ -433,7 +433,7 @@ q4s_status q4s_chain_create(const q4s_chain_shape* shape, const void* const* w_p
  * by the gate/up and q tiles, read by down and o; gate and up pair when they
  * have at most two K splits, i.e. E <= 4096) and, with Q4S_CHAIN_TAGGED, the
  * words through which down's K ranges meet when each runs on its own
- * workgroup (four K splits of at most 16 chunks, i.e. 4128 <= F <= 16384);
+ * workgroup (four K splits of at most 32 chunks, i.e. 4128 <= F <= 32768);
  * the upload zeroes both.  Needs the GPU: resolves and checks the workgroup
  * count.
  */
