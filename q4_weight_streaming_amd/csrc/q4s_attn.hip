@@ -35,8 +35,9 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// workspace of split s (attn_split_floats(n_q) floats, a multiple of 4): [n_q][128]
-// unnormalized outputs, then [n_q] maxima m, then [n_q] sums l
+// workspace (S * attn_split_floats(n_q) floats), head-major so that the combine reads
+// each head's splits contiguously: unnormalized outputs [n_q][S][128], then maxima m
+// [n_q][S], then sums l [n_q][S]
 struct AttnParams {
     const float* q;      // [n_q][128]
     const float* kb;     // [n_kv][l_cap/64][128][64]
@@ -122,9 +123,9 @@ __global__ __launch_bounds__(256) void k_attn_partial(AttnParams a) {
         const float l = wave_sum(p);
         pr[h][lane] = p;
         if (lane == 0) {
-            float* wsm = a.ws + (int64_t)s * attn_split_floats(a.n_q) + (int64_t)a.n_q * kHd;
-            gwr<float>(wsm)[g * G + h] = m;
-            gwr<float>(wsm)[a.n_q + g * G + h] = l;
+            float* wsm = a.ws + (int64_t)a.n_q * a.S * kHd + (int64_t)(g * G + h) * a.S + s;
+            gwr<float>(wsm)[0] = m;
+            gwr<float>(wsm)[(int64_t)a.n_q * a.S] = l;
         }
     }
     __syncthreads();
@@ -146,38 +147,43 @@ __global__ __launch_bounds__(256) void k_attn_partial(AttnParams a) {
         f32x4 o = vred[0][h][d4];
 #pragma unroll
         for (int k = 1; k < 8; ++k) o += vred[k][h][d4];
-        float* wso = a.ws + (int64_t)s * attn_split_floats(a.n_q);
-        gwr<f32x4>(wso + (int64_t)(g * G + h) * kHd)[d4] = o;
+        float* wso = a.ws + ((int64_t)(g * G + h) * a.S + s) * kHd;
+        gwr<f32x4>(wso)[d4] = o;
     }
 }
 
-// Workgroup (query head h, 4-dimension block), 256 threads: thread (split
-// slice k, dimension) takes splits [k*S/64, (k+1)*S/64) in order, all of its
-// loads issued together.  The 64 slices are reduced in a fixed tree: the 16
-// slices of a wave by an xor butterfly over lanes 4, 8, 16 and 32 apart, then
-// the 4 waves in order through LDS.
+// Workgroup (query head h, 16-dimension block), 256 threads: thread (split
+// slice k, dimension quad) takes splits [k*S/64, (k+1)*S/64) in order, one
+// 16-byte load of its 4 dimensions per split, all of a batch's loads issued
+// together.  The 64 slices are reduced in a fixed tree: the 16 slices of a wave
+// by an xor butterfly over lanes 4, 8, 16 and 32 apart, then the 4 waves in
+// order through LDS.
 constexpr int kCombSlices = 64;
-constexpr int kCombDims = 4;
-constexpr int kCombWaves = kCombSlices * kCombDims / 64;  // 4
+constexpr int kCombQuads = 4;                                // dimension quads per workgroup
+constexpr int kCombDims = 4 * kCombQuads;                    // 16
+constexpr int kCombWaves = kCombSlices * kCombQuads / 64;    // 4
 constexpr int kCombBatch = 8;  // splits per slice whose loads are in flight together
-__global__ __launch_bounds__(kCombSlices * kCombDims) void k_attn_combine(AttnParams a) {
+
+__global__ __launch_bounds__(kCombSlices * kCombQuads) void k_attn_combine(AttnParams a) {
     __shared__ float mred[kCombWaves];
-    __shared__ float num[kCombWaves][kCombDims];
+    __shared__ f32x4 num[kCombWaves][kCombQuads];
     __shared__ float den[kCombWaves];
     const int h = blockIdx.x, d0 = blockIdx.y * kCombDims;
-    const int t = threadIdx.x, dd = t % kCombDims, k = t / kCombDims, wv = t >> 6, lane = t & 63;
-    const int64_t stride = attn_split_floats(a.n_q);
-    const int64_t om = (int64_t)a.n_q * kHd, ol = om + a.n_q;  // offsets of m and l in a split
+    const int t = threadIdx.x, dq = t % kCombQuads, k = t / kCombQuads, wv = t >> 6, lane = t & 63;
+    const float* om = a.ws + (int64_t)a.n_q * a.S * kHd + (int64_t)h * a.S;  // m of head h; l follows n_q*S later
+    const float* ol = om + (int64_t)a.n_q * a.S;
+    const float* oo = a.ws + (int64_t)h * a.S * kHd + d0 + 4 * dq;
     const int s0 = (int)((int64_t)k * a.S / kCombSlices), s1 = (int)((int64_t)(k + 1) * a.S / kCombSlices);
     // the first batch of the slice (all of it up to 512 splits) loaded at once
-    float mm[kCombBatch], ll[kCombBatch], oo[kCombBatch];
+    float mm[kCombBatch], ll[kCombBatch];
+    f32x4 ov[kCombBatch];
     auto load_batch = [&](int b) {
 #pragma unroll
         for (int i = 0; i < kCombBatch; ++i) {
-            const float* wsm = a.ws + max(min(b + i, s1 - 1), 0) * stride;
-            mm[i] = wsm[om + h];
-            ll[i] = wsm[ol + h];
-            oo[i] = wsm[(int64_t)h * kHd + d0 + dd];
+            const int sp = max(min(b + i, s1 - 1), 0);
+            mm[i] = om[sp];
+            ll[i] = ol[sp];
+            ov[i] = gp<f32x4>(oo + (int64_t)sp * kHd)[0];
         }
     };
     load_batch(s0);
@@ -185,15 +191,16 @@ __global__ __launch_bounds__(kCombSlices * kCombDims) void k_attn_combine(AttnPa
 #pragma unroll
     for (int i = 0; i < kCombBatch; ++i)
         if (s0 + i < s1) mk = fmaxf(mk, mm[i]);
-    for (int b = s0 + kCombBatch; b < s1; ++b) mk = fmaxf(mk, a.ws[b * stride + om + h]);
+    for (int b = s0 + kCombBatch; b < s1; ++b) mk = fmaxf(mk, om[b]);
 #pragma unroll
-    for (int off = kCombDims; off < 64; off <<= 1) mk = fmaxf(mk, __shfl_xor(mk, off, 64));
+    for (int off = kCombQuads; off < 64; off <<= 1) mk = fmaxf(mk, __shfl_xor(mk, off, 64));
     if (lane == 0) mred[wv] = mk;
     __syncthreads();
     float M = mred[0];
 #pragma unroll
     for (int i = 1; i < kCombWaves; ++i) M = fmaxf(M, mred[i]);
-    float nu = 0.0f, de = 0.0f;
+    f32x4 nu = {0.f, 0.f, 0.f, 0.f};
+    float de = 0.0f;
     for (int b = s0; b < s1; b += kCombBatch) {
         if (b != s0) load_batch(b);
 #pragma unroll
@@ -201,25 +208,31 @@ __global__ __launch_bounds__(kCombSlices * kCombDims) void k_attn_combine(AttnPa
             if (b + i >= s1) break;
             const float f = expf(mm[i] - M);
             de = fmaf(f, ll[i], de);
-            nu = fmaf(f, oo[i], nu);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) nu[c] = fmaf(f, ov[i][c], nu[c]);
         }
     }
 #pragma unroll
-    for (int off = kCombDims; off < 64; off <<= 1) {
-        nu += __shfl_xor(nu, off, 64);
+    for (int off = kCombQuads; off < 64; off <<= 1) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) nu[c] += __shfl_xor(nu[c], off, 64);
         de += __shfl_xor(de, off, 64);
     }
-    if (lane < kCombDims) num[wv][dd] = nu;
+    if (lane < kCombQuads) num[wv][dq] = nu;
     if (lane == 0) den[wv] = de;
     __syncthreads();
-    if (t < kCombDims) {
-        float n = num[0][dd], d = den[0];
+    if (t < kCombQuads) {
+        f32x4 n = num[0][dq];
+        float d = den[0];
 #pragma unroll
         for (int i = 1; i < kCombWaves; ++i) {
-            n += num[i][dd];
+            n += num[i][dq];
             d += den[i];
         }
-        gwr<float>(a.o)[(int64_t)h * kHd + d0 + dd] = n / d;
+        f32x4 r;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r[c] = n[c] / d;
+        gwr<f32x4>(a.o + (int64_t)h * kHd + d0)[dq] = r;
     }
 }
 
@@ -242,7 +255,7 @@ hipError_t launch_attn_decode(const float* q, const float* kb, const float* v, f
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)n_q, kHd / kCombDims), dim3(kCombSlices * kCombDims), 0, st,
+    hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)n_q, kHd / kCombDims), dim3(kCombSlices * kCombQuads), 0, st,
                        a);
     return hipGetLastError();
 }
