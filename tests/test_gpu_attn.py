@@ -66,6 +66,13 @@ def test_attn_full_context(oracle):
     _check(_run(qv, k, v, pad=0), oracle.attn_decode(qv, k, v))
 
 
+@pytest.mark.parametrize("L,n_q,n_kv", [(40000, 2, 1), (70001, 4, 2)])
+def test_attn_beyond_one_combine_batch(oracle, L, n_q, n_kv):
+    # more than 512 splits: each of the combine's 64 slices takes its splits in several load batches
+    qv, k, v = _cache(L, n_q, n_kv, seed=L + n_q)
+    _check(_run(qv, k, v), oracle.attn_decode(qv, k, v))
+
+
 def test_attn_peaked_scores(oracle):
     qv, k, v = _cache(3000, 12, 2, seed=8, spread=4.0)     # sharper softmax
     _check(_run(qv, k, v), oracle.attn_decode(qv, k, v))
