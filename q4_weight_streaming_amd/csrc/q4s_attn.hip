@@ -49,74 +49,78 @@ struct AttnParams {
     float scale;
 };
 
+// Sum of v over the 4 lanes of a lane quad (xor 1, then xor 2: a fixed order), by DPP moves.
+__device__ __forceinline__ float quad_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
+    return v;
+}
+
+constexpr int kPartThreads = 512;  // 8 waves per (kv head, split)
+
 template <int G>
-__global__ __launch_bounds__(256) void k_attn_partial(AttnParams a) {
+__global__ __launch_bounds__(kPartThreads) void k_attn_partial(AttnParams a) {
     __shared__ f32x4 qs[G][kHd / 4];
     __shared__ float pr[G][kSplit];
-    // the partial dots are dead once the scores are formed; the value slices reuse their space
+    // the partial dots are dead once the scores are formed; the value sums reuse their space
     __shared__ union {
-        f32x4 part[16][G][kSplit / 4];  // [dimension group][head][position quad]
-        f32x4 vred[8][G][kHd / 4];      // [position slice][head][dimension quad]
+        f32x4 part[8][G][kSplit / 4];  // [wave: 16 dimensions][head][position quad]
+        f32x4 vred[4][G][kHd / 4];     // [16-position group][head][dimension quad]
     } u;
     auto& part = u.part;
     auto& vred = u.vred;
     const int s = blockIdx.x, g = blockIdx.y;
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, ql = lane & 3;
     const int64_t j0 = (int64_t)s * kSplit;
     const int nk = (int)min((int64_t)kSplit, a.L - j0);
     // Every load of the split is issued up front (queries, keys, values), as
     // 16-byte non-temporal loads; positions past L are masked below.
     f32x4 qv = {0.f, 0.f, 0.f, 0.f};
     if (t < G * kHd / 4) qv = gp<f32x4>(a.q + (int64_t)(g * G) * kHd)[t];
-    // keys: thread (dimension group dg = t/16: dimensions 8dg .. 8dg+7, position quad pq = t%16);
-    // the workgroup reads its split's 32 KB key block contiguously
-    const int pq = t & 15, dg = t >> 4;
-    f32x4 kv[8];
+    // keys: thread (dimension group dg = 4w + ql: dimensions 4dg .. 4dg+3, position quad pq = lane/4);
+    // each wave load reads 4 rows of 256 contiguous bytes of the split's 32 KB key block
+    const int pq = lane >> 2, dg = 4 * w + ql;
+    f32x4 kv[4];
     {
-        const float* kp = a.kb + (((int64_t)g * (a.l_cap / kSplit) + s) * kHd + 8 * dg) * kSplit + 4 * pq;
+        const float* kp = a.kb + (((int64_t)g * (a.l_cap / kSplit) + s) * kHd + 4 * dg) * kSplit + 4 * pq;
 #pragma unroll
-        for (int d = 0; d < 8; ++d) kv[d] = __builtin_nontemporal_load(gp<f32x4>(kp + d * kSplit));
+        for (int d = 0; d < 4; ++d) kv[d] = __builtin_nontemporal_load(gp<f32x4>(kp + d * kSplit));
     }
-    const int dq = t & 31, ks = t >> 5;  // values: dimensions 4dq .. 4dq+3, positions 8ks .. 8ks+7
-    f32x4 vv[8];
+    // values: thread (dimension quad dq = 16 (w&1) + lane/4, positions 16 (w>>1) + 4 ql .. +3)
+    const int dq = 16 * (w & 1) + (lane >> 2), pg = w >> 1;
+    f32x4 vv[4];
     {
         const float* vp = a.v + ((int64_t)g * a.l_cap + j0) * kHd + 4 * dq;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            vv[e] = __builtin_nontemporal_load(gp<f32x4>(vp + (int64_t)min(8 * ks + e, nk - 1) * kHd));
+        for (int e = 0; e < 4; ++e)
+            vv[e] = __builtin_nontemporal_load(gp<f32x4>(vp + (int64_t)min(16 * pg + 4 * ql + e, nk - 1) * kHd));
     }
     if (t < G * kHd / 4) qs[t / (kHd / 4)][t % (kHd / 4)] = qv;
     __syncthreads();
-    // partial dots over the thread's 8 dimensions for its 4 positions
-    {
+    // partial dots over the thread's 4 dimensions for its 4 positions, then over the
+    // quad's 16 dimensions
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const f32x4 q0 = qs[h][2 * dg], q1 = qs[h][2 * dg + 1];
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < G; ++h) {
+        const f32x4 q0 = qs[h][dg];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                acc[0] = fmaf(q0[d], kv[d][0], acc[0]);
-                acc[1] = fmaf(q0[d], kv[d][1], acc[1]);
-                acc[2] = fmaf(q0[d], kv[d][2], acc[2]);
-                acc[3] = fmaf(q0[d], kv[d][3], acc[3]);
-            }
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                acc[0] = fmaf(q1[d], kv[4 + d][0], acc[0]);
-                acc[1] = fmaf(q1[d], kv[4 + d][1], acc[1]);
-                acc[2] = fmaf(q1[d], kv[4 + d][2], acc[2]);
-                acc[3] = fmaf(q1[d], kv[4 + d][3], acc[3]);
-            }
-            part[dg][h][pq] = acc;
+        for (int d = 0; d < 4; ++d) {
+            acc[0] = fmaf(q0[d], kv[d][0], acc[0]);
+            acc[1] = fmaf(q0[d], kv[d][1], acc[1]);
+            acc[2] = fmaf(q0[d], kv[d][2], acc[2]);
+            acc[3] = fmaf(q0[d], kv[d][3], acc[3]);
         }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = quad_sum(acc[c]);
+        if (ql == 0) part[w][h][pq] = acc;
     }
     __syncthreads();
-    // scores (the 16 dimension groups added in order) and the split's softmax:
-    // wave w takes heads w, w + 4; lane = position
-    for (int h = w; h < G; h += 4) {
+    // scores (the 8 waves' dimension groups added in order) and the split's softmax:
+    // wave w takes head w; lane = position
+    for (int h = w; h < G; h += 8) {
         float sc = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) sc += ((const float*)part[k][h])[lane];
+        for (int k = 0; k < 8; ++k) sc += ((const float*)part[k][h])[lane];
         sc = lane < nk ? sc * a.scale : -INFINITY;
         const float m = wave_max(sc);
         const float p = lane < nk ? expf(sc - m) : 0.0f;
@@ -129,24 +133,27 @@ __global__ __launch_bounds__(256) void k_attn_partial(AttnParams a) {
         }
     }
     __syncthreads();
-    // weighted values over the thread's 8 positions, then the 8 position slices in order
+    // weighted values over the thread's 4 positions, then over the quad's 16 positions,
+    // then the 4 position groups in order
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float p = pr[h][8 * ks + e];  // 0 past the split's last position
+        for (int e = 0; e < 4; ++e) {
+            const float p = pr[h][16 * pg + 4 * ql + e];  // 0 past the split's last position
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[c] = fmaf(p, vv[e][c], acc[c]);
         }
-        vred[ks][h][dq] = acc;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = quad_sum(acc[c]);
+        if (ql == 0) vred[pg][h][dq] = acc;
     }
     __syncthreads();
     if (t < G * kHd / 4) {
         const int h = t / (kHd / 4), d4 = t % (kHd / 4);
         f32x4 o = vred[0][h][d4];
 #pragma unroll
-        for (int k = 1; k < 8; ++k) o += vred[k][h][d4];
+        for (int k = 1; k < 4; ++k) o += vred[k][h][d4];
         float* wso = a.ws + ((int64_t)(g * G + h) * a.S + s) * kHd;
         gwr<f32x4>(wso)[d4] = o;
     }
@@ -243,14 +250,14 @@ hipError_t launch_attn_decode(const float* q, const float* kb, const float* v, f
     AttnParams a{q, kb, v, o, ws, L, l_cap, n_q, n_kv, (int)((L + kSplit - 1) / kSplit), scale};
     const dim3 grid((unsigned)a.S, (unsigned)n_kv);
     switch (n_q / n_kv) {
-        case 1: hipLaunchKernelGGL(k_attn_partial<1>, grid, dim3(256), 0, st, a); break;
-        case 2: hipLaunchKernelGGL(k_attn_partial<2>, grid, dim3(256), 0, st, a); break;
-        case 3: hipLaunchKernelGGL(k_attn_partial<3>, grid, dim3(256), 0, st, a); break;
-        case 4: hipLaunchKernelGGL(k_attn_partial<4>, grid, dim3(256), 0, st, a); break;
-        case 5: hipLaunchKernelGGL(k_attn_partial<5>, grid, dim3(256), 0, st, a); break;
-        case 6: hipLaunchKernelGGL(k_attn_partial<6>, grid, dim3(256), 0, st, a); break;
-        case 7: hipLaunchKernelGGL(k_attn_partial<7>, grid, dim3(256), 0, st, a); break;
-        case 8: hipLaunchKernelGGL(k_attn_partial<8>, grid, dim3(256), 0, st, a); break;
+        case 1: hipLaunchKernelGGL(k_attn_partial<1>, grid, dim3(kPartThreads), 0, st, a); break;
+        case 2: hipLaunchKernelGGL(k_attn_partial<2>, grid, dim3(kPartThreads), 0, st, a); break;
+        case 3: hipLaunchKernelGGL(k_attn_partial<3>, grid, dim3(kPartThreads), 0, st, a); break;
+        case 4: hipLaunchKernelGGL(k_attn_partial<4>, grid, dim3(kPartThreads), 0, st, a); break;
+        case 5: hipLaunchKernelGGL(k_attn_partial<5>, grid, dim3(kPartThreads), 0, st, a); break;
+        case 6: hipLaunchKernelGGL(k_attn_partial<6>, grid, dim3(kPartThreads), 0, st, a); break;
+        case 7: hipLaunchKernelGGL(k_attn_partial<7>, grid, dim3(kPartThreads), 0, st, a); break;
+        case 8: hipLaunchKernelGGL(k_attn_partial<8>, grid, dim3(kPartThreads), 0, st, a); break;
         default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
