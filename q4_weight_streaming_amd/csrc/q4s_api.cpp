@@ -574,7 +574,7 @@ struct q4s_chain {
 // spread over the 4 waves (matrices with one or two K splits), or two row
 // groups per tile with two waves each (one K split); else a group set per tile
 // (one wave per row group, or per K range).  With tagged phases a phase whose
-// one matrix has K-range words (four K splits of <= 16 chunks: down) runs one
+// one matrix has K-range words (four K splits of <= 32 chunks: down) runs one
 // tile per (K range, row group) instead, ranges 1..3 first and range 0 last,
 // whatever the workgroup count.  The device image keeps room for the largest
 // table (one tile per row group, or per K range and row group).
@@ -770,7 +770,7 @@ q4s_status q4s_chain_create(const q4s_chain_shape* shape, const void* const* w_p
             cm.y = word(l, odn), cm.res = word(l, oh1), cm.y2 = word(l, oh2);
             add(cm);
             if (pair) p->q8_in.back() = q8_at;
-            // with tagged phases, four K splits of <= 16 chunks each run as K-range tiles
+            // with tagged phases, four K splits of <= 32 chunks each run as K-range tiles
             if (sync_mode == Q4S_CHAIN_TAGGED && cm.m.ks == 4 && cm.m.C <= 4 * kChainRangeChunks) {
                 p->kp_off.back() = (int64_t)p->kp_bytes;
                 p->kp_bytes += (size_t)(cm.m.ks - 1) * (size_t)cm.m.G * 64 * 8;

@@ -57,7 +57,7 @@ constexpr uint32_t kChainDefaultSpin = 1u << 20;
 // Tile word: the tile index in bits 0-28; bit 31: one row group whose chunks
 // are spread over the 4 waves; bit 30: two row groups, two waves each; bit 29:
 // one K range of one row group (index = range * G + group) of a matrix with
-// four K splits of at most 16 chunks, its chunks spread over the 4 waves, the
+// four K splits of at most kChainRangeChunks chunks, its chunks spread over the 4 waves, the
 // ranges meeting through kpart (tagged phases only); none: a group set (one
 // wave per row group, or per K range).
 constexpr uint32_t kChainSplit4 = 1u << 31;
