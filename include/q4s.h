@@ -278,6 +278,27 @@ size_t q4s_attn_workspace_bytes(int n_q, int64_t L);
 q4s_status q4s_attn_decode(const float* q, const float* k_blk, const float* v, float* o, int n_q, int n_kv,
                            int64_t L, int64_t l_cap, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * q4s_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The per-split partials go to a static
+ * array of Q4S_ATTN_SCRATCH_BYTES bytes in device memory, one per GPU: it is
+ * held from the first call on that GPU until the process ends, and the
+ * library takes its address once per GPU (the calling thread's current
+ * device, which must be the device of `stream`).  Everything else -- the
+ * arguments, their checks, the kernels and the results, bit for bit -- is as
+ * for q4s_attn_decode.  A call whose partials, q4s_attn_workspace_bytes(n_q,
+ * L), exceed Q4S_ATTN_SCRATCH_BYTES returns Q4S_ERR_SHAPE and enqueues
+ * nothing (12 query heads: L up to 86016).  Nothing is allocated or freed,
+ * by the library or anything it calls.  All calls on one GPU share its
+ * array, which keeps the last call's partials (every call overwrites all it
+ * reads, so nothing needs clearing): calls that may overlap in time on one
+ * GPU (other streams, other threads) race and give undefined results.
+ */
+#define Q4S_ATTN_SCRATCH_BYTES ((size_t)8 << 20)
+q4s_status q4s_attn_decode_noalloc(const float* q, const float* k_blk, const float* v, float* o, int n_q,
+                                   int n_kv, int64_t L, int64_t l_cap, void* stream);
+
 /* ---------------------------------------------------- layer-stack sweep */
 
 /*

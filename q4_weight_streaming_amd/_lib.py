@@ -87,6 +87,7 @@ def lib():
             "q4s_requant_q8_0_to_q4_0": ([p, p, i64, i64, p], i32),
             "q4s_attn_workspace_bytes": ([i32, i64], sz),
             "q4s_attn_decode": ([p, p, p, p, i32, i32, i64, i64, p, sz, p], i32),
+            "q4s_attn_decode_noalloc": ([p, p, p, p, i32, i32, i64, i64, p], i32),
             "q4s_sweep_plan_create": ([p, i32, i32, ctypes.POINTER(sz), ctypes.POINTER(p)], i32),
             "q4s_sweep_plan_upload": ([p, p, sz, p], i32),
             "q4s_sweep_run": ([p, p], i32),
@@ -313,6 +314,21 @@ def attn_decode(q: torch.Tensor, k_blk: torch.Tensor, v: torch.Tensor, L: int,
         _dev(q, "q", torch.float32), _dev(k_blk, "k_blk", torch.float32), _dev(v, "v", torch.float32),
         _dev(out, "out", torch.float32), n_q, n_kv, L, l_cap, _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return out
+
+
+ATTN_SCRATCH_BYTES = 8 << 20
+
+
+def attn_decode_noalloc(q: torch.Tensor, k_blk: torch.Tensor, v: torch.Tensor, L: int,
+                        out: torch.Tensor) -> torch.Tensor:
+    """attn_decode with the split partials in the library's static per-GPU scratch
+    (q4s_attn_decode_noalloc): the call allocates nothing; `out` fp32 [n_q][128] is required."""
+    n_q = q.shape[0]
+    n_kv, l_cap = v.shape[0], v.shape[1]
+    _check("q4s_attn_decode_noalloc", lib().q4s_attn_decode_noalloc(
+        _dev(q, "q", torch.float32), _dev(k_blk, "k_blk", torch.float32), _dev(v, "v", torch.float32),
+        _dev(out, "out", torch.float32), n_q, n_kv, L, l_cap, _stream(q.device)))
     return out
 
 

@@ -313,8 +313,11 @@ size_t q4s_attn_workspace_bytes(int n_q, int64_t L) {
     return (size_t)attn_splits(L) * (size_t)attn_split_floats(n_q) * 4;
 }
 
-q4s_status q4s_attn_decode(const float* q, const float* k_blk, const float* v, float* o, int n_q, int n_kv,
-                           int64_t L, int64_t l_cap, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// shapes and buffers of a decode-attention call, except the workspace
+q4s_status check_attn(const float* q, const float* k_blk, const float* v, const float* o, int n_q, int n_kv,
+                      int64_t L, int64_t l_cap) {
     if (n_q < 1 || n_q > 4096 || n_kv < 1 || n_q % n_kv != 0 || n_q / n_kv > 8)
         return fail(Q4S_ERR_SHAPE, "n_q=%d, n_kv=%d: n_kv must divide n_q with a group of 1..8", n_q, n_kv);
     if (L < 1 || l_cap < L || l_cap >= kMaxDim || l_cap % kAttnSplit != 0)
@@ -322,21 +325,49 @@ q4s_status q4s_attn_decode(const float* q, const float* k_blk, const float* v, f
                     (long long)L, (long long)l_cap);
     const size_t qb = (size_t)n_q * kAttnHeadDim * 4;
     const size_t kvb = (size_t)l_cap * n_kv * kAttnHeadDim * 4;
-    const size_t wsb = q4s_attn_workspace_bytes(n_q, L);
     q4s_status s;
     if ((s = check_ptr(q, qb, 16, "q"))) return s;
     if ((s = check_ptr(k_blk, kvb, 16, "k_blk"))) return s;
     if ((s = check_ptr(v, kvb, 16, "v"))) return s;
     if ((s = check_ptr(o, qb, 4, "o"))) return s;
+    if (overlap(o, qb, q, qb) || overlap(o, qb, k_blk, kvb) || overlap(o, qb, v, kvb))
+        return fail(Q4S_ERR_ALIAS, "o overlaps an input");
+    return Q4S_OK;
+}
+
+}  // namespace
+
+q4s_status q4s_attn_decode(const float* q, const float* k_blk, const float* v, float* o, int n_q, int n_kv,
+                           int64_t L, int64_t l_cap, void* workspace, size_t workspace_bytes, void* stream) {
+    q4s_status s;
+    if ((s = check_attn(q, k_blk, v, o, n_q, n_kv, L, l_cap))) return s;
+    const size_t qb = (size_t)n_q * kAttnHeadDim * 4;
+    const size_t kvb = (size_t)l_cap * n_kv * kAttnHeadDim * 4;
+    const size_t wsb = q4s_attn_workspace_bytes(n_q, L);
     if ((s = check_ptr(workspace, wsb, 16, "workspace"))) return s;
     if (workspace_bytes < wsb)
         return fail(Q4S_ERR_SHAPE, "workspace holds %zu bytes, needs %zu", workspace_bytes, wsb);
-    if (overlap(o, qb, q, qb) || overlap(o, qb, k_blk, kvb) || overlap(o, qb, v, kvb) ||
-        overlap(o, qb, workspace, wsb))
-        return fail(Q4S_ERR_ALIAS, "o overlaps an input or the workspace");
+    if (overlap(o, qb, workspace, wsb)) return fail(Q4S_ERR_ALIAS, "o overlaps the workspace");
     if (overlap(workspace, wsb, q, qb) || overlap(workspace, wsb, k_blk, kvb) || overlap(workspace, wsb, v, kvb))
         return fail(Q4S_ERR_ALIAS, "workspace overlaps an input");
     return hip_status(launch_attn_decode(q, k_blk, v, o, (float*)workspace, n_q, n_kv, L, l_cap,
+                                         (float)(1.0 / std::sqrt((double)kAttnHeadDim)), (hipStream_t)stream),
+                      "attention launch");
+}
+
+q4s_status q4s_attn_decode_noalloc(const float* q, const float* k_blk, const float* v, float* o, int n_q, int n_kv,
+                                   int64_t L, int64_t l_cap, void* stream) {
+    static_assert(Q4S_ATTN_SCRATCH_BYTES == kAttnScratchBytes, "header and library agree on the scratch size");
+    q4s_status s;
+    if ((s = check_attn(q, k_blk, v, o, n_q, n_kv, L, l_cap))) return s;
+    const size_t wsb = q4s_attn_workspace_bytes(n_q, L);
+    if (wsb > kAttnScratchBytes)
+        return fail(Q4S_ERR_SHAPE, "n_q=%d, L=%lld needs %zu bytes of split partials; the static scratch holds %zu",
+                    n_q, (long long)L, wsb, (size_t)kAttnScratchBytes);
+    float* ws = nullptr;
+    const hipError_t e = attn_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "attention scratch lookup");
+    return hip_status(launch_attn_decode(q, k_blk, v, o, ws, n_q, n_kv, L, l_cap,
                                          (float)(1.0 / std::sqrt((double)kAttnHeadDim)), (hipStream_t)stream),
                       "attention launch");
 }

@@ -9,14 +9,20 @@
 // consecutive positions of a dimension and no dot product crosses lanes;
 // values head-major, V [n_kv][l_cap][128].
 //
-// A workgroup takes one (kv head, 64-position split) and issues all of its
-// loads up front: 4 waves each form the partial dots over 32 head dimensions
-// for all G query heads of the group, the partials are added in a fixed
-// order, then a local softmax (maximum, exp, sum by wave reduction), then the
-// weighted sum of the split's values over 8 position slices added in order.
-// The combine rescales each split by exp(m_s - M) and adds the splits in a
-// fixed order, so results are deterministic.
+// A workgroup of 8 waves takes one (kv head, 64-position split) and issues
+// all of its loads up front.  Wave w forms the partial dots over head
+// dimensions 16w .. 16w+15 for all G query heads of the group: a thread holds
+// 4 dimensions x 4 positions of the keys, and the 4 lanes of a lane quad are
+// added by two DPP moves.  The 8 waves' partials are added in order through
+// LDS, then a local softmax per head (one wave per head: maximum, exp, sum by
+// wave reduction), then the weighted sum of the split's values: a thread
+// holds 4 dimensions x 4 positions, lane quads are added by DPP, and the 4
+// groups of 16 positions are added in order.  The combine rescales each split
+// by exp(m_s - M) and adds the splits in a fixed order, so results are
+// deterministic.
 #include "q4s_device.h"
+
+#include <mutex>
 
 namespace q4s {
 namespace {
@@ -265,6 +271,39 @@ hipError_t launch_attn_decode(const float* q, const float* kb, const float* v, f
     hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)n_q, kHd / kCombDims), dim3(kCombSlices * kCombQuads), 0, st,
                        a);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- static scratch
+//
+// The split partials of q4s_attn_decode_noalloc live in this fixed array, for
+// callers that cannot allocate device memory (code under graph capture, tight
+// serving loops).  Every GPU the library runs on holds its own copy, from the
+// first use until the process ends.  On the host the array's name only stands
+// for the symbol: its device address on the current device comes from
+// hipGetSymbolAddress, taken once per device and kept, and only that address is
+// ever handed to a kernel.
+static __device__ __align__(256) float scratch[kAttnScratchBytes / sizeof(float)];
+
+constexpr int kScratchDevices = 64;
+
+hipError_t attn_scratch(float** out) {
+    *out = nullptr;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    static std::mutex mu;
+    static void* ptr[kScratchDevices] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        ptr[dev] = p;
+    }
+    *out = (float*)ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace q4s

@@ -106,6 +106,10 @@ inline int64_t attn_splits(int64_t L) { return (L + kAttnSplit - 1) / kAttnSplit
 __host__ __device__ inline int64_t attn_split_floats(int64_t n_q) { return (n_q * (kAttnHeadDim + 2) + 3) / 4 * 4; }
 hipError_t launch_attn_decode(const float* q, const float* kb, const float* v, float* o, float* ws, int n_q,
                               int n_kv, int64_t L, int64_t l_cap, float scale, hipStream_t st);
+// The static scratch of q4s_attn_decode_noalloc: its device address on the current device (looked up
+// once per device), or an error.
+constexpr size_t kAttnScratchBytes = (size_t)8 << 20;
+hipError_t attn_scratch(float** out);
 // Grid-barrier measurement (q4s_barrier.hip); kind 0..9 (counter, flags, tree, relaxed-poll counter, spread trees, fence-free variants).
 size_t grid_barrier_scratch_words(int n_wg);
 hipError_t launch_grid_barrier(int kind, int n_wg, int phases, uint32_t* scratch, hipStream_t st);

@@ -132,6 +132,15 @@ def test_other_entry_points_validate(L):
     assert a(FAKE + 4, *ok[1:]) == 3                                    # q needs 16 bytes
     assert a(*ok[:3], FAKE, *ok[4:]) == 4                               # o overlaps q
     assert a(*ok[:8], FAKE + (1 << 28) + 64, W, None) == 4              # workspace overlaps o
+    # the allocation-free variant: the same checks, and its scratch limit, all before any HIP call
+    nz = L.q4s_attn_decode_noalloc
+    assert nz(*ok[:6], 129, 128, None) == 2                              # L > l_cap
+    assert nz(FAKE + 4, *ok[1:8], None) == 3                             # q needs 16 bytes
+    assert nz(*ok[:3], FAKE, *ok[4:8], None) == 4                        # o overlaps q
+    big = 86016 + 64                                                     # one split past 8 MiB at 12 heads
+    assert q.attn_workspace_bytes(12, big) > q.ATTN_SCRATCH_BYTES >= q.attn_workspace_bytes(12, big - 64)
+    assert nz(*ok[:6], big, big, None) == 2
+    assert "static scratch" in _err(L)
 
 
 def _plan(L, mats, n):
