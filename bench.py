@@ -129,15 +129,23 @@ def traffic_from_profile(workload: str, n: int, launch_bytes: int):
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(host, shapes, n: int, budget_s: float):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload: whole
-    passes (quantize + GEMV of every matrix of copy 0) repeated until `budget_s`
-    seconds have been spent, or matrices of one pass if a pass alone exceeds it."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_sweep_rate(host, shapes, budget_s: float):
+    """Whole passes (quantize + GEMV of every matrix of copy 0) until `budget_s` seconds have
+    been spent, or matrices of one pass if a pass alone exceeds it -> (GB/s, sample text)."""
     from oracle import oracle
-    oracle.build(force=False)
-    threads = oracle.max_threads()
     t0 = time.perf_counter()
     done_bytes, done, passes = 0, 0, 0
+    n = host[0][1].shape[0]
     while True:
         for (w, x), s in zip(host, shapes):
             xq = oracle.quantize_q8_0(x)
@@ -152,9 +160,25 @@ def cpu_baseline(host, shapes, n: int, budget_s: float):
                 continue
         break
     dt = time.perf_counter() - t0
-    return {"value": round(done_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} matrix products ({passes} whole passes over the {len(shapes)} matrices of copy 0, "
-                      f"{done_bytes} Q4_0 bytes), quantize + GEMV, {dt:.1f} s"}
+    return done_bytes / dt / 1e9, (f"{done} matrix products ({passes} whole passes over the {len(shapes)} "
+                                   f"matrices of copy 0, {done_bytes} Q4_0 bytes), quantize + GEMV, {dt:.1f} s")
+
+
+def cpu_baseline(host, shapes, n: int, budget_s: float):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload: on every host
+    thread (OpenMP over output rows), then on one thread, each for about `budget_s` / 2 s."""
+    from oracle import oracle
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    rate, sample = _oracle_sweep_rate(host, shapes, budget_s / 2)
+    oracle.set_threads(1)
+    try:
+        rate1, sample1 = _oracle_sweep_rate(host, shapes, budget_s / 2)
+    finally:
+        oracle.set_threads(threads)
+    return {"value": round(rate, 3), "unit": "GB/s", "cores": threads, "kind": "oracle", "sample": sample,
+            "cpu_model": cpu_model(), "visible_cpus": len(os.sched_getaffinity(0)),
+            "single_thread": {"value": round(rate1, 3), "unit": "GB/s", "cores": 1, "sample": sample1}}
 
 
 Q8_SRCS = [os.path.join(ROOT, "q4_weight_streaming_amd", "csrc", f)
@@ -474,47 +498,138 @@ def run_chain(args, dev, stream) -> int:
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qwen2.5-1.5b",
-                    choices=["qwen2.5-1.5b", "qwen2.5-7b", "lm_head", "gemv1536", "lm_head_q8", "attn", "chain"])
-    ap.add_argument("--chain-model", default="1.5b", choices=["1.5b", "7b"], help="stack of --workload chain")
-    ap.add_argument("--sync", default="all", choices=["all", *CHAIN_MODES], help="phase sync of --workload chain")
-    ap.add_argument("--chain-workgroups", type=int, default=0, help="persistent workgroups (0: one per CU)")
-    ap.add_argument("--context", type=int, default=32768, help="KV positions for --workload attn")
-    ap.add_argument("--n", type=int, default=1, help="activation rows per GEMV (1..24; 1..8 for lm_head_q8)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-verify-ratio", action="store_true", help="skip the N=8 / N=1 step-cost ratio")
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--verify-n", default="2,4,8,16,24",
-                    help="comma list of row counts for the step-cost curve t(N)/t(1)")
-    ap.add_argument("--profile-only", action="store_true",
-                    help="run a few GEMV-only sweeps plus a 1 GiB copy, for rocprofv3 counter runs")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU part; see DESIGN.md for how it would shard)", file=sys.stderr)
-        return 2
-    if not 1 <= args.n <= (8 if args.workload == "lm_head_q8" else 24):
-        raise SystemExit("--n must be in 1..24 (1..8 for lm_head_q8)")
+def timeline_summary(trace, n_tiles: int, waves: int, bin_us: float = 1.0) -> dict:
+    """A traced launch (q4s_sweep_set_trace: per workgroup its start and its waves' ends on
+    the 100 MHz clock) as when workgroups start and finish: the span, how fast the launch
+    reaches its peak concurrency, when the last workgroup starts, how long the last 5% and
+    the last workgroup take, and the number of workgroups running per bin."""
+    import numpy as np
+    t = trace.reshape(n_tiles, 9).astype(np.float64)
+    start = t[:, 0]
+    end = t[:, 1:1 + waves].max(axis=1)
+    t0 = start.min()
+    start, end = (start - t0) / 100.0, (end - t0) / 100.0      # us
+    span = float(end.max())
+    ev = np.concatenate([np.stack([start, np.ones_like(start)], 1), np.stack([end, -np.ones_like(end)], 1)])
+    ev = ev[np.lexsort((ev[:, 1], ev[:, 0]))]
+    conc = np.cumsum(ev[:, 1])
+    peak = float(conc.max())
+    ramp = float(ev[np.argmax(conc >= 0.9 * peak), 0])
+    done = np.sort(end)
+    edges = np.arange(0.0, span + bin_us, bin_us)
+    running = [int(((start < b + bin_us) & (end > b)).sum()) for b in edges[:-1]]
+    dur = end - start
+    return {"span_us": round(span, 2), "workgroups": n_tiles, "peak_concurrent": int(peak),
+            "ramp_to_90pct_us": round(ramp, 2), "last_start_us": round(float(start.max()), 2),
+            "drain_after_last_start_us": round(span - float(start.max()), 2),
+            "last_5pct_of_workgroups_us": round(span - float(done[int(0.95 * (n_tiles - 1))]), 2),
+            "workgroup_us_median": round(float(np.median(dur)), 2), "workgroup_us_max": round(float(dur.max()), 2),
+            "running_per_us": running}
 
+
+def sweep_plans(shapes, copies, n: int, act_cfg: int, dev):
+    """Sweeps of n activation rows over the weights of each copy, with fresh seeded activations."""
     import torch
 
     from q4_weight_streaming_amd import _lib as q
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream(dev)
-    q.lib()
+    from q4_weight_streaming_amd import synth
+    plans, mats_all = [], []
+    for c, m in enumerate(copies):
+        mats_v = []
+        for mi, (s, mm) in enumerate(zip(shapes, m)):
+            x = synth.activation(n, s.cols, synth.generator(act_cfg, mi, c, 1),
+                                 outliers=0 if s.name == "lm_head" and len(shapes) == 1 else 8)
+            mats_v.append({"w_packed": mm["w_packed"], "x": torch.from_numpy(x).to(dev),
+                           "x_q8": torch.empty(q.q8_bytes(n, s.cols), dtype=torch.uint8, device=dev),
+                           "y": torch.empty((n, s.rows), dtype=torch.float32, device=dev),
+                           "rows": s.rows, "cols": s.cols})
+        plans.append(q.Sweep(mats_v, n))
+        mats_all.append(mats_v)
+    return plans, mats_all
 
-    if args.workload == "lm_head_q8":
-        return run_q8_head(args, dev, stream)
-    if args.workload == "attn":
-        return run_attn(args, dev, stream)
-    if args.workload == "chain":
-        return run_chain(args, dev, stream)
+
+def step_kernel_name(shapes, n: int, fused: bool) -> str:
+    """The kernel that dominates a step (the whole step when it is one launch)."""
+    if fused:
+        split = n == 1 and all(s.cols <= 2048 for s in shapes)
+        return ("k_sweep_split<true> (the whole step)" if split else "k_sweep_fused (the whole step)") if n == 1 \
+            else f"k_sweep_fused<{n}> (the whole step)"
+    if n == 1:
+        return "k_sweep_one (GEMV launch of the sweep)"
+    return (f"k_sweep<{n}>" if n <= 8 else "k_sweep_tiled") + " (GEMV launch of the sweep)"
+
+
+def measure_plans(name, shapes, full, mats_all, n: int, args, stream):
+    """Times the step (the full plans) and, when the step takes two launches, the GEMV launch
+    alone over the quantized activations; returns the timings and the step's roofline."""
+    from q4_weight_streaming_amd import _lib as q
+    info = full[0].info()
+    fused = bool(info["fused_quantize"])
+    weight_bytes = info["weight_bytes"]
+    launch_bytes = info["weight_bytes"] + info["act_bytes"] + info["out_bytes"]
+    if fused:
+        # one launch per step: fp32 activations read, Q8_0 bytes written, weights, y
+        launch_bytes += sum(4 * n * s.cols for s in shapes)
+    ms = time_steps([p.run for p in full], args.steps, args.warmup, stream)
+    gemv = [q.Sweep([{k: v for k, v in mm.items() if k != "x"} for mm in m], n) for m in mats_all]
+    k_b2b = time_steps([p.run for p in gemv], args.steps, args.warmup, stream)
+    k_avg, k_med, k_min = time_kernel([p.run for p in gemv], args.steps, stream)
+    dom_ms = ms if fused else k_b2b
+    if not fused:  # the GEMV launch's bytes: Q8_0 activations read, no fp32 activations
+        launch_bytes = info["weight_bytes"] + info["act_bytes"] + info["out_bytes"]
+    achieved = launch_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile(name, n, launch_bytes)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "kernel": step_kernel_name(shapes, n, fused), "algorithmic_bytes_per_launch": launch_bytes}
+    gemv_only = {"us_back_to_back": round(k_b2b * 1e3, 2), "us_bracketed_avg": round(k_avg * 1e3, 2),
+                 "us_bracketed_median": round(k_med * 1e3, 2), "us_bracketed_min": round(k_min * 1e3, 2),
+                 "weight_gb_s": round(weight_bytes / (k_b2b * 1e-3) / 1e9, 1)}
+    for p in gemv:
+        p.close()
+    return {"ms": ms, "fused": fused, "info": info, "weight_bytes": weight_bytes, "roofline": roof,
+            "gemv_only": gemv_only}
+
+
+def extra_workload(name: str, ns, args, dev, stream) -> dict:
+    """A further configuration on the same line: the step at each row count in ns (the first
+    is 1), as weight GB/s, % of peak and the step's roofline; t(n)/t(1) for n > 1."""
+    import torch
+    shapes, cfg, ncopies = workload_shapes(name)
+    log(f"generating {ncopies} copies of {name} ({len(shapes)} matrices)")
+    copies = []
+    for c in range(ncopies):
+        mats, _ = make_copy(shapes, cfg, c, 1, dev, keep_host=False)
+        copies.append(mats)
+    res, t1 = {}, None
+    for n in ns:
+        full, mats_all = sweep_plans(shapes, copies, n, cfg if n == 1 else 3, dev)
+        r = measure_plans(name, shapes, full, mats_all, n, args, stream)
+        for p in full:
+            p.close()
+        t1 = r["ms"] if n == 1 else t1
+        gbs = r["weight_bytes"] / (r["ms"] * 1e-3) / 1e9
+        e = {"ms_per_step": round(r["ms"], 5), "weight_gb_s": round(gbs, 1),
+             "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2), "launches_per_step": 1 if r["fused"] else 2,
+             "roofline": r["roofline"], "gemv_only_us": r["gemv_only"]["us_back_to_back"]}
+        if n == 1 and name.startswith("qwen"):
+            e["tok_s"] = round(1000.0 / r["ms"], 1)
+        if n > 1 and t1:
+            e["ratio_to_n1"] = round(r["ms"] / t1, 3)
+        res[f"n{n}"] = e
+        log(f"{name} n={n}: step {r['ms'] * 1e3:.1f} us, {gbs:.0f} GB/s, roofline frac {r['roofline']['frac']}")
+        del full, mats_all
+    res["workload"] = (f"{name}: {len(shapes)} Q4_0 matrices ({sum(s.q4_bytes for s in shapes)} B), "
+                       f"{ncopies} rotated seeded copies, fresh seeded activations per matrix")
+    del copies
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_sweep(args, dev, stream) -> int:
+    import torch
+
+    from q4_weight_streaming_amd import _lib as q
     shapes, cfg, ncopies = workload_shapes(args.workload)
     n = args.n
     log(f"generating {ncopies} copies of {args.workload} ({len(shapes)} matrices), n={n}")
@@ -526,16 +641,10 @@ def main() -> int:
             host0 = host
         log(f"copy {c} ready")
     full = [q.Sweep(m, n) for m in copies]                                 # quantize + GEMV
-    gemv = [q.Sweep([{k: v for k, v in mm.items() if k != "x"} for mm in m], n) for m in copies]
-    info = gemv[0].info()
-    fused = bool(full[0].info()["fused_quantize"])
-    weight_bytes = info["weight_bytes"]
-    launch_bytes = info["weight_bytes"] + info["act_bytes"] + info["out_bytes"]
-    if fused:
-        # one launch per step: fp32 activations read, Q8_0 bytes written, weights, y
-        launch_bytes += sum(4 * n * s.cols for s in shapes)
 
     if args.profile_only:
+        info = full[0].info()
+        gemv = [q.Sweep([{k: v for k, v in mm.items() if k != "x"} for mm in m], n) for m in copies]
         for i in range(10):
             full[i % ncopies].run()              # the step (quantized activations in place)
         for i in range(10):
@@ -544,24 +653,18 @@ def main() -> int:
         dst = torch.empty_like(src)
         q.bench_copy(src, dst)
         torch.cuda.synchronize()
-        log(f"profile run done: 10 GEMV sweeps of {launch_bytes} algorithmic bytes, one 1 GiB copy")
+        log(f"profile run done: 10 steps and 10 GEMV-only sweeps ({info['weight_bytes']} weight bytes), "
+            "one 1 GiB copy")
         return 0
 
-    ms = time_steps([p.run for p in full], args.steps, args.warmup, stream)
+    r = measure_plans(args.workload, shapes, full, copies, n, args, stream)
+    ms, fused, info, weight_bytes = r["ms"], r["fused"], r["info"], r["weight_bytes"]
     log(f"step {ms * 1e3:.1f} us ({'one fused launch' if fused else 'quantize + GEMV launches'})")
-    k_b2b = time_steps([p.run for p in gemv], args.steps, args.warmup, stream)
-    k_avg, k_med, k_min = time_kernel([p.run for p in gemv], args.steps, stream)
-    log(f"GEMV-only launches back to back: {k_b2b * 1e3:.1f} us each; bracketed one by one: avg "
-        f"{k_avg * 1e3:.1f} us, median {k_med * 1e3:.1f}, min {k_min * 1e3:.1f}")
+    g = r["gemv_only"]
+    log(f"GEMV-only launches back to back: {g['us_back_to_back']:.1f} us each; bracketed one by one: avg "
+        f"{g['us_bracketed_avg']:.1f} us, median {g['us_bracketed_median']:.1f}, min {g['us_bracketed_min']:.1f}")
 
     value = weight_bytes / (ms * 1e-3) / 1e9
-    # a 1-row plan whose matrices all have at most 8 chunks (K <= 2048) runs the split-tile kernel
-    split = n == 1 and all(s.cols <= 2048 for s in shapes)
-    step_kernel = "k_sweep_split<true> (the whole step)" if split else "k_sweep_fused (the whole step)"
-    # the dominant kernel: the fused step launch itself, else the GEMV launch
-    dom_ms = ms if fused else k_b2b
-    achieved = launch_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile(args.workload, n, launch_bytes)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -583,35 +686,35 @@ def main() -> int:
                    "accumulate": "f32", "gemv_tiles": info["n_tiles"]},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "tok_s": round(1000.0 / ms, 1) if n == 1 and args.workload.startswith("qwen") else None,
-        "gemv_only": {"us_back_to_back": round(k_b2b * 1e3, 2), "us_bracketed_avg": round(k_avg * 1e3, 2),
-                      "us_bracketed_median": round(k_med * 1e3, 2), "us_bracketed_min": round(k_min * 1e3, 2),
-                      "weight_gb_s": round(weight_bytes / (k_b2b * 1e-3) / 1e9, 1)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": step_kernel if fused else ("k_sweep_one" if n == 1 else f"k_sweep<{n}>")
-                     + " (GEMV launch of the sweep)",
-                     "algorithmic_bytes_per_launch": launch_bytes},
+        "gemv_only": g,
+        "roofline": r["roofline"],
     }
+
+    if args.timeline:
+        # one traced step after the timed ones: when the step launch's workgroups start and finish
+        waves = 8 if (n == 1 and all(sh.cols <= 2048 for sh in shapes)) else 4
+        tr = full[0].set_trace(True)
+        full[1 % ncopies].run()
+        full[0].run()
+        torch.cuda.synchronize()
+        full[0].set_trace(False)
+        tl = timeline_summary(tr.cpu().numpy(), info["n_tiles"], waves)
+        out["timeline"] = tl
+        log(f"timeline: span {tl['span_us']} us, peak {tl['peak_concurrent']} workgroups, ramp {tl['ramp_to_90pct_us']} us, "
+            f"last start {tl['last_start_us']} us, drain {tl['drain_after_last_start_us']} us, "
+            f"last 5% {tl['last_5pct_of_workgroups_us']} us, workgroup median {tl['workgroup_us_median']} us")
 
     if n == 1 and not args.no_verify_ratio:
         # the same weight copies stepped with several activation rows (multi-token verify)
-        from q4_weight_streaming_amd import synth
         verify = {}
         for nv in sorted({int(v) for v in args.verify_n.split(",") if v}):
-            plans = []
-            for c, m in enumerate(copies):
-                mats_v = []
-                for mi, (s, mm) in enumerate(zip(shapes, m)):
-                    x = synth.activation(nv, s.cols, synth.generator(3, mi, c, 1))
-                    mats_v.append({"w_packed": mm["w_packed"], "x": torch.from_numpy(x).to(dev),
-                                   "x_q8": torch.empty(q.q8_bytes(nv, s.cols), dtype=torch.uint8, device=dev),
-                                   "y": torch.empty((nv, s.rows), dtype=torch.float32, device=dev),
-                                   "rows": s.rows, "cols": s.cols})
-                plans.append(q.Sweep(mats_v, nv))
+            plans, _ = sweep_plans(shapes, copies, nv, 3, dev)
             msv = time_steps([p.run for p in plans], args.steps, args.warmup, stream)
-            verify[f"n{nv}"] = {"ms_per_step": round(msv, 5), "ratio_to_n1": round(msv / ms, 3)}
+            verify[f"n{nv}"] = {"ms_per_step": round(msv, 5), "ratio_to_n1": round(msv / ms, 3),
+                                "launches_per_step": 1 if plans[0].info()["fused_quantize"] else 2}
             log(f"n={nv} step {msv * 1e3:.1f} us, ratio {msv / ms:.3f}")
+            for p in plans:
+                p.close()
             del plans
         out["verify"] = verify
 
@@ -632,10 +735,67 @@ def main() -> int:
                               "note": "one 1536x1536 GEMV per launch; the bracket holds the dispatch latency"}
         log(f"single GEMV launch: median {s_med * 1e3:.2f} us, min {s_min * 1e3:.2f} us")
 
+    if args.workload == "qwen2.5-1.5b" and n == 1 and not args.no_extra_configs:
+        # the other configurations' pass bars on the same line: the lone head, the 7B stream at N = 1 and 8
+        for p in full:
+            p.close()
+        del full, copies
+        torch.cuda.empty_cache()
+        out["lm_head"] = extra_workload("lm_head", [1], args, dev, stream)
+        out["qwen2.5-7b"] = extra_workload("qwen2.5-7b", [1, 8], args, dev, stream)
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(host0, shapes, n, args.cpu_budget)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen2.5-1.5b",
+                    choices=["qwen2.5-1.5b", "qwen2.5-7b", "lm_head", "gemv1536", "lm_head_q8", "attn", "chain"])
+    ap.add_argument("--chain-model", default="1.5b", choices=["1.5b", "7b"], help="stack of --workload chain")
+    ap.add_argument("--sync", default="all", choices=["all", *CHAIN_MODES], help="phase sync of --workload chain")
+    ap.add_argument("--chain-workgroups", type=int, default=0, help="persistent workgroups (0: one per CU)")
+    ap.add_argument("--context", type=int, default=32768, help="KV positions for --workload attn")
+    ap.add_argument("--n", type=int, default=1, help="activation rows per GEMV (1..24; 1..8 for lm_head_q8)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify-ratio", action="store_true", help="skip the N=8 / N=1 step-cost ratio")
+    ap.add_argument("--timeline", action="store_true",
+                    help="add the step launch's per-workgroup timeline (one traced step) to the line")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="with the default workload, skip the lone-head and 7B lines")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (half all-thread, half single)")
+    ap.add_argument("--verify-n", default="2,4,8,16,24",
+                    help="comma list of row counts for the step-cost curve t(N)/t(1)")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="run a few GEMV-only sweeps plus a 1 GiB copy, for rocprofv3 counter runs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU part)", file=sys.stderr)
+        return 2
+    if not 1 <= args.n <= (8 if args.workload == "lm_head_q8" else 24):
+        raise SystemExit("--n must be in 1..24 (1..8 for lm_head_q8)")
+
+    import torch
+
+    from q4_weight_streaming_amd import _lib as q
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    q.lib()
+
+    if args.workload == "lm_head_q8":
+        return run_q8_head(args, dev, stream)
+    if args.workload == "attn":
+        return run_attn(args, dev, stream)
+    if args.workload == "chain":
+        return run_chain(args, dev, stream)
+    return run_sweep(args, dev, stream)
 
 
 if __name__ == "__main__":

@@ -368,6 +368,19 @@ q4s_status q4s_sweep_run(const q4s_plan* plan, void* stream);
 
 q4s_status q4s_sweep_plan_info(const q4s_plan* plan, q4s_plan_info* info);
 
+/*
+ * Timeline of later runs' GEMV launch (the pages' clock-delta profiling of the
+ * decode step, milestone M19): with a trace buffer set, for workgroup b of the
+ * launch (b < n_tiles of q4s_sweep_plan_info), word 9b receives the GPU's
+ * 100 MHz constant clock when b started and word 9b + 1 + w when its wave w
+ * finished (4 waves, or 8 for the 1-row plans whose matrices all have at most
+ * 8 chunks); other words are left untouched.  trace: q4s_sweep_trace_bytes
+ * bytes of device memory (8-byte aligned); NULL turns it off.  Plans of more
+ * than 8 rows cannot be traced (Q4S_ERR_PLAN).
+ */
+size_t q4s_sweep_trace_bytes(const q4s_plan* plan);
+q4s_status q4s_sweep_set_trace(q4s_plan* plan, uint64_t* trace, size_t trace_bytes);
+
 void q4s_sweep_plan_destroy(q4s_plan* plan);
 
 /* ------------------------------------------------------ chained step */
@@ -498,6 +511,25 @@ q4s_status q4s_chain_get_info(const q4s_chain* chain, q4s_chain_info* info);
  */
 size_t q4s_chain_trace_bytes(const q4s_chain* chain);
 q4s_status q4s_chain_set_trace(q4s_chain* chain, uint64_t* trace, size_t trace_bytes);
+
+/*
+ * Test hook: the Q8_0 input each phase's GEMVs read, as staged by the step
+ * (after the wait, the RMS norm where the phase has one, the quantization;
+ * or, for o and down, the codes their producers wrote).  With a dump buffer
+ * set, every later step writes, for phase p (4 per layer: q/k/v, o, gate/up,
+ * down; then the head) and chunk c of the phase's activation (256 values),
+ * at word (p * C + c) * 64 + l, C = max(ceil(E/256), ceil(F/256)): the code
+ * dword l of the chunk (int8 values 256c + 4l .. 256c + 4l + 3, low byte
+ * first; zero past the vector) in the low half and the fp32 bits of the
+ * binary16 d_x of its block (8c + l/8) in the high half.  Words of chunks a
+ * phase does not have are left untouched.  dump:
+ * q4s_chain_stage_dump_bytes bytes of device memory (8-byte aligned); NULL
+ * turns it off.  Source: the pages validate every GPU kernel of the decode
+ * step against the CPU reference ("How it works", src/cpu_infer.cpp bullet;
+ * milestones M15, M19).
+ */
+size_t q4s_chain_stage_dump_bytes(const q4s_chain* chain);
+q4s_status q4s_chain_set_stage_dump(q4s_chain* chain, uint64_t* dump, size_t dump_bytes);
 
 void q4s_chain_destroy(q4s_chain* chain);
 

@@ -247,6 +247,15 @@ def rmsnorm(x: np.ndarray):
     return out, float(ss)
 
 
+def rmsnorm_f64(x: np.ndarray) -> np.ndarray:
+    """The RMS norm of the chained step by its plain definition, in fp64 and with no
+    prescribed summation order: x / sqrt(mean(x^2) + 1e-6) -- Qwen2.5's RMS norm with its
+    epsilon of 1e-6 and no learned weight (the synthetic model's norm weights are 1); the
+    pages name the "norm prologues" of milestone M19 without a formula.  Returns float64."""
+    x64 = np.asarray(x, dtype=np.float64)
+    return x64 / np.sqrt(np.mean(x64 * x64) + 1e-6)
+
+
 def chain_layout(E: int, D: int, F: int):
     """Offsets of q, k, v, o, h1, g, u, dn, h2 within one layer's block of activations."""
     sizes = [("q", E), ("k", D), ("v", D), ("o", E), ("h1", E), ("g", F), ("u", F), ("dn", E), ("h2", E)]

@@ -93,6 +93,8 @@ def lib():
             "q4s_sweep_run": ([p, p], i32),
             "q4s_sweep_plan_info": ([p, ctypes.POINTER(PlanInfo)], i32),
             "q4s_sweep_plan_destroy": ([p], None),
+            "q4s_sweep_trace_bytes": ([p], sz),
+            "q4s_sweep_set_trace": ([p, p, sz], i32),
             "q4s_chain_act_words": ([ctypes.POINTER(ChainShape)], i64),
             "q4s_chain_create": ([ctypes.POINTER(ChainShape), p, p, p, p, i32, i32, ctypes.POINTER(sz),
                                   ctypes.POINTER(p)], i32),
@@ -104,6 +106,8 @@ def lib():
             "q4s_chain_trace_bytes": ([p], sz),
             "q4s_chain_set_trace": ([p, p, sz], i32),
             "q4s_chain_set_wait_limit": ([p, ctypes.c_uint32], i32),
+            "q4s_chain_stage_dump_bytes": ([p], sz),
+            "q4s_chain_set_stage_dump": ([p, p, sz], i32),
             "q4s_bench_read": ([p, sz, i32, i32, p, p], i32),
             "q4s_bench_read_units": ([p, sz, sz, p, p], i32),
             "q4s_bench_copy": ([p, p, sz, p], i32),
@@ -370,6 +374,18 @@ class Sweep:
     def run(self) -> None:
         _check("q4s_sweep_run", lib().q4s_sweep_run(self._plan, _stream(self.device)))
 
+    def set_trace(self, on: bool) -> torch.Tensor | None:
+        """Record the GEMV launch's timeline in later runs; returns the zeroed int64 tensor
+        [n_tiles][9] (word 0: workgroup start, 1 + w: wave w done; 100 MHz clock)."""
+        if not on:
+            _check("q4s_sweep_set_trace", lib().q4s_sweep_set_trace(self._plan, None, 0))
+            self._trace = None
+            return None
+        n = int(lib().q4s_sweep_trace_bytes(self._plan)) // 8
+        self._trace = torch.zeros(max(n, 1), dtype=torch.int64, device=self.device)
+        _check("q4s_sweep_set_trace", lib().q4s_sweep_set_trace(self._plan, self._trace.data_ptr(), n * 8))
+        return self._trace
+
     def close(self) -> None:
         if self._plan:
             lib().q4s_sweep_plan_destroy(self._plan)
@@ -444,6 +460,18 @@ class Chain:
         self._trace = torch.zeros(n, dtype=torch.int64, device=self.device)
         _check("q4s_chain_set_trace", lib().q4s_chain_set_trace(self._chain, self._trace.data_ptr(), n * 8))
         return self._trace
+
+    def set_stage_dump(self, on: bool) -> torch.Tensor | None:
+        """Test hook: record the staged Q8_0 input of every phase of later steps; returns the
+        int64 dump tensor [n_phases][C][64] (code dword | d_x fp32 bits << 32, see q4s.h)."""
+        if not on:
+            _check("q4s_chain_set_stage_dump", lib().q4s_chain_set_stage_dump(self._chain, None, 0))
+            self._dump = None
+            return None
+        nbytes = int(lib().q4s_chain_stage_dump_bytes(self._chain))
+        self._dump = torch.zeros(nbytes // 8, dtype=torch.int64, device=self.device)
+        _check("q4s_chain_set_stage_dump", lib().q4s_chain_set_stage_dump(self._chain, self._dump.data_ptr(), nbytes))
+        return self._dump
 
     def set_wait_limit(self, polls: int) -> None:
         _check("q4s_chain_set_wait_limit", lib().q4s_chain_set_wait_limit(self._chain, polls))

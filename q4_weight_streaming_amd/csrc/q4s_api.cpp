@@ -388,6 +388,7 @@ struct q4s_plan {
     size_t off_mats = 0, off_quant = 0, off_tiles = 0, off_qtiles = 0, dev_bytes = 0;
     std::vector<uint8_t> image;
     uint8_t* dev = nullptr;
+    uint64_t* trace = nullptr;       // the GEMV launch's timeline, or NULL
 };
 
 q4s_status q4s_sweep_plan_create(const q4s_mat* mats, int n_mats, int n, size_t* dev_bytes_needed,
@@ -432,7 +433,10 @@ q4s_status q4s_sweep_plan_create(const q4s_mat* mats, int n_mats, int n, size_t*
     if (!p) return fail(Q4S_ERR_PLAN, "out of host memory");
     p->n = n;
     // One activation row, every matrix live and given as fp32: the GEMV waves
-    // quantize the activation themselves (no separate quantize launch).
+    // quantize the activation themselves (no separate quantize launch).  With 2..8
+    // rows the quantization stays a launch of its own: the many-row dots leave the
+    // waves no spare VALU issue (quantizing inside them took the 8-row step of the
+    // Qwen2.5-1.5B sweep from 172 to 231 us).
     p->fused = n == 1 && n_mats > 0;
     for (int i = 0; i < n_mats && p->fused; ++i) {
         const q4s_mat& a = mats[i];
@@ -533,16 +537,12 @@ q4s_status q4s_sweep_run(const q4s_plan* p, void* stream) {
     if (!p) return fail(Q4S_ERR_NULL, "plan is NULL");
     if (!p->dev) return fail(Q4S_ERR_PLAN, "plan was not uploaded");
     hipStream_t st = (hipStream_t)stream;
+    const MatDesc* mats = (const MatDesc*)(p->dev + p->off_mats);
+    const uint32_t* tiles = (const uint32_t*)(p->dev + p->off_tiles);
+    const int64_t n_tiles = (int64_t)p->tiles.size() / 2;
     if (p->split_tiles && p->fused)
-        return hip_status(launch_sweep_split((const MatDesc*)(p->dev + p->off_mats),
-                                            (const uint32_t*)(p->dev + p->off_tiles), (int64_t)p->tiles.size() / 2,
-                                            true, st),
-                          "sweep launch");
-    if (p->fused)
-        return hip_status(launch_sweep_fused((const MatDesc*)(p->dev + p->off_mats),
-                                             (const uint32_t*)(p->dev + p->off_tiles), (int64_t)p->tiles.size() / 2,
-                                             st),
-                          "sweep launch");
+        return hip_status(launch_sweep_split(mats, tiles, n_tiles, true, p->trace, st), "sweep launch");
+    if (p->fused) return hip_status(launch_sweep_fused(mats, tiles, n_tiles, p->trace, st), "sweep launch");
     if (!p->quant.empty()) {
         hipError_t e = launch_quantize_batch((const QuantDesc*)(p->dev + p->off_quant),
                                              (const uint32_t*)(p->dev + p->off_qtiles),
@@ -550,14 +550,28 @@ q4s_status q4s_sweep_run(const q4s_plan* p, void* stream) {
         if (e != hipSuccess) return hip_status(e, "sweep quantize launch");
     }
     if (p->split_tiles)
-        return hip_status(launch_sweep_split((const MatDesc*)(p->dev + p->off_mats),
-                                            (const uint32_t*)(p->dev + p->off_tiles), (int64_t)p->tiles.size() / 2,
-                                            false, st),
-                          "sweep launch");
-    return hip_status(launch_sweep((const MatDesc*)(p->dev + p->off_mats),
-                                   (const uint32_t*)(p->dev + p->off_tiles), (int64_t)p->tiles.size() / 2,
-                                   p->n, st),
+        return hip_status(launch_sweep_split(mats, tiles, n_tiles, false, p->trace, st), "sweep launch");
+    // the tiled many-row kernels are not traced
+    return hip_status(launch_sweep(mats, tiles, n_tiles, p->n, p->n <= kTokTile ? p->trace : nullptr, st),
                       "sweep launch");
+}
+
+size_t q4s_sweep_trace_bytes(const q4s_plan* p) {
+    if (!p) return 0;
+    return p->tiles.size() / 2 * kSweepTraceWords * 8;
+}
+
+q4s_status q4s_sweep_set_trace(q4s_plan* p, uint64_t* trace, size_t trace_bytes) {
+    if (!p) return fail(Q4S_ERR_NULL, "plan is NULL");
+    if (trace) {
+        q4s_status s;
+        const size_t need = q4s_sweep_trace_bytes(p);
+        if ((s = check_ptr(trace, need, 8, "trace"))) return s;
+        if (trace_bytes < need) return fail(Q4S_ERR_SHAPE, "trace holds %zu bytes, needs %zu", trace_bytes, need);
+        if (p->n > kTokTile) return fail(Q4S_ERR_PLAN, "the timeline covers steps of at most 8 rows");
+    }
+    p->trace = trace;
+    return ok();
 }
 
 q4s_status q4s_sweep_plan_info(const q4s_plan* p, q4s_plan_info* info) {
@@ -597,6 +611,7 @@ struct q4s_chain {
     uint32_t gen = 0;
     int64_t steps = 0;
     uint64_t* trace = nullptr;
+    uint64_t* dump = nullptr;
     uint32_t spin_limit = kChainDefaultSpin;
 };
 
@@ -865,6 +880,11 @@ q4s_status q4s_chain_upload(q4s_chain* p, void* dev_mem, size_t dev_bytes, void*
     return ok();
 }
 
+// chunks per phase in the staged-input dump: those of the widest activation (E or F)
+static int64_t chain_dump_chunks(const q4s_chain* p) {
+    return std::max(chunks_of(p->shape.hidden), chunks_of(p->shape.ff));
+}
+
 q4s_status q4s_chain_run(q4s_chain* p, void* stream) {
     if (!p) return fail(Q4S_ERR_NULL, "chain is NULL");
     if (!p->dev) return fail(Q4S_ERR_PLAN, "chain was not uploaded");
@@ -877,6 +897,8 @@ q4s_status q4s_chain_run(q4s_chain* p, void* stream) {
     cp.n_phases = (int32_t)p->phase_end.size();
     cp.gen = p->gen;
     cp.trace = p->trace;
+    cp.dump = p->dump;
+    cp.dump_chunks = (int32_t)chain_dump_chunks(p);
     q4s_status s =
         hip_status(launch_chain(p->mode, cp, p->workgroups, p->spin_limit, (hipStream_t)stream), "chain launch");
     if (s == Q4S_OK) ++p->steps;
@@ -909,6 +931,23 @@ q4s_status q4s_chain_set_trace(q4s_chain* p, uint64_t* trace, size_t trace_bytes
         if (trace_bytes < need) return fail(Q4S_ERR_SHAPE, "trace holds %zu bytes, needs %zu", trace_bytes, need);
     }
     p->trace = trace;
+    return ok();
+}
+
+size_t q4s_chain_stage_dump_bytes(const q4s_chain* p) {
+    if (!p) return 0;
+    return (size_t)p->phase_end.size() * (size_t)chain_dump_chunks(p) * 64 * 8;
+}
+
+q4s_status q4s_chain_set_stage_dump(q4s_chain* p, uint64_t* dump, size_t dump_bytes) {
+    if (!p) return fail(Q4S_ERR_NULL, "chain is NULL");
+    if (dump) {
+        q4s_status s;
+        const size_t need = q4s_chain_stage_dump_bytes(p);
+        if ((s = check_ptr(dump, need, 8, "dump"))) return s;
+        if (dump_bytes < need) return fail(Q4S_ERR_SHAPE, "dump holds %zu bytes, needs %zu", dump_bytes, need);
+    }
+    p->dump = dump;
     return ok();
 }
 

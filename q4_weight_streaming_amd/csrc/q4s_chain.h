@@ -42,6 +42,8 @@ struct ChainParams {
     const uint32_t* phase_end;  // cumulative tile count at the end of each phase
     uint32_t* sync;             // error word, then barrier counters (zeroed before every launch)
     uint64_t* trace;            // NULL, or the phase timeline (see q4s_chain_set_trace; 100 MHz clock)
+    uint64_t* dump;             // NULL, or the staged Q8_0 inputs [phase][chunk < dump_chunks][lane]
+    int32_t dump_chunks;        // chunks per phase in dump (those of the widest activation)
     int32_t n_phases;
     uint32_t gen;               // this step's tag (never 0)
 };

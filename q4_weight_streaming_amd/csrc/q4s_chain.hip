@@ -430,6 +430,7 @@ struct ActStaged {
     int phase;
     bool staged;
     uint64_t* mark;  // NULL, or where to record when the first tile of the phase had its activation
+    uint64_t* dump;  // NULL, or where the phase's staged codes are copied ([chunk][lane] words)
     struct Prep {
         uint32_t packed;
         uint32_t dbits;
@@ -453,6 +454,13 @@ struct ActStaged {
             if (gen == 0) err[2] = touch;  // never taken (tags start at 1); keeps the touches
             staged = true;
             key = {phase, c0, c1};
+            if (dump) {  // test hook: the lane's code word and d_x bits of every staged chunk
+                const int lane = threadIdx.x & 63;
+                for (int cc = 0; cc < c1 - c0; ++cc) {
+                    const u32x2 e = slice[cc * 64 + lane];
+                    gwr<uint64_t>(dump)[(size_t)(c0 + cc) * 64 + lane] = ((uint64_t)e[1] << 32) | e[0];
+                }
+            }
             if (mark && threadIdx.x == 0) gwr<uint64_t>(mark)[0] = __builtin_amdgcn_s_memrealtime();
         }
         const u32x2 e = slice[(c - c0) * 64 + (threadIdx.x & 63)];
@@ -468,7 +476,7 @@ struct ActStaged {
 template <int kSync>
 __device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, float* red, Q4S_LDS u32x2* stage,
                                            StageKey& key, int phase, uint32_t gen, uint32_t* err,
-                                           uint64_t* mark_start, uint64_t* mark_ready) {
+                                           uint64_t* mark_start, uint64_t* mark_ready, uint64_t* dump) {
     if (mark_start && threadIdx.x == 0) gwr<uint64_t>(mark_start)[0] = __builtin_amdgcn_s_memrealtime();
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -487,7 +495,7 @@ __device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, flo
     uint64_t rword = 0;
     if (cm.res && !cm.res_plain && sp == 0 && g < m.G) rword = chain_ld<kSync>((const uint64_t*)cm.res + rrow);
     ActStaged<kSync> act{cm, m.w, g, c0, c1, gen, err, stage + wave * (kChainMaxChunks * 64), key, phase, false,
-                         mark_ready};
+                         mark_ready, dump};
     wave_task<1>(m, (int)g, c0, c1, acc, act);
     float v = acc[0];
     if (ks > 1 || cm.w2) {
@@ -564,7 +572,7 @@ template <int kSync, int kWpg>
 __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t tile, float* red,
                                                  Q4S_LDS u32x2* stage, Q4S_LDS uint32_t* terms, StageKey& key,
                                                  int phase, uint32_t gen, uint32_t* err, uint64_t* mark_start,
-                                                 uint64_t* mark_ready) {
+                                                 uint64_t* mark_ready, uint64_t* dump) {
     if (mark_start && threadIdx.x == 0) gwr<uint64_t>(mark_start)[0] = __builtin_amdgcn_s_memrealtime();
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -584,7 +592,8 @@ __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t til
     const int i0 = split_first<kWpg>(lw, C), i1 = split_first<kWpg>(lw + 1, C);
     if (live && i0 < i1) {
         Q4S_LDS u32x2* slice = stage + wave * (kChainMaxChunks * 64);
-        ActStaged<kSync> act{cm, m.w, g, i0, i1, gen, err, slice, key, phase, false, wave == 0 ? mark_ready : nullptr};
+        ActStaged<kSync> act{cm, m.w, g, i0, i1, gen, err, slice, key, phase, false, wave == 0 ? mark_ready : nullptr,
+                             dump};
         const uint8_t* wp = m.w + ((size_t)g * m.C + i0) * kChunkBytes + lane * kBlockNibBytes;
         Chunk a, b;
         load_chunk(a, wp);
@@ -662,7 +671,8 @@ __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t til
 template <int kSync>
 __device__ __forceinline__ void chain_tile_range(const ChainMat& cm, int64_t idx, float* red, Q4S_LDS u32x2* stage,
                                                  Q4S_LDS uint32_t* terms, StageKey& key, int phase, uint32_t gen,
-                                                 uint32_t* err, uint64_t* mark_start, uint64_t* mark_ready) {
+                                                 uint32_t* err, uint64_t* mark_start, uint64_t* mark_ready,
+                                                 uint64_t* dump) {
     if (mark_start && threadIdx.x == 0) gwr<uint64_t>(mark_start)[0] = __builtin_amdgcn_s_memrealtime();
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -681,7 +691,8 @@ __device__ __forceinline__ void chain_tile_range(const ChainMat& cm, int64_t idx
     const int i0 = c0 + split_first<4>(wave, n), i1 = c0 + split_first<4>(wave + 1, n);
     if (i0 < i1) {
         Q4S_LDS u32x2* slice = stage + wave * (kChainMaxChunks * 64);
-        ActStaged<kSync> act{cm, m.w, g, i0, i1, gen, err, slice, key, phase, false, wave == 0 ? mark_ready : nullptr};
+        ActStaged<kSync> act{cm, m.w, g, i0, i1, gen, err, slice, key, phase, false, wave == 0 ? mark_ready : nullptr,
+                             dump};
         const uint8_t* wp = m.w + ((size_t)g * m.C + i0) * kChunkBytes + lane * kBlockNibBytes;
         Chunk a, b;
         load_chunk(a, wp);
@@ -823,17 +834,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_chain(ChainParams P) {
             uint64_t* ms = P.trace && j == j0 ? P.trace + plane + nwg + slot : nullptr;
             uint64_t* mr = P.trace && j == j0 ? P.trace + 2 * plane + nwg + slot : nullptr;
             const uint32_t tw = P.tiles[2 * (size_t)t + 1];
+            uint64_t* dp = P.dump ? P.dump + (size_t)p * P.dump_chunks * 64 : nullptr;
             if (tw & kChainSplit4)  // one row group, its chunks spread over the 4 waves
                 chain_tile_split<kSync, 4>(cm, tw & kChainTileIndex, red, (Q4S_LDS u32x2*)stage,
-                                           (Q4S_LDS uint32_t*)terms, key, p, P.gen, P.sync, ms, mr);
+                                           (Q4S_LDS uint32_t*)terms, key, p, P.gen, P.sync, ms, mr, dp);
             else if (tw & kChainSplit2)  // two row groups, two waves each
                 chain_tile_split<kSync, 2>(cm, tw & kChainTileIndex, red, (Q4S_LDS u32x2*)stage,
-                                           (Q4S_LDS uint32_t*)terms, key, p, P.gen, P.sync, ms, mr);
+                                           (Q4S_LDS uint32_t*)terms, key, p, P.gen, P.sync, ms, mr, dp);
             else if (kSync == kChainTagged && (tw & kChainRange))  // one K range of a row group
                 chain_tile_range<kSync>(cm, tw & kChainTileIndex, red, (Q4S_LDS u32x2*)stage,
-                                        (Q4S_LDS uint32_t*)terms, key, p, P.gen, P.sync, ms, mr);
+                                        (Q4S_LDS uint32_t*)terms, key, p, P.gen, P.sync, ms, mr, dp);
             else  // a group set: one wave per row group (or K range)
-                chain_tile<kSync>(cm, tw, red, (Q4S_LDS u32x2*)stage, key, p, P.gen, P.sync, ms, mr);
+                chain_tile<kSync>(cm, tw, red, (Q4S_LDS u32x2*)stage, key, p, P.gen, P.sync, ms, mr, dp);
             __syncthreads();
         }
         if (P.trace && threadIdx.x == 0)  // when this workgroup is done with the phase

@@ -81,15 +81,17 @@ hipError_t launch_quantize_batch(const QuantDesc* dev_descs, const uint32_t* dev
                                  hipStream_t st);
 hipError_t launch_gemv(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st);
 // Tiles are (matrix, group set) pairs; with n == 1 a single-split matrix's tiles are its row groups.
+// trace: NULL, or the launch's timeline (kSweepTraceWords words per workgroup, see q4s_sweep_set_trace).
+constexpr int kSweepTraceWords = 9;
 hipError_t launch_sweep(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles,
-                        int n, hipStream_t st);
+                        int n, uint64_t* trace, hipStream_t st);
 hipError_t launch_block_sums(const MatDesc& m, int n, int32_t* s, hipStream_t st);
 // 1-row sweeps whose matrices all have one K split: one 8-wave workgroup per (matrix, row group) entry.
 hipError_t launch_sweep_split(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles, bool fused,
-                             hipStream_t st);
+                             uint64_t* trace, hipStream_t st);
 // The 1-row sweep with the activation quantized by the GEMV waves themselves (tiles as launch_sweep's at n == 1).
 hipError_t launch_sweep_fused(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles,
-                              hipStream_t st);
+                              uint64_t* trace, hipStream_t st);
 // Q8_0 weights (q4s_q8w.hip).
 hipError_t launch_repack_q8_0(const uint8_t* w, uint8_t* packed, int64_t rows, int64_t cols,
                               hipStream_t st);

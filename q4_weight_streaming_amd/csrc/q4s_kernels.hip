@@ -26,6 +26,26 @@
 namespace q4s {
 namespace {
 
+// ---------------------------------------------------------------- timeline
+//
+// With a trace buffer (q4s_sweep_set_trace), a sweep launch records, per
+// workgroup b, the 100 MHz constant clock when it started (word 9b) and when
+// each of its waves w finished its work (word 9b + 1 + w).  NULL: nothing.
+constexpr int kTraceWords = kSweepTraceWords;
+
+// Traced kernels are separate instantiations (kTrace), so the untraced ones
+// keep their code; a traced one reads the clock when it starts and stores
+// both marks only when it is done, so that no store precedes the weight loads.
+__device__ __forceinline__ uint64_t trace_clock() { return __builtin_amdgcn_s_memrealtime(); }
+
+__device__ __forceinline__ void trace_marks(uint64_t* trace, uint64_t start) {
+    if ((threadIdx.x & 63) == 0) {
+        auto* t = gwr<uint64_t>(trace) + (size_t)blockIdx.x * kTraceWords;
+        if (threadIdx.x == 0) t[0] = start;
+        t[1 + (threadIdx.x >> 6)] = __builtin_amdgcn_s_memrealtime();
+    }
+}
+
 // ---------------------------------------------------------------- MFMA path (n >= 2)
 //
 // For 2..8 activation rows the per-block dots run on the matrix cores with
@@ -199,14 +219,17 @@ __global__ __launch_bounds__(kThreads, N == 1 ? 1 : 2) void k_gemv(MatDesc m) {
 // The sweep: workgroup i takes tile i = (matrix, group set) of a table sorted
 // by tile size, largest first, so the hardware dispatcher's in-order
 // assignment to free slots is a longest-first list schedule.
-template <int N>
+template <int N, bool kTrace>
 __global__ __launch_bounds__(kThreads, N == 1 ? 1 : 2) void k_sweep(const MatDesc* __restrict__ mats,
-                                                    const uint32_t* __restrict__ tiles) {
+                                                    const uint32_t* __restrict__ tiles,
+                                                    uint64_t* __restrict__ trace) {
     __shared__ TileLds<N> l;
+    const uint64_t t_start = kTrace ? trace_clock() : 0;
     const uint32_t mi = tiles[2 * (size_t)blockIdx.x];
     const uint32_t gs = tiles[2 * (size_t)blockIdx.x + 1];
     const MatDesc m = mats[mi];
     run_any<N>(m, gs, l);
+    if constexpr (kTrace) trace_marks(trace, t_start);
 }
 
 // ---------------------------------------------------------------- tiled steps (9..24 rows)
@@ -463,12 +486,15 @@ __device__ __forceinline__ void split_group(const MatDesc& m, int g, SplitLds& l
     }
 }
 
-template <bool kFused, int kW>
+template <bool kFused, int kW, bool kTrace>
 __global__ __launch_bounds__(64 * kW) void k_sweep_split(const MatDesc* __restrict__ mats,
-                                                          const uint32_t* __restrict__ tiles) {
+                                                          const uint32_t* __restrict__ tiles,
+                                                          uint64_t* __restrict__ trace) {
     __shared__ SplitLds l;
+    const uint64_t t_start = kTrace ? trace_clock() : 0;
     const MatDesc m = mats[tiles[2 * (size_t)blockIdx.x]];
     split_group<kFused, kW>(m, (int)tiles[2 * (size_t)blockIdx.x + 1], l);
+    if constexpr (kTrace) trace_marks(trace, t_start);
 }
 
 template <int kW>
@@ -515,17 +541,25 @@ __device__ __forceinline__ void sweep_row1(const MatDesc& m, uint32_t t, FusedLd
     }
 }
 
+template <bool kTrace>
 __global__ __launch_bounds__(kThreads, 1) void k_sweep_fused(const MatDesc* __restrict__ mats,
-                                                            const uint32_t* __restrict__ tiles) {
+                                                            const uint32_t* __restrict__ tiles,
+                                                            uint64_t* __restrict__ trace) {
     __shared__ FusedLds l;
+    const uint64_t t_start = kTrace ? trace_clock() : 0;
     sweep_row1<true>(mats[tiles[2 * (size_t)blockIdx.x]], tiles[2 * (size_t)blockIdx.x + 1], l);
+    if constexpr (kTrace) trace_marks(trace, t_start);
 }
 
 // The same tiles over activations quantized beforehand.
+template <bool kTrace>
 __global__ __launch_bounds__(kThreads, 1) void k_sweep_one(const MatDesc* __restrict__ mats,
-                                                          const uint32_t* __restrict__ tiles) {
+                                                          const uint32_t* __restrict__ tiles,
+                                                          uint64_t* __restrict__ trace) {
     __shared__ FusedLds l;
+    const uint64_t t_start = kTrace ? trace_clock() : 0;
     sweep_row1<false>(mats[tiles[2 * (size_t)blockIdx.x]], tiles[2 * (size_t)blockIdx.x + 1], l);
+    if constexpr (kTrace) trace_marks(trace, t_start);
 }
 
 // ---------------------------------------------------------------- measurement
@@ -638,12 +672,15 @@ hipError_t launch_gemv(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st)
 }
 
 template <int N>
-static void sweep_n(const MatDesc* mats, const uint32_t* tiles, int64_t n_tiles, hipStream_t st) {
-    hipLaunchKernelGGL(k_sweep<N>, dim3((unsigned)n_tiles), dim3(kThreads), 0, st, mats, tiles);
+static void sweep_n(const MatDesc* mats, const uint32_t* tiles, int64_t n_tiles, uint64_t* trace, hipStream_t st) {
+    if (trace)
+        hipLaunchKernelGGL((k_sweep<N, true>), dim3((unsigned)n_tiles), dim3(kThreads), 0, st, mats, tiles, trace);
+    else
+        hipLaunchKernelGGL((k_sweep<N, false>), dim3((unsigned)n_tiles), dim3(kThreads), 0, st, mats, tiles, trace);
 }
 
 hipError_t launch_sweep(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles, int n,
-                        hipStream_t st) {
+                        uint64_t* trace, hipStream_t st) {
     if (n_tiles == 0 || n == 0) return hipSuccess;
     if (n > kTokTile) {
         const int tt = (n + kTokTile - 1) / kTokTile;
@@ -653,34 +690,49 @@ hipError_t launch_sweep(const MatDesc* dev_mats, const uint32_t* dev_tiles, int6
     }
     switch (n) {
         case 1:  // tiles of single-split matrices are row groups (split tiles)
-            hipLaunchKernelGGL(k_sweep_one, dim3((unsigned)n_tiles), dim3(kThreads), 0, st, dev_mats, dev_tiles);
+            if (trace)
+                hipLaunchKernelGGL(k_sweep_one<true>, dim3((unsigned)n_tiles), dim3(kThreads), 0, st, dev_mats,
+                                   dev_tiles, trace);
+            else
+                hipLaunchKernelGGL(k_sweep_one<false>, dim3((unsigned)n_tiles), dim3(kThreads), 0, st, dev_mats,
+                                   dev_tiles, trace);
             break;
-        case 2: sweep_n<2>(dev_mats, dev_tiles, n_tiles, st); break;
-        case 3: sweep_n<3>(dev_mats, dev_tiles, n_tiles, st); break;
-        case 4: sweep_n<4>(dev_mats, dev_tiles, n_tiles, st); break;
-        case 5: sweep_n<5>(dev_mats, dev_tiles, n_tiles, st); break;
-        case 6: sweep_n<6>(dev_mats, dev_tiles, n_tiles, st); break;
-        case 7: sweep_n<7>(dev_mats, dev_tiles, n_tiles, st); break;
-        case 8: sweep_n<8>(dev_mats, dev_tiles, n_tiles, st); break;
+        case 2: sweep_n<2>(dev_mats, dev_tiles, n_tiles, trace, st); break;
+        case 3: sweep_n<3>(dev_mats, dev_tiles, n_tiles, trace, st); break;
+        case 4: sweep_n<4>(dev_mats, dev_tiles, n_tiles, trace, st); break;
+        case 5: sweep_n<5>(dev_mats, dev_tiles, n_tiles, trace, st); break;
+        case 6: sweep_n<6>(dev_mats, dev_tiles, n_tiles, trace, st); break;
+        case 7: sweep_n<7>(dev_mats, dev_tiles, n_tiles, trace, st); break;
+        case 8: sweep_n<8>(dev_mats, dev_tiles, n_tiles, trace, st); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_sweep_split(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles, bool fused,
-                             hipStream_t st) {
+                             uint64_t* trace, hipStream_t st) {
     if (n_tiles == 0) return hipSuccess;
-    if (fused)
-        hipLaunchKernelGGL((k_sweep_split<true, kSplitWaves>), dim3((unsigned)n_tiles), dim3(64 * kSplitWaves), 0, st, dev_mats, dev_tiles);
+    const dim3 grid((unsigned)n_tiles), block(64 * kSplitWaves);
+    if (fused && trace)
+        hipLaunchKernelGGL((k_sweep_split<true, kSplitWaves, true>), grid, block, 0, st, dev_mats, dev_tiles, trace);
+    else if (fused)
+        hipLaunchKernelGGL((k_sweep_split<true, kSplitWaves, false>), grid, block, 0, st, dev_mats, dev_tiles, trace);
+    else if (trace)
+        hipLaunchKernelGGL((k_sweep_split<false, kSplitWaves, true>), grid, block, 0, st, dev_mats, dev_tiles, trace);
     else
-        hipLaunchKernelGGL((k_sweep_split<false, kSplitWaves>), dim3((unsigned)n_tiles), dim3(64 * kSplitWaves), 0, st, dev_mats, dev_tiles);
+        hipLaunchKernelGGL((k_sweep_split<false, kSplitWaves, false>), grid, block, 0, st, dev_mats, dev_tiles, trace);
     return hipGetLastError();
 }
 
 hipError_t launch_sweep_fused(const MatDesc* dev_mats, const uint32_t* dev_tiles, int64_t n_tiles,
-                              hipStream_t st) {
+                              uint64_t* trace, hipStream_t st) {
     if (n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_sweep_fused, dim3((unsigned)n_tiles), dim3(kThreads), 0, st, dev_mats, dev_tiles);
+    if (trace)
+        hipLaunchKernelGGL(k_sweep_fused<true>, dim3((unsigned)n_tiles), dim3(kThreads), 0, st, dev_mats, dev_tiles,
+                           trace);
+    else
+        hipLaunchKernelGGL(k_sweep_fused<false>, dim3((unsigned)n_tiles), dim3(kThreads), 0, st, dev_mats, dev_tiles,
+                           trace);
     return hipGetLastError();
 }
 

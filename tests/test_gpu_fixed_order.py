@@ -1,7 +1,10 @@
-"""The GEMV entry points equal the oracle's fixed-order fp32 GEMV (the reading of
-milestone M16: one rounded expression per block and one accumulation order)
-bit for bit: 1-row dot4 path, 2..8-row MFMA path and 9..24-row tiled path, at
-shapes covering one, two and four K splits, segments and ragged tails."""
+"""Order and determinism checks: the GEMV entry points equal the oracle's
+fixed-order fp32 GEMV (a transcription of the kernels' own summation order, the
+reading of milestone M16: one rounded expression per block and one
+accumulation order) bit for bit: 1-row dot4 path, 2..8-row MFMA path and
+9..24-row tiled path, at shapes covering one, two and four K splits, segments
+and ragged tails.  The parity bar itself -- within 1e-5 * sum|terms| of the fp64
+definition -- is checked in test_gpu_kernels.py and test_gpu_sweep.py."""
 import numpy as np
 import pytest
 import torch
@@ -24,7 +27,9 @@ def test_gemv_equals_fixed_order_oracle(oracle, rows, cols, n):
     wp = packed_weights(w, rows, cols)
     xq = q.quantize_q8_0(to_dev(x))
     y = q.gemv_q4_0(wp, xq, rows, cols, n)
-    ref = oracle.gemv_f32(w, q8_canonical(xq, n, cols), rows, cols, n)
+    xq8 = oracle.quantize_q8_0(x)
+    assert np.array_equal(q8_canonical(xq, n, cols), xq8)      # the GPU's bytes are the oracle's
+    ref = oracle.gemv_f32(w, xq8, rows, cols, n)
     got = y.cpu().numpy()
     bad = np.argwhere(got != ref)
     assert bad.size == 0, f"{len(bad)} of {got.size} differ, first {bad[0]}: {got[tuple(bad[0])]!r} vs {ref[tuple(bad[0])]!r}"

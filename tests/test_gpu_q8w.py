@@ -63,7 +63,9 @@ def test_block_sums_q8_bit_exact(oracle, rows, cols, n):
     w8, x = _inputs(rows, cols, n, 1)
     xq = q.quantize_q8_0(to_dev(x))
     s = q.block_sums_q8_0(_packed(w8, rows, cols), xq, rows, cols, n).cpu().numpy()
-    assert np.array_equal(s, oracle.q8w_block_sums(w8, q8_canonical(xq, n, cols), rows, cols, n))
+    xq8 = oracle.quantize_q8_0(x)
+    assert np.array_equal(q8_canonical(xq, n, cols), xq8)      # the GPU's bytes are the oracle's
+    assert np.array_equal(s, oracle.q8w_block_sums(w8, xq8, rows, cols, n))
 
 
 # -------------------------------------------------------------------- GEMV

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import assert_within, dev, packed_weights, require_gpu, to_dev
+from gpu_helpers import assert_within, dev, packed_weights, q8_canonical, require_gpu, to_dev
 from q4_weight_streaming_amd import _lib as q
 from q4_weight_streaming_amd import synth
 
@@ -86,6 +86,132 @@ def test_sweep_fused_quantize_equals_two_launches(oracle):
                               oracle.quantize_q8_0(x)[0, :, 2:].reshape(-1))
         y = q.gemv_q4_0(m["w_packed"], xq, m["rows"], m["cols"], 1)
         assert torch.equal(y, m["y"])
+
+
+@pytest.mark.parametrize("n", [2, 3, 5, 8])
+def test_sweep_many_rows_equals_standalone(oracle, n):
+    # 2..8 rows with every activation given as fp32: a quantize launch, then one GEMV launch
+    # over all matrices; x_q8 and y equal the standalone quantize + GEMV bit for bit -- one,
+    # two and four K splits, partial chunks and row groups, segments past 16 chunks, padded
+    # d_x rows -- and the Q8_0 bytes equal the oracle's
+    require_gpu()
+    shapes = [synth.MatShape("a", 257, 1536), synth.MatShape("b", 64, 8960), synth.MatShape("c", 1, 32),
+              synth.MatShape("d", 130, 4128), synth.MatShape("e", 90, 96), synth.MatShape("f", 70, 18944),
+              synth.MatShape("g", 3, 33792), synth.MatShape("h", 200, 3072), synth.MatShape("i", 65, 2080)]
+    hw, hx, mats = _stack(81 + n, shapes, n)
+    for m in mats:
+        m["x_q8"].fill_(0xA5)                                # every byte must be written
+        m["y"].fill_(float("nan"))
+    sw = q.Sweep(mats, n)
+    info = sw.info()
+    assert info["fused_quantize"] == 0
+    assert info["n_quant_blocks"] == n * sum(s.cols // 32 for s in shapes)
+    sw.run()
+    torch.cuda.synchronize()
+    for m, x, sh in zip(mats, hx, shapes):
+        xq = q.quantize_q8_0(to_dev(x))
+        assert torch.equal(xq, m["x_q8"]), sh.name            # q, d_x and the zeroed padding
+        assert np.array_equal(q8_canonical(m["x_q8"], n, m["cols"]), oracle.quantize_q8_0(x)), sh.name
+        y = q.gemv_q4_0(m["w_packed"], xq, m["rows"], m["cols"], n)
+        assert torch.equal(y, m["y"]), sh.name
+    for i in (0, 3, 8):                                       # and against the fp64 oracle
+        y_ref, S = oracle.gemv(hw[i], oracle.quantize_q8_0(hx[i]), shapes[i].rows, shapes[i].cols, n)
+        assert_within(mats[i]["y"].cpu().numpy(), y_ref, S, what=shapes[i].name)
+
+
+def _adversarial_blocks(rng, nblk):
+    """Q8_0 blocks whose maxima span the quantizer's division-free range and its guards, with
+    near-ties (k + 1/2) d nudged by an ulp either way, all-zero blocks and the maximum anywhere."""
+    f32 = np.float32
+    amax = (f32(2.0) ** rng.uniform(-100, 22, nblk).astype(np.float32)).astype(np.float32)
+    amax[::7] = f32(127 * 2.0 ** -125)
+    amax[3::11] = f32(7.9e6)
+    d = (amax / f32(127)).astype(np.float32)
+    k = rng.integers(-126, 126, size=(nblk, 23)).astype(np.float32)
+    ties = ((k + f32(0.5)) * d[:, None]).astype(np.float32)
+    ties = np.where(rng.random(ties.shape) < 0.4, np.nextafter(ties, f32(np.inf)), ties)
+    ties = np.where(rng.random(ties.shape) < 0.4, np.nextafter(ties, f32(-np.inf)), ties)
+    rand = ((rng.random((nblk, 8)) * 2 - 1) * amax[:, None]).astype(np.float32)
+    x = np.clip(np.concatenate([ties, rand], 1), -amax[:, None], amax[:, None])
+    sign = np.where(rng.random((nblk, 1)) < 0.5, f32(-1), f32(1))
+    blocks = np.concatenate([amax[:, None] * sign, x], 1).astype(np.float32)
+    blocks = np.take_along_axis(blocks, rng.permuted(np.tile(np.arange(32), (nblk, 1)), axis=1), 1)
+    blocks[::13] = 0
+    return blocks
+
+
+@pytest.mark.parametrize("n", [1, 4, 8])
+def test_sweep_quantizers_near_ties_and_extreme_scales(oracle, n):
+    # the sweep's quantizers (one row: inside the GEMV launch; 2..8 rows: the batched quantize
+    # launch) on adversarial activations: x_q8 equals the oracle's Q8_0 bytes, y the GEMV of
+    # those bytes
+    require_gpu()
+    rng = np.random.default_rng(300 + n)
+    shapes = [synth.MatShape("a", 130, 4096), synth.MatShape("b", 64, 1056)]
+    hw, _, mats = _stack(90 + n, shapes, n)
+    hx = []
+    for m, sh in zip(mats, shapes):
+        x = _adversarial_blocks(rng, n * sh.cols // 32).reshape(n, sh.cols)
+        hx.append(x)
+        m["x"] = to_dev(x)
+    sw = q.Sweep(mats, n)
+    assert sw.info()["fused_quantize"] == int(n == 1)
+    sw.run()
+    torch.cuda.synchronize()
+    for m, w, x, sh in zip(mats, hw, hx, shapes):
+        ref = oracle.quantize_q8_0(x)
+        assert np.array_equal(q8_canonical(m["x_q8"], n, sh.cols), ref), sh.name
+        y = q.gemv_q4_0(m["w_packed"], m["x_q8"], sh.rows, sh.cols, n)
+        assert torch.equal(y, m["y"]), sh.name
+
+
+def test_lm_head_fused_sweep_full_parity(oracle):
+    # the lone head as the benchmark times it: a 1-row sweep of one 151936 x 1536 matrix given
+    # as fp32, i.e. one launch of 8-wave split tiles quantizing as they stream; every output
+    # against the oracle, the Q8_0 bytes bit for bit
+    require_gpu()
+    rows, cols = 151936, 1536
+    w = synth.q4_0_weights(rows, cols, synth.generator(2, 0, 1, 0))
+    x = synth.activation(1, cols, synth.generator(2, 0, 1, 1), outliers=0)
+    m = {"w_packed": packed_weights(w, rows, cols), "x": to_dev(x),
+         "x_q8": torch.full((q.q8_bytes(1, cols),), 0xA5, dtype=torch.uint8, device=dev()),
+         "y": torch.full((1, rows), float("nan"), dtype=torch.float32, device=dev()), "rows": rows, "cols": cols}
+    sw = q.Sweep([m], 1)
+    info = sw.info()
+    assert info["fused_quantize"] == 1 and info["n_tiles"] == rows // 64
+    sw.run()
+    torch.cuda.synchronize()
+    xq = oracle.quantize_q8_0(x)
+    assert np.array_equal(q8_canonical(m["x_q8"], 1, cols), xq)
+    y_ref, S = oracle.gemv(w, xq, rows, cols, 1)
+    assert_within(m["y"].cpu().numpy(), y_ref, S, what="lm_head sweep")
+
+
+@pytest.mark.parametrize("n,split", [(1, True), (1, False), (8, False)])
+def test_sweep_timeline(n, split):
+    # a traced run records every workgroup's start and its waves' ends (100 MHz clock, ends
+    # after the start) and leaves the results bit for bit as an untraced run's
+    require_gpu()
+    shapes = ([synth.MatShape("a", 257, 1536), synth.MatShape("b", 130, 2048)] if split else
+              [synth.MatShape("a", 257, 1536), synth.MatShape("b", 64, 8960), synth.MatShape("c", 90, 4128)])
+    _, _, mats = _stack(95 + n, shapes, n)
+    sw = q.Sweep(mats, n)
+    sw.run()
+    torch.cuda.synchronize()
+    ref = [m["y"].clone() for m in mats]
+    tr = sw.set_trace(True)
+    sw.run()
+    torch.cuda.synchronize()
+    sw.set_trace(False)
+    nt = sw.info()["n_tiles"]
+    t = tr.cpu().numpy().reshape(nt, 9)
+    waves = 8 if split else 4
+    assert (t[:, 0] > 0).all() and (t[:, 1:1 + waves] >= t[:, :1]).all()
+    assert (t[:, 1 + waves:] == 0).all()
+    span_us = (t[:, 1:1 + waves].max() - t[:, 0].min()) / 100.0
+    assert 0 < span_us < 1e5
+    for m, r in zip(mats, ref):
+        assert torch.equal(m["y"], r)
 
 
 def _one_row_tiles(shapes):

@@ -9,6 +9,7 @@ step ("How it works", src/mega.cu bullet; M15, M19) is pinned by an independent
 fp64 evaluation without quantization and by the special case in which it
 reduces to one GEMV.
 """
+import math
 import os
 
 import numpy as np
@@ -135,6 +136,48 @@ def test_rmsnorm_within_bound_of_fp64(oracle):
     assert abs(ss - ss64) <= (8960 / 64 + 8) * U * ss64
     ref = x64 / np.sqrt(ss64 / 8960 + 1e-6)
     assert np.all(np.abs(out - ref) <= 1e-5 * np.abs(ref) + 1e-30)
+
+
+@pytest.mark.parametrize("c,n", [(1e-3, 64), (1e-3, 1536), (3.0, 128), (1e-4, 3584)])
+def test_rmsnorm_f64_constant_vector_closed_form(oracle, c, n):
+    """The order-free fp64 norm on x_i = c: c / sqrt(c^2 + 1e-6).  At c = 1e-3 the epsilon is
+    as large as the mean square (result 1/sqrt(2)), so a wrong epsilon, a sum in place of the
+    mean or a missing square root moves it far beyond the 4-ulp margin."""
+    out = oracle.rmsnorm_f64(np.full(n, c, np.float32))
+    c32 = float(np.float32(c))
+    ref = c32 / math.sqrt(c32 * c32 + 1e-6)
+    assert out.dtype == np.float64 and np.all(np.abs(out - ref) <= 4 * 2.0 ** -53 * abs(ref))
+    if c == 1e-3:
+        assert abs(out[0] - 2 ** -0.5) < 1e-3
+
+
+def test_rmsnorm_f64_exact_arithmetic():
+    """Against the definition in exact rational arithmetic (the mean square as a fraction,
+    the square root to 40 digits): every element within 1e-15 relative."""
+    from decimal import Decimal, getcontext
+    from fractions import Fraction
+    from oracle import oracle
+    getcontext().prec = 40
+    x = synth.activation(1, 96, synth.generator(94, 0, 0, 1))[0]
+    ms = sum(Fraction(float(v)) ** 2 for v in x) / len(x) + Fraction(1, 10 ** 6)
+    root = (Decimal(ms.numerator) / Decimal(ms.denominator)).sqrt()
+    out = oracle.rmsnorm_f64(x)
+    for v, o in zip(x, out):
+        exact = Decimal(float(v)) / root
+        assert abs(Decimal(float(o)) - exact) <= Decimal("1e-15") * abs(exact) + Decimal("1e-300")
+
+
+def test_rmsnorm_fixed_order_within_fp32_bound_of_f64(oracle):
+    """The fixed-order fp32 norm against the order-free fp64 one: each output within
+    ((n/64 + 6)/2 + 4) ulp-units (2^-24) of relative error -- the bound the GPU norm-phase
+    check uses (half the sum of squares' chain and butterfly error, then the mean, epsilon,
+    square root and division)."""
+    for n, seed in [(1536, 95), (3584, 96), (8960, 97)]:
+        x = synth.activation(1, n, synth.generator(seed, 0, 0, 1))[0]
+        out, _ = oracle.rmsnorm(x)
+        ref = oracle.rmsnorm_f64(x)
+        delta = ((n / 64 + 6) / 2 + 4) * U
+        assert np.all(np.abs(out - ref) <= delta * np.abs(ref) + 1e-30)
 
 
 # ---------------------------------------------------------------- chained step
