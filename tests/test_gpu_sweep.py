@@ -88,16 +88,39 @@ def test_sweep_fused_quantize_equals_two_launches(oracle):
         assert torch.equal(y, m["y"])
 
 
+MANY_ROW_SHAPES = [synth.MatShape("a", 257, 1536), synth.MatShape("b", 64, 8960), synth.MatShape("c", 1, 32),
+                   synth.MatShape("d", 130, 4128), synth.MatShape("e", 90, 96), synth.MatShape("f", 70, 18944),
+                   synth.MatShape("g", 3, 33792), synth.MatShape("h", 200, 3072), synth.MatShape("i", 65, 2080)]
+
+
+def _new_activations(mats, n, cfg):
+    """Overwrite every x with a fresh seeded activation; returns the host copies."""
+    hx = []
+    for i, m in enumerate(mats):
+        x = synth.activation(n, m["cols"], synth.generator(cfg, i, 0, 1))
+        m["x"].copy_(to_dev(x))
+        hx.append(x)
+    torch.cuda.synchronize()
+    return hx
+
+
+def _check_standalone(mats, hx, n, names):
+    for m, x, name in zip(mats, hx, names):
+        xq = q.quantize_q8_0(to_dev(x))
+        assert torch.equal(xq, m["x_q8"]), name                # q, d_x and the zeroed padding
+        y = q.gemv_q4_0(m["w_packed"], xq, m["rows"], m["cols"], n)
+        assert torch.equal(y, m["y"]), name
+
+
 @pytest.mark.parametrize("n", [2, 3, 5, 8])
 def test_sweep_many_rows_equals_standalone(oracle, n):
     # 2..8 rows with every activation given as fp32: a quantize launch, then one GEMV launch
     # over all matrices; x_q8 and y equal the standalone quantize + GEMV bit for bit -- one,
     # two and four K splits, partial chunks and row groups, segments past 16 chunks, padded
-    # d_x rows -- and the Q8_0 bytes equal the oracle's
+    # d_x rows -- and the Q8_0 bytes equal the oracle's; three steps over fresh activations
+    # (a GEMV that read the previous step's codes would differ)
     require_gpu()
-    shapes = [synth.MatShape("a", 257, 1536), synth.MatShape("b", 64, 8960), synth.MatShape("c", 1, 32),
-              synth.MatShape("d", 130, 4128), synth.MatShape("e", 90, 96), synth.MatShape("f", 70, 18944),
-              synth.MatShape("g", 3, 33792), synth.MatShape("h", 200, 3072), synth.MatShape("i", 65, 2080)]
+    shapes = MANY_ROW_SHAPES
     hw, hx, mats = _stack(81 + n, shapes, n)
     for m in mats:
         m["x_q8"].fill_(0xA5)                                # every byte must be written
@@ -109,14 +132,45 @@ def test_sweep_many_rows_equals_standalone(oracle, n):
     sw.run()
     torch.cuda.synchronize()
     for m, x, sh in zip(mats, hx, shapes):
-        xq = q.quantize_q8_0(to_dev(x))
-        assert torch.equal(xq, m["x_q8"]), sh.name            # q, d_x and the zeroed padding
         assert np.array_equal(q8_canonical(m["x_q8"], n, m["cols"]), oracle.quantize_q8_0(x)), sh.name
-        y = q.gemv_q4_0(m["w_packed"], xq, m["rows"], m["cols"], n)
-        assert torch.equal(y, m["y"]), sh.name
+    _check_standalone(mats, hx, n, [s.name for s in shapes])
     for i in (0, 3, 8):                                       # and against the fp64 oracle
         y_ref, S = oracle.gemv(hw[i], oracle.quantize_q8_0(hx[i]), shapes[i].rows, shapes[i].cols, n)
         assert_within(mats[i]["y"].cpu().numpy(), y_ref, S, what=shapes[i].name)
+    for step in (1, 2):
+        hx = _new_activations(mats, n, 181 + 10 * step + n)
+        sw.run()
+        torch.cuda.synchronize()
+        _check_standalone(mats, hx, n, [f"{s.name} step {step}" for s in shapes])
+
+
+def test_sweep_many_rows_graph_replay():
+    # the 8-row sweep (quantize launch + GEMV launch) captured in a graph: each replay, with
+    # eager activation updates and synchronizations between replays, equals the standalone
+    # quantize + GEMV bit for bit, and an eager step in between stays exact
+    require_gpu()
+    n = 8
+    shapes = MANY_ROW_SHAPES[:6]
+    _, hx, mats = _stack(95, shapes, n, keep_host=False)
+    sw = q.Sweep(mats, n)
+    sw.run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sw.run()
+    torch.cuda.synchronize()
+    for r in range(4):
+        hx = _new_activations(mats, n, 400 + r)
+        for m in mats:
+            m["y"].fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        _check_standalone(mats, hx, n, [f"{s.name} replay {r}" for s in shapes])
+        if r == 1:
+            hx = _new_activations(mats, n, 410)
+            sw.run()
+            torch.cuda.synchronize()
+            _check_standalone(mats, hx, n, [f"{s.name} eager" for s in shapes])
 
 
 def _adversarial_blocks(rng, nblk):
@@ -257,18 +311,19 @@ def test_sweep_one_row_prequantized_mixed_equals_standalone(oracle):
         assert_within(mats[i]["y"].cpu().numpy(), y_ref, S, what=shapes[i].name)
 
 
-def test_sweep_not_fused_with_a_prequantized_activation():
+@pytest.mark.parametrize("n", [1, 4])
+def test_sweep_not_fused_with_a_prequantized_activation(n):
     # a matrix without x reads its x_q8 as given: the plan keeps two launches
     require_gpu()
     shapes = [synth.MatShape("a", 65, 1536), synth.MatShape("b", 3, 2048)]
-    _, hx, mats = _stack(79, shapes, 1)
+    _, hx, mats = _stack(79, shapes, n)
     mats[1]["x_q8"] = q.quantize_q8_0(mats[1].pop("x"))
-    sw = q.Sweep(mats, 1)
+    sw = q.Sweep(mats, n)
     assert sw.info()["fused_quantize"] == 0
     sw.run()
     torch.cuda.synchronize()
     for m, x in zip(mats, hx):
-        y = q.gemv_q4_0(m["w_packed"], q.quantize_q8_0(to_dev(x)), m["rows"], m["cols"], 1)
+        y = q.gemv_q4_0(m["w_packed"], q.quantize_q8_0(to_dev(x)), m["rows"], m["cols"], n)
         assert torch.equal(y, m["y"])
 
 
