@@ -89,7 +89,17 @@ __device__ __forceinline__ void rows4(uint32_t x, uint32_t (&y)[4]) {
 // turns, so each accumulator is read again three instructions after it was
 // written, and the leading s_nop covers the operands the compiler wrote just
 // before (five wait states, which also covers a VALU write of EXEC).  Integer
-// sums, so the order of the dots does not change them.
+// sums, so the order of the dots does not change them.  The wait states are
+// counted by hand, so only end-to-end results show a miscount; each user has a
+// bit-exact test against the two-launch form or the fixed-order oracle:
+//   the fused 1-row sweep's group sets and split tiles (test_gpu_sweep.py:
+//     test_sweep_fused_quantize_equals_two_launches, test_qwen15_n1_full_parity;
+//     test_gpu_fixed_order.py: test_single_split_sweep_equals_fixed_order_oracle),
+//   the lone head's 8-wave split tiles (test_lm_head_fused_sweep_full_parity),
+//   the Q8_0 head quantizing in the same launch (test_gpu_q8w.py:
+//     test_gemv_q8_from_f32_equals_two_launches, test_gemv_q8_from_f32_lm_head_full),
+//   the chained step's GEMVs (test_gpu_chain.py: test_chain_small_bit_exact,
+//     test_chain_small_against_definition).
 #define Q4S_DOT_BCAST(acc, y, w, n) \
     "v_dot4c_i32_i8_dpp %" #acc ", %" #y ", %" #w " row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n"
 #define Q4S_DOT_ROUND(wa, wb, wc, wd, n, n8) \

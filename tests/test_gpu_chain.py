@@ -115,13 +115,16 @@ def test_chain_wide_hidden_unpaired(oracle, mode):
     _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, "wide hidden")
 
 
-@pytest.mark.parametrize("F,workgroups", [(4608, 0), (4608, 5), (17408, 0), (17408, 5)],
-                         ids=["ranges4_per_cu", "ranges4_wg5", "ranges17_per_cu", "ranges17_wg5"])
+@pytest.mark.parametrize("F,workgroups", [(4608, 0), (4608, 5), (17408, 0), (17408, 5), (32768, 0), (32768, 5)],
+                         ids=["ranges4_per_cu", "ranges4_wg5", "ranges17_per_cu", "ranges17_wg5",
+                              "ranges32_per_cu", "ranges32_wg5"])
 def test_chain_k_range_tiles_bit_exact(oracle, F, workgroups):
     """Tagged phases: down with four K splits runs one tile per (K range, row group), ranges
     1..3 handing their sums to range 0 as tagged words.  F = 4608: ranges of 4-5 chunks; F =
-    17408: 17 chunks, two fp32 segments per range.  With 5 workgroups each runs several such
-    tiles in turn (range 0 last).  Results equal the oracle's bit for bit."""
+    17408: 17 chunks, two fp32 segments per range; F = 32768 (the largest ff a chain accepts):
+    32-chunk ranges that fill the terms table and exactly two 16-chunk segments, 8 chunks per
+    wave.  With 5 workgroups each runs several such tiles in turn (range 0 last).  Results
+    equal the oracle's bit for bit."""
     require_gpu()
     L, E, D, V = 2, 256, 64, 320
     shapes, ws, h0 = _inputs(47, L, E, D, F, V)
