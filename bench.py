@@ -300,6 +300,29 @@ def run_q8_head(args, dev, stream) -> int:
 
 ATTN_SRCS = [os.path.join(ROOT, "q4_weight_streaming_amd", "csrc", f)
               for f in ("q4s_attn.hip", "q4s_device.h", "q4s_internal.h")]
+CHAIN_SRCS = [os.path.join(ROOT, "q4_weight_streaming_amd", "csrc", f)
+              for f in ("q4s_chain.hip", "q4s_chain.h", "q4s_lane.h", "q4s_device.h", "q4s_internal.h")]
+
+
+def chain_kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in CHAIN_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def chain_traffic_from_profile(model: str, mode: str):
+    """HBM bytes per chained step (its k_chain launch) from the committed summary, if taken on
+    the current chain source and for this model and sync mode; else None."""
+    path = os.path.join(ROOT, "profiles", "chain_decode_step.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
+    m = re.search(rf"hbm_bytes_per_launch\[{re.escape(model)} {re.escape(mode)}\]:\s*([0-9]+)", text)
+    if not m_hash or not m or m_hash.group(1) != chain_kernel_hash():
+        return None
+    return float(m.group(1))
 
 
 def attn_traffic_from_profile(L: int):
@@ -428,10 +451,32 @@ def run_chain(args, dev, stream) -> int:
         del ws
     torch.cuda.synchronize()
     modes = list(CHAIN_MODES) if args.sync == "all" else [args.sync]
+    if args.profile_only:
+        # 10 steps of the first mode over the rotated copies, then a 1 GiB copy to calibrate counters
+        chains = [q.Chain(L, E, D, F, V, c["wp"], c["h0"], c["acts"], c["logits"], sync_mode=CHAIN_MODES[modes[0]],
+                          workgroups=args.chain_workgroups) for c in copies]
+        for ch in chains:
+            ch.set_cooperative(not args.chain_plain_launch)
+        for i in range(10):
+            chains[i % ncopies].run()
+        for ch in chains:
+            ch.check()
+            ch.close()
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        q.bench_copy(src, dst)
+        torch.cuda.synchronize()
+        del chains, src, dst
+        copies.clear()
+        torch.cuda.empty_cache()
+        log(f"profile run done: 10 chained steps ({modes[0]}), one 1 GiB copy")
+        return 0
     results, chains_by_mode = {}, {}
     for mode in modes:
         chains = [q.Chain(L, E, D, F, V, c["wp"], c["h0"], c["acts"], c["logits"], sync_mode=CHAIN_MODES[mode],
                           workgroups=args.chain_workgroups) for c in copies]
+        for ch in chains:
+            ch.set_cooperative(not args.chain_plain_launch)
         ms = time_steps([ch.run for ch in chains], args.steps, args.warmup, stream)
         for ch in chains:
             ch.check()
@@ -485,7 +530,8 @@ def run_chain(args, dev, stream) -> int:
                                f"residual epilogues, one cooperative launch, {ncopies} rotated seeded copies",
                    "sync": best, "modes": results},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": f"k_chain<{best}>",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": chain_traffic_from_profile(model, best),
+                     "kernel": f"k_chain<{best}>",
                      "algorithmic_bytes_per_launch": packed},
     }
     if host0 is not None:
@@ -770,6 +816,8 @@ def main() -> int:
     ap.add_argument("--chain-model", default="1.5b", choices=["1.5b", "7b"], help="stack of --workload chain")
     ap.add_argument("--sync", default="all", choices=["all", *CHAIN_MODES], help="phase sync of --workload chain")
     ap.add_argument("--chain-workgroups", type=int, default=0, help="persistent workgroups (0: one per CU)")
+    ap.add_argument("--chain-plain-launch", action="store_true",
+                    help="launch the chained step without the cooperative-launch call (for the profiler)")
     ap.add_argument("--context", type=int, default=32768, help="KV positions for --workload attn")
     ap.add_argument("--n", type=int, default=1, help="activation rows per GEMV (1..24; 1..8 for lm_head_q8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

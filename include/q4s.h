@@ -492,6 +492,18 @@ q4s_status q4s_chain_check(const q4s_chain* chain, void* stream);
  */
 q4s_status q4s_chain_set_wait_limit(q4s_chain* chain, uint32_t polls);
 
+/*
+ * How later steps launch the persistent workgroups: cooperative != 0 (the
+ * default) through the cooperative-launch call, which guarantees that all of
+ * them are resident at once; 0 through a plain launch, for tools that do not
+ * handle cooperative launches (the profiler).  The workgroup count never
+ * exceeds what the GPU can hold at once, so on an otherwise idle GPU a plain
+ * launch also starts them all; where it cannot (other work holding the GPU),
+ * the bounded waits give up and q4s_chain_check reports Q4S_ERR_WAIT.
+ * Results are the same either way.
+ */
+q4s_status q4s_chain_set_cooperative(q4s_chain* chain, int cooperative);
+
 q4s_status q4s_chain_get_info(const q4s_chain* chain, q4s_chain_info* info);
 
 /*

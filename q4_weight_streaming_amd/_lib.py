@@ -106,6 +106,7 @@ def lib():
             "q4s_chain_trace_bytes": ([p], sz),
             "q4s_chain_set_trace": ([p, p, sz], i32),
             "q4s_chain_set_wait_limit": ([p, ctypes.c_uint32], i32),
+            "q4s_chain_set_cooperative": ([p, i32], i32),
             "q4s_chain_stage_dump_bytes": ([p], sz),
             "q4s_chain_set_stage_dump": ([p, p, sz], i32),
             "q4s_bench_read": ([p, sz, i32, i32, p, p], i32),
@@ -475,6 +476,9 @@ class Chain:
 
     def set_wait_limit(self, polls: int) -> None:
         _check("q4s_chain_set_wait_limit", lib().q4s_chain_set_wait_limit(self._chain, polls))
+
+    def set_cooperative(self, on: bool) -> None:
+        _check("q4s_chain_set_cooperative", lib().q4s_chain_set_cooperative(self._chain, 1 if on else 0))
 
     def check(self) -> None:
         """Synchronize; raise Q4SError (status 7) if a bounded wait of the last step gave up."""

@@ -610,6 +610,7 @@ struct q4s_chain {
     uint8_t* dev = nullptr;
     uint32_t gen = 0;
     int64_t steps = 0;
+    bool cooperative = true;
     uint64_t* trace = nullptr;
     uint64_t* dump = nullptr;
     uint32_t spin_limit = kChainDefaultSpin;
@@ -900,7 +901,8 @@ q4s_status q4s_chain_run(q4s_chain* p, void* stream) {
     cp.dump = p->dump;
     cp.dump_chunks = (int32_t)chain_dump_chunks(p);
     q4s_status s =
-        hip_status(launch_chain(p->mode, cp, p->workgroups, p->spin_limit, (hipStream_t)stream), "chain launch");
+        hip_status(launch_chain(p->mode, cp, p->workgroups, p->spin_limit, p->cooperative, (hipStream_t)stream),
+                   "chain launch");
     if (s == Q4S_OK) ++p->steps;
     return s;
 }
@@ -954,6 +956,12 @@ q4s_status q4s_chain_set_stage_dump(q4s_chain* p, uint64_t* dump, size_t dump_by
 q4s_status q4s_chain_set_wait_limit(q4s_chain* p, uint32_t polls) {
     if (!p) return fail(Q4S_ERR_NULL, "chain is NULL");
     p->spin_limit = polls;
+    return ok();
+}
+
+q4s_status q4s_chain_set_cooperative(q4s_chain* p, int cooperative) {
+    if (!p) return fail(Q4S_ERR_NULL, "chain is NULL");
+    p->cooperative = cooperative != 0;
     return ok();
 }
 

@@ -54,7 +54,8 @@ enum ChainSync { kChainCounter = 0, kChainTree = 1, kChainTagged = 2 };
 constexpr int kChainSyncWords = 32 * 18;
 
 // The chained decode step (one cooperative launch; grid = resident workgroups).
-hipError_t launch_chain(int sync_mode, const ChainParams& p, int workgroups, uint32_t spin_limit, hipStream_t st);
+hipError_t launch_chain(int sync_mode, const ChainParams& p, int workgroups, uint32_t spin_limit, bool cooperative,
+                        hipStream_t st);
 constexpr uint32_t kChainDefaultSpin = 1u << 20;
 // Tile word: the tile index in bits 0-28; bit 31: one row group whose chunks
 // are spread over the 4 waves; bit 30: two row groups, two waves each; bit 29:

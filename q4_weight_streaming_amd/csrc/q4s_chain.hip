@@ -863,7 +863,8 @@ __global__ __launch_bounds__(256) void k_chain_reset(uint32_t* w, int n, uint32_
 
 }  // namespace
 
-hipError_t launch_chain(int sync_mode, const ChainParams& p, int workgroups, uint32_t spin_limit, hipStream_t st) {
+hipError_t launch_chain(int sync_mode, const ChainParams& p, int workgroups, uint32_t spin_limit, bool cooperative,
+                        hipStream_t st) {
     hipLaunchKernelGGL(k_chain_reset, dim3(1), dim3(256), 0, st, p.sync, kChainSyncWords, spin_limit);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -872,6 +873,9 @@ hipError_t launch_chain(int sync_mode, const ChainParams& p, int workgroups, uin
     const void* fn = sync_mode == kChainCounter ? (const void*)k_chain<kChainCounter>
                      : sync_mode == kChainTree  ? (const void*)k_chain<kChainTree>
                                                 : (const void*)k_chain<kChainTagged>;
+    // (the workgroup count never exceeds what can be resident, so a plain launch on an otherwise
+    // idle GPU also starts them all; its waits are bounded either way)
+    if (!cooperative) return hipLaunchKernel(fn, dim3(workgroups), dim3(kThreads), args, 0, st);
     return hipLaunchCooperativeKernel(fn, dim3(workgroups), dim3(kThreads), args, 0, st);
 }
 

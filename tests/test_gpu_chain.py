@@ -135,6 +135,26 @@ def test_chain_k_range_tiles_bit_exact(oracle, F, workgroups):
     _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, f"K-range tiles, {workgroups} workgroups")
 
 
+def test_chain_plain_launch_equals_cooperative(oracle):
+    """The step launched without the cooperative-launch call (one workgroup per CU, on an
+    otherwise idle GPU) gives the same bits as the cooperative launch and the oracle."""
+    require_gpu()
+    L, E, D, F, V = 2, 256, 64, 384, 320
+    shapes, ws, h0 = _inputs(48, L, E, D, F, V)
+    ref_acts, ref_logits = oracle.chain_step(ws, E, D, F, V, h0)
+    wp, h0d, acts, logits = _device(shapes, ws, h0, L, E, D, F, V)
+    ch = q.Chain(L, E, D, F, V, wp, h0d, acts, logits, sync_mode=q.CHAIN_TAGGED, workgroups=0)
+    ch.set_cooperative(False)
+    ch.run()
+    ch.run()
+    ch.check()
+    ch.close()
+    words = q.chain_act_words(L, E, D, F, V)
+    vals, tags = q.chain_values(acts[:words])
+    assert (tags.cpu().numpy() == 2).all()
+    _compare(ref_acts, ref_logits, vals.cpu().numpy(), logits.cpu().numpy(), L, E, D, F, "plain launch")
+
+
 def test_chain_head_only(oracle):
     require_gpu()
     L, E, D, F, V = 0, 128, 64, 64, 200
