@@ -543,12 +543,52 @@ static_assert(kChainRangeChunks <= 4 * kSegChunks, "a K-range tile's segments fi
 template <int kWpg>
 __device__ __forceinline__ int split_first(int w, int C) { return (w * C + kWpg - 1) / kWpg; }
 
-// Chunk c's exact block sums and binary16 d_w into entry tc of the term table.
+// The fixed-order chains read each chunk's exact block sums and binary16 d_w
+// (the term table) and its blocks' d_x (the d_x table, 8 floats per chunk,
+// written by the wave that staged the chunk).  They read them kChainFold
+// chunks at a time, every read of a batch issued before the first fmaf (read
+// one after another, each read's latency adds up along the chain); a chunk
+// past the range adds fmaf(0, s, p) == p (p is never -0), an exact no-op.
+constexpr int kChainFold = 4;
+
+// Table entries of blocks 4 hb .. 4 hb + 3 of chunks cb .. cb + kChainFold - 1
+// (entry c - tbase; a chunk from c_end on reads chunk c_end - 1's, which the
+// fold then leaves out).
+__device__ __forceinline__ void chain_fetch(int cb, int c_end, int tbase, int hb, const Q4S_LDS uint32_t* terms,
+                                            const Q4S_LDS f32x4* dx, uint32_t (&t)[kChainFold][4],
+                                            f32x4 (&d)[kChainFold]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 0; k < kChainFold; ++k) {
+        const int e = min(cb + k, c_end - 1) - tbase;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) t[k][x] = terms[(e * kChunkBlocks + 4 * hb + x) * 64 + lane];
+        d[k] = dx[2 * e + hb];
+    }
+}
+
+// p through the batch's first n chunks in order: fmaf(d_w/16 * d_x, 16 s, p) per block.
+__device__ __forceinline__ void chain_fold(const uint32_t (&t)[kChainFold][4], const f32x4 (&d)[kChainFold], int n,
+                                           float& p) {
+#pragma unroll
+    for (int k = 0; k < kChainFold; ++k)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const float dw16 = half_hi(t[k][x]) * 0.0625f;
+            const float s16 = (float)((int)(int16_t)(t[k][x] & 0xffffu) * 16);
+            const float m = dw16 * d[k][x];
+            p = fmaf(k < n ? m : 0.0f, s16, p);
+        }
+}
+
+// Chunk c's exact block sums and binary16 d_w into entry tc of the term table,
+// its blocks' d_x into entry tc of the d_x table.
 template <int kSync>
 __device__ __forceinline__ void chunk_terms(int c, int tc, const Chunk& ch, ActStaged<kSync>& act,
-                                            Q4S_LDS uint32_t* terms) {
+                                            Q4S_LDS uint32_t* terms, Q4S_LDS float* dx) {
     const int lane = threadIdx.x & 63;
     const auto pr = act.prepare(0, c);
+    if ((lane & 7) == 0) dx[tc * kChunkBlocks + (lane >> 3)] = __uint_as_float(pr.dbits);  // lane 8 b: block b's d_x
     uint32_t y[4];
     rows4(pr.packed, y);
 #pragma unroll
@@ -570,9 +610,9 @@ __device__ __forceinline__ void chunk_terms(int c, int tc, const Chunk& ch, ActS
 
 template <int kSync, int kWpg>
 __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t tile, float* red,
-                                                 Q4S_LDS u32x2* stage, Q4S_LDS uint32_t* terms, StageKey& key,
-                                                 int phase, uint32_t gen, uint32_t* err, uint64_t* mark_start,
-                                                 uint64_t* mark_ready, uint64_t* dump) {
+                                                 Q4S_LDS u32x2* stage, Q4S_LDS uint32_t* terms, Q4S_LDS float* dxt,
+                                                 StageKey& key, int phase, uint32_t gen, uint32_t* err,
+                                                 uint64_t* mark_start, uint64_t* mark_ready, uint64_t* dump) {
     if (mark_start && threadIdx.x == 0) gwr<uint64_t>(mark_start)[0] = __builtin_amdgcn_s_memrealtime();
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -584,6 +624,7 @@ __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t til
     const bool live = g < m.G;
     // one group's table takes all kChainTermWords (<= 16 chunks); two groups (<= 8 chunks each) halve it
     Q4S_LDS uint32_t* gterms = terms + gi * (kChainTermWords / 2);
+    Q4S_LDS float* gdx = dxt + gi * (kChainSplitChunks * kChunkBlocks / 2);
     const int64_t row = g * kGroupRows + lane;
     const int64_t rrow = min(row, (int64_t)m.rows - 1);
     uint64_t rword = 0;
@@ -599,47 +640,40 @@ __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t til
         load_chunk(a, wp);
         if (i0 + 1 < i1) load_chunk(b, wp + kChunkBytes);
         for (int c = i0; c < i1; c += 2) {
-            chunk_terms<kSync>(c, c, a, act, gterms);
+            chunk_terms<kSync>(c, c, a, act, gterms, gdx);
             if (c + 2 < i1) load_chunk(a, wp + (size_t)(c + 2 - i0) * kChunkBytes);
             if (c + 1 < i1) {
-                chunk_terms<kSync>(c + 1, c + 1, b, act, gterms);
+                chunk_terms<kSync>(c + 1, c + 1, b, act, gterms, gdx);
                 if (c + 3 < i1) load_chunk(b, wp + (size_t)(c + 3 - i0) * kChunkBytes);
             }
         }
     }
     __syncthreads();
-    // the fixed-order fp32 chains, one wave per K range (a range of <= 8 chunks is one segment)
-    if (live && lw < ks) {
-        const int c0 = (int)((int64_t)lw * C / ks), c1 = (int)((int64_t)(lw + 1) * C / ks);
-        // where the group's waves' slices start (wave w staged chunks [first[w], first[w + 1]))
-        int first[kWpg + 1];
-#pragma unroll
-        for (int w = 0; w <= kWpg; ++w) first[w] = split_first<kWpg>(w, C);
-        float pa = 0.0f, pb = 0.0f;
-        int w = 0;  // the wave of the group that staged chunk c
-        for (int c = c0; c < c1; ++c) {
-            while (c >= first[w + 1]) ++w;
-            const Q4S_LDS u32x2* st = stage + (gi * kWpg + w) * (kChainMaxChunks * 64) + (c - first[w]) * 64;
-#pragma unroll
-            for (int b = 0; b < kChunkBlocks; ++b) {
-                const uint32_t t = gterms[(c * kChunkBlocks + b) * 64 + lane];
-                const float dw16 = half_hi(t) * 0.0625f;
-                const float dx = __uint_as_float(st[8 * b][1]);
-                const float s16 = (float)((int)(int16_t)(t & 0xffffu) * 16);
-                float& p = b < kChunkBlocks / 2 ? pa : pb;
-                p = fmaf(dw16 * dx, s16, p);
-            }
+    // the fixed-order fp32 chains: K range r of a group on its waves 2r (chain A, blocks 0-3 of
+    // every chunk) and 2r + 1 (chain B, blocks 4-7); a range of <= 8 chunks is one segment
+    const int r = lw >> 1, hb = lw & 1;
+    if (live && r < ks) {
+        const int c0 = (int)((int64_t)r * C / ks), c1 = (int)((int64_t)(r + 1) * C / ks);
+        float p = 0.0f;
+        for (int cb = c0; cb < c1; cb += kChainFold) {
+            uint32_t t[kChainFold][4];
+            f32x4 d[kChainFold];
+            chain_fetch(cb, c1, 0, hb, gterms, (const Q4S_LDS f32x4*)gdx, t, d);
+            chain_fold(t, d, c1 - cb, p);
         }
-        float acc = 0.0f;
-        acc += pa + pb;
-        red[wave * 64 + lane] = acc;
+        red[wave * 64 + lane] = p;
     }
     __syncthreads();
     if (!live || lw != 0) return;
-    // a row group's K ranges added in order; a pair's first half also forms its partner's
+    // a row group's K ranges added in order, each 0 + (A + B); a pair's first half also forms
+    // its partner's
     auto total = [&](int w0) {
-        float t = red[w0 * 64 + lane];
-        for (int j = 1; j < ks; ++j) t += red[(w0 + j) * 64 + lane];
+        float t = 0.0f;
+        for (int j = 0; j < ks; ++j) {
+            float a = 0.0f;
+            a += red[(w0 + 2 * j) * 64 + lane] + red[(w0 + 2 * j + 1) * 64 + lane];
+            t = j == 0 ? a : t + a;
+        }
         return t;
     };
     const float v = total(wave);
@@ -670,9 +704,9 @@ __device__ __forceinline__ void chain_tile_split(const ChainMat& cm, int64_t til
 // instead of 4.
 template <int kSync>
 __device__ __forceinline__ void chain_tile_range(const ChainMat& cm, int64_t idx, float* red, Q4S_LDS u32x2* stage,
-                                                 Q4S_LDS uint32_t* terms, StageKey& key, int phase, uint32_t gen,
-                                                 uint32_t* err, uint64_t* mark_start, uint64_t* mark_ready,
-                                                 uint64_t* dump) {
+                                                 Q4S_LDS uint32_t* terms, Q4S_LDS float* dxt, StageKey& key,
+                                                 int phase, uint32_t gen, uint32_t* err, uint64_t* mark_start,
+                                                 uint64_t* mark_ready, uint64_t* dump) {
     if (mark_start && threadIdx.x == 0) gwr<uint64_t>(mark_start)[0] = __builtin_amdgcn_s_memrealtime();
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -698,10 +732,10 @@ __device__ __forceinline__ void chain_tile_range(const ChainMat& cm, int64_t idx
         load_chunk(a, wp);
         if (i0 + 1 < i1) load_chunk(b, wp + kChunkBytes);
         for (int c = i0; c < i1; c += 2) {
-            chunk_terms<kSync>(c, c - c0, a, act, terms);
+            chunk_terms<kSync>(c, c - c0, a, act, terms, dxt);
             if (c + 2 < i1) load_chunk(a, wp + (size_t)(c + 2 - i0) * kChunkBytes);
             if (c + 1 < i1) {
-                chunk_terms<kSync>(c + 1, c + 1 - c0, b, act, terms);
+                chunk_terms<kSync>(c + 1, c + 1 - c0, b, act, terms, dxt);
                 if (c + 3 < i1) load_chunk(b, wp + (size_t)(c + 3 - i0) * kChunkBytes);
             }
         }
@@ -715,25 +749,15 @@ __device__ __forceinline__ void chain_tile_range(const ChainMat& cm, int64_t idx
 #pragma unroll
     for (int k = 0; k < kMaxSeg; ++k) pseg[k] = 0.0f;
     if (wave < 2) {
-        int first[5];
-#pragma unroll
-        for (int w = 0; w <= 4; ++w) first[w] = c0 + split_first<4>(w, n);
-        int w = 0;  // the wave that staged chunk c
         float p = 0.0f;
         int seg = 0;
-        for (int c = c0; c < c1; ++c) {
-            while (c >= first[w + 1]) ++w;
-            const Q4S_LDS u32x2* st = stage + w * (kChainMaxChunks * 64) + (c - first[w]) * 64;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int bk = 4 * wave + x;
-                const uint32_t t = terms[((c - c0) * kChunkBlocks + bk) * 64 + lane];
-                const float dw16 = half_hi(t) * 0.0625f;
-                const float dx = __uint_as_float(st[8 * bk][1]);
-                const float s16 = (float)((int)(int16_t)(t & 0xffffu) * 16);
-                p = fmaf(dw16 * dx, s16, p);
-            }
-            if (c + 1 == c1 || (c + 1 - c0) % kSegChunks == 0) {  // segment end
+        for (int cb = c0; cb < c1; cb += kChainFold) {
+            uint32_t t[kChainFold][4];
+            f32x4 d[kChainFold];
+            chain_fetch(cb, c1, c0, wave, terms, (const Q4S_LDS f32x4*)dxt, t, d);
+            chain_fold(t, d, c1 - cb, p);
+            // segments are kSegChunks (a multiple of kChainFold) chunks from c0, the last one to c1
+            if (cb + kChainFold >= c1 || (cb + kChainFold - c0) % kSegChunks == 0) {
                 if (wave == 1) red[seg * 64 + lane] = p;
 #pragma unroll
                 for (int k = 0; k < kMaxSeg; ++k)
@@ -818,6 +842,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chain(ChainParams P) {
     __shared__ float red[kWaves * 64];
     __shared__ u32x2 stage[kWaves * kChainMaxChunks * 64];
     __shared__ uint32_t terms[kChainTableWords];
+    __shared__ f32x4 dxt[kChainTableWords / 64 / 4];  // the d_x table: 8 floats per chunk of the term table
     const uint32_t nwg = gridDim.x, b = blockIdx.x;
     if (P.trace && threadIdx.x == 0)  // when this workgroup started, after the phase-end plane
         gwr<uint64_t>(P.trace)[(size_t)P.n_phases * nwg + b] = __builtin_amdgcn_s_memrealtime();
@@ -837,13 +862,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_chain(ChainParams P) {
             uint64_t* dp = P.dump ? P.dump + (size_t)p * P.dump_chunks * 64 : nullptr;
             if (tw & kChainSplit4)  // one row group, its chunks spread over the 4 waves
                 chain_tile_split<kSync, 4>(cm, tw & kChainTileIndex, red, (Q4S_LDS u32x2*)stage,
-                                           (Q4S_LDS uint32_t*)terms, key, p, P.gen, P.sync, ms, mr, dp);
+                                           (Q4S_LDS uint32_t*)terms, (Q4S_LDS float*)dxt, key, p, P.gen, P.sync,
+                                           ms, mr, dp);
             else if (tw & kChainSplit2)  // two row groups, two waves each
                 chain_tile_split<kSync, 2>(cm, tw & kChainTileIndex, red, (Q4S_LDS u32x2*)stage,
-                                           (Q4S_LDS uint32_t*)terms, key, p, P.gen, P.sync, ms, mr, dp);
+                                           (Q4S_LDS uint32_t*)terms, (Q4S_LDS float*)dxt, key, p, P.gen, P.sync,
+                                           ms, mr, dp);
             else if (kSync == kChainTagged && (tw & kChainRange))  // one K range of a row group
                 chain_tile_range<kSync>(cm, tw & kChainTileIndex, red, (Q4S_LDS u32x2*)stage,
-                                        (Q4S_LDS uint32_t*)terms, key, p, P.gen, P.sync, ms, mr, dp);
+                                        (Q4S_LDS uint32_t*)terms, (Q4S_LDS float*)dxt, key, p, P.gen, P.sync, ms,
+                                        mr, dp);
             else  // a group set: one wave per row group (or K range)
                 chain_tile<kSync>(cm, tw, red, (Q4S_LDS u32x2*)stage, key, p, P.gen, P.sync, ms, mr, dp);
             __syncthreads();
