@@ -100,6 +100,19 @@ __device__ __forceinline__ float chain_value(const uint64_t* p, uint64_t w, uint
 
 constexpr int kChainMaxChunks = 32;  // chunks of one wave's K range (its LDS slice)
 constexpr int kChainBatch = 6;       // chunks per prologue load batch (a 1536-wide vector in one)
+
+// A norm phase's input vector, read from global memory once per workgroup: the
+// first wave of the workgroup to stage it in a phase claims it (an LDS max on
+// the phase number), loads and polls it as every wave otherwise would, leaves
+// it here as fp32 and publishes the phase number; the workgroup's other waves
+// wait for that and take the vector from LDS.  (The waves of a workgroup are
+// always in the same tile, so no later phase overwrites the copy while one of
+// them reads it.)  With tagged phases only: there every wave otherwise polls
+// the vector at device scope, past the L2 (after a barrier the L2 serves the
+// other waves' reads).  Vectors longer than kChainNormShare are read by every wave.
+constexpr int kChainNormShare = 4096;
+__shared__ f32x4 chain_xs[kChainNormShare / 4];
+__shared__ int chain_xs_claim, chain_xs_ready;  // the phase last claimed / published
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define Q4S_LDS __attribute__((address_space(3)))
 
@@ -335,6 +348,40 @@ __device__ __forceinline__ MatDesc chain_group(const ChainMat& cm, int64_t vg, i
     return m;
 }
 
+// The workgroup's copy of a norm phase's vector (nc chunks, nc * 256 <=
+// kChainNormShare) in chain_xs: loaded by the wave that claims it, waited for
+// by the others.  Called by a whole wave.
+template <int kSync>
+__device__ __forceinline__ void chain_norm_shared(const ChainSrc& cm, int nc, int phase, uint32_t gen,
+                                                  uint32_t* err) {
+    const int lane = threadIdx.x & 63;
+    int prev = 0;
+    if (lane == 0) prev = atomicMax(&chain_xs_claim, phase);
+    if (__builtin_amdgcn_readfirstlane(prev) < phase) {  // the first wave here in this phase
+        float v[kChainBatch][4];
+        for (int b0 = 0; b0 < nc; b0 += kChainBatch) {
+            const int cnt = min(kChainBatch, nc - b0);
+            chain_values<kSync, kChainBatch>(cm, b0, cnt, gen, err, b0 == 0, v);
+#pragma unroll
+            for (int cc = 0; cc < kChainBatch; ++cc)
+                if (cc < cnt) chain_xs[(b0 + cc) * 64 + lane] = (f32x4){v[cc][0], v[cc][1], v[cc][2], v[cc][3]};
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        if (lane == 0) __hip_atomic_store(&chain_xs_ready, phase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+        const int64_t limit = chain_spin_limit(err);
+        int64_t spins = 0;
+        while (__hip_atomic_load(&chain_xs_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < phase) {
+            if (++spins > limit) {  // the loading wave's own waits are bounded, so this is not reached
+                chain_fail(err);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    }
+}
+
 // Prologue of a chained-step wave that streams chunks [c0, c1): waits for the
 // activation, takes the RMS norm of the whole vector when asked, and leaves
 // the Q8_0 codes and scales of its chunks in its LDS slice ([chunk][lane]).
@@ -344,7 +391,8 @@ __device__ __forceinline__ MatDesc chain_group(const ChainMat& cm, int64_t vg, i
 // step adds the same two values on both lanes.
 template <int kSync>
 __device__ __noinline__ void chain_stage(const void* x, const uint64_t* x2, const uint64_t* xq, int x_plain, int norm,
-                                         int n, int c0, int c1, uint32_t gen, uint32_t* err, Q4S_LDS u32x2* slice) {
+                                         int n, int c0, int c1, int phase, uint32_t gen, uint32_t* err,
+                                         Q4S_LDS u32x2* slice) {
     if (xq) {  // already quantized by the producing tiles
         chain_stage_q8<kSync>(xq, n, c0, c1, gen, err, slice);
         return;
@@ -363,6 +411,29 @@ __device__ __noinline__ void chain_stage(const void* x, const uint64_t* x2, cons
             for (int cc = 0; cc < kB; ++cc)
                 if (cc < cnt) chain_quant((f32x4){v[cc][0], v[cc][1], v[cc][2], v[cc][3]}, b0 + cc, nb,
                                           slice + (b0 + cc - c0) * 64);
+        }
+        return;
+    }
+    if (kSync == kChainTagged && norm && nc * 256 <= kChainNormShare) {  // the workgroup's copy (same order)
+        chain_norm_shared<kSync>(cm, nc, phase, gen, err);
+        float p = 0.0f;
+        for (int cb = 0; cb < nc; cb += 4) {  // four chunks' reads issued before their fmafs
+            f32x4 f[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f[j] = chain_xs[min(cb + j, nc - 1) * 64 + lane];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (cb + j < nc && (cb + j) * 256 + 4 * lane < n) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) p = fmaf(f[j][k], f[j][k], p);
+                }
+        }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
+        const float sn = sqrtf(p / (float)n + 1e-6f);
+        for (int c = c0; c < c1; ++c) {
+            const f32x4 f = chain_xs[c * 64 + lane];
+            chain_quant((f32x4){f[0] / sn, f[1] / sn, f[2] / sn, f[3] / sn}, c, nb, slice + (c - c0) * 64);
         }
         return;
     }
@@ -450,7 +521,7 @@ struct ActStaged {
                 const int lines = max(c1 - c0 - 2, 0) * (kChunkBytes / 128);
                 for (int i = lane; i < lines; i += 64) touch ^= *gp<uint32_t>(w0 + (size_t)i * 128);
             }
-            chain_stage<kSync>(cm.x, cm.x2, cm.xq, cm.x_plain, cm.norm, cm.m.cols, c0, c1, gen, err, slice);
+            chain_stage<kSync>(cm.x, cm.x2, cm.xq, cm.x_plain, cm.norm, cm.m.cols, c0, c1, phase, gen, err, slice);
             if (gen == 0) err[2] = touch;  // never taken (tags start at 1); keeps the touches
             staged = true;
             key = {phase, c0, c1};
@@ -848,6 +919,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_chain(ChainParams P) {
         gwr<uint64_t>(P.trace)[(size_t)P.n_phases * nwg + b] = __builtin_amdgcn_s_memrealtime();
     uint32_t begin = 0;
     StageKey key{-1, 0, 0};  // this wave's LDS slice holds nothing yet
+    if (threadIdx.x == 0) chain_xs_claim = chain_xs_ready = -1;  // no phase's vector yet
+    __syncthreads();
     for (int p = 0; p < P.n_phases; ++p) {
         const uint32_t end = P.phase_end[p];
         const uint32_t j0 = (b + nwg - begin % nwg) % nwg;  // phase tiles start on workgroup begin mod nwg
