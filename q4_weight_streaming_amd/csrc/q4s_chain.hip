@@ -382,6 +382,39 @@ __device__ __forceinline__ void chain_norm_shared(const ChainSrc& cm, int nc, in
     }
 }
 
+// The norm prologue from the workgroup's copy of the vector: the same sum of
+// squares (lane partials over elements 256c + 4 lane + k, chunk by chunk, then
+// the xor butterfly), divisor and quantization as the per-wave path in
+// chain_stage.  Inlined into the tile code rather than added to chain_stage:
+// as part of that called function it would push its register use past what a
+// call may clobber, and every call would save registers to scratch memory.
+template <int kSync>
+__device__ __forceinline__ void chain_stage_norm_shared(ChainSrc cm, int nc, int c0, int c1, int phase,
+                                                     uint32_t gen, uint32_t* err, Q4S_LDS u32x2* slice) {
+    const int lane = threadIdx.x & 63;
+    const int n = cm.n, nb = n / 32;
+    chain_norm_shared<kSync>(cm, nc, phase, gen, err);
+    float p = 0.0f;
+    for (int cb = 0; cb < nc; cb += 2) {  // two chunks' reads issued before their fmafs
+        f32x4 f[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) f[j] = chain_xs[min(cb + j, nc - 1) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (cb + j < nc && (cb + j) * 256 + 4 * lane < n) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) p = fmaf(f[j][k], f[j][k], p);
+            }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
+    const float sn = sqrtf(p / (float)n + 1e-6f);
+    for (int c = c0; c < c1; ++c) {
+        const f32x4 f = chain_xs[c * 64 + lane];
+        chain_quant((f32x4){f[0] / sn, f[1] / sn, f[2] / sn, f[3] / sn}, c, nb, slice + (c - c0) * 64);
+    }
+}
+
 // Prologue of a chained-step wave that streams chunks [c0, c1): waits for the
 // activation, takes the RMS norm of the whole vector when asked, and leaves
 // the Q8_0 codes and scales of its chunks in its LDS slice ([chunk][lane]).
@@ -391,8 +424,7 @@ __device__ __forceinline__ void chain_norm_shared(const ChainSrc& cm, int nc, in
 // step adds the same two values on both lanes.
 template <int kSync>
 __device__ __noinline__ void chain_stage(const void* x, const uint64_t* x2, const uint64_t* xq, int x_plain, int norm,
-                                         int n, int c0, int c1, int phase, uint32_t gen, uint32_t* err,
-                                         Q4S_LDS u32x2* slice) {
+                                         int n, int c0, int c1, uint32_t gen, uint32_t* err, Q4S_LDS u32x2* slice) {
     if (xq) {  // already quantized by the producing tiles
         chain_stage_q8<kSync>(xq, n, c0, c1, gen, err, slice);
         return;
@@ -411,29 +443,6 @@ __device__ __noinline__ void chain_stage(const void* x, const uint64_t* x2, cons
             for (int cc = 0; cc < kB; ++cc)
                 if (cc < cnt) chain_quant((f32x4){v[cc][0], v[cc][1], v[cc][2], v[cc][3]}, b0 + cc, nb,
                                           slice + (b0 + cc - c0) * 64);
-        }
-        return;
-    }
-    if (kSync == kChainTagged && norm && nc * 256 <= kChainNormShare) {  // the workgroup's copy (same order)
-        chain_norm_shared<kSync>(cm, nc, phase, gen, err);
-        float p = 0.0f;
-        for (int cb = 0; cb < nc; cb += 4) {  // four chunks' reads issued before their fmafs
-            f32x4 f[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) f[j] = chain_xs[min(cb + j, nc - 1) * 64 + lane];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (cb + j < nc && (cb + j) * 256 + 4 * lane < n) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) p = fmaf(f[j][k], f[j][k], p);
-                }
-        }
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
-        const float sn = sqrtf(p / (float)n + 1e-6f);
-        for (int c = c0; c < c1; ++c) {
-            const f32x4 f = chain_xs[c * 64 + lane];
-            chain_quant((f32x4){f[0] / sn, f[1] / sn, f[2] / sn, f[3] / sn}, c, nb, slice + (c - c0) * 64);
         }
         return;
     }
@@ -521,7 +530,12 @@ struct ActStaged {
                 const int lines = max(c1 - c0 - 2, 0) * (kChunkBytes / 128);
                 for (int i = lane; i < lines; i += 64) touch ^= *gp<uint32_t>(w0 + (size_t)i * 128);
             }
-            chain_stage<kSync>(cm.x, cm.x2, cm.xq, cm.x_plain, cm.norm, cm.m.cols, c0, c1, phase, gen, err, slice);
+            const int n = cm.m.cols, nc = (n / 32 + kChunkBlocks - 1) / kChunkBlocks;
+            if (kSync == kChainTagged && cm.norm && !cm.xq && !cm.x2 && nc * 256 <= kChainNormShare)
+                chain_stage_norm_shared<kSync>(ChainSrc{cm.x, nullptr, cm.x_plain, n}, nc, c0, c1, phase, gen, err,
+                                               slice);  // from the workgroup's copy of the vector
+            else
+                chain_stage<kSync>(cm.x, cm.x2, cm.xq, cm.x_plain, cm.norm, n, c0, c1, gen, err, slice);
             if (gen == 0) err[2] = touch;  // never taken (tags start at 1); keeps the touches
             staged = true;
             key = {phase, c0, c1};
