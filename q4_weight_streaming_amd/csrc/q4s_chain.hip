@@ -348,6 +348,30 @@ __device__ __forceinline__ MatDesc chain_group(const ChainMat& cm, int64_t vg, i
     return m;
 }
 
+// p + (p of lane ^ d) for d = 32, 16, 8, 4, 2, 1 in turn: the xor butterfly
+// of __shfl_xor, every lane ending with the same sum (each step adds the same
+// two values on both lanes of a pair), by lane swaps and DPP moves instead of
+// LDS permutes, which a lone wave waits out one after another.  Called by a
+// whole wave.
+constexpr int kDppRowShl4 = 0x104;  // row_shl:4: lane i <- lane i + 4 within 16
+constexpr int kDppRowShr4 = 0x114;  // row_shr:4: lane i <- lane i - 4 within 16
+constexpr int kDppRowRor8 = 0x128;  // row_ror:8: lane i <- lane i ^ 8 within 16
+__device__ __forceinline__ float wave_sum_xor(float p) {
+    const int lane = threadIdx.x & 63;
+    uint32_t v = __float_as_uint(p);
+    auto step = [&](uint32_t a, uint32_t b) { v = __float_as_uint(__uint_as_float(a) + __uint_as_float(b)); };
+    auto sw32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // {own, lane ^ 32}
+    step(sw32[0], sw32[1]);
+    auto sw16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // {own, lane ^ 16}
+    step(sw16[0], sw16[1]);
+    step(v, dpp_move<kDppRowRor8>(v));
+    const uint32_t up = dpp_move<kDppRowShl4>(v), down = dpp_move<kDppRowShr4>(v);
+    step(v, (lane & 4) ? down : up);
+    step(v, dpp_move<kDppQuadSwap2>(v));
+    step(v, dpp_move<kDppQuadSwap1>(v));
+    return __uint_as_float(v);
+}
+
 // The workgroup's copy of a norm phase's vector (nc chunks, nc * 256 <=
 // kChainNormShare) in chain_xs: loaded by the wave that claims it, waited for
 // by the others.  Called by a whole wave.
@@ -406,8 +430,7 @@ __device__ __forceinline__ void chain_stage_norm_shared(ChainSrc cm, int nc, int
                 for (int k = 0; k < 4; ++k) p = fmaf(f[j][k], f[j][k], p);
             }
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
+    p = wave_sum_xor(p);
     const float sn = sqrtf(p / (float)n + 1e-6f);
     for (int c = c0; c < c1; ++c) {
         const f32x4 f = chain_xs[c * 64 + lane];
@@ -459,9 +482,7 @@ __device__ __noinline__ void chain_stage(const void* x, const uint64_t* x2, cons
                 for (int k = 0; k < 4; ++k)
                     if (cc < cnt && (b0 + cc) * 256 + 4 * lane + k < n) p = fmaf(v[cc][k], v[cc][k], p);
         }
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) p = p + __shfl_xor(p, d);
-        s = sqrtf(p / (float)n + 1e-6f);
+        s = sqrtf(wave_sum_xor(p) / (float)n + 1e-6f);
         if (nc <= kChainBatch) {  // the one batch was the whole vector: quantize this wave's chunks from it
 #pragma unroll
             for (int cc = 0; cc < kChainBatch; ++cc)
