@@ -326,8 +326,9 @@ __device__ __forceinline__ void chain_store_q8(uint64_t* yq, int64_t rows, int64
         else
             code = (uint32_t)(uint8_t)(int8_t)(int)roundf(p / dd);
     }
-    const uint32_t word = code | (__shfl_down(code, 1) << 8) | (__shfl_down(code, 2) << 16) |
-                          (__shfl_down(code, 3) << 24);
+    // lane 4k gathers the codes of lanes 4k+1 .. 4k+3 (quad_perm broadcasts, no LDS permutes)
+    const uint32_t word = code | (dpp_move<0x55>(code) << 8) | (dpp_move<0xAA>(code) << 16) |
+                          (dpp_move<0xFF>(code) << 24);
     const uint32_t dbits = __float_as_uint(__half2float(__float2half_rn(dd)));
     if (valid && (lane & 3) == 0) chain_st<kSync>(yq + row / 4, tag_bits(word, gen));
     if (valid && (lane & 31) == 0) chain_st<kSync>(yq + rows / 4 + row / 32, tag_bits(dbits, gen));
