@@ -23,6 +23,7 @@
 #include "q4s_device.h"
 
 #include <mutex>
+#include <type_traits>
 
 namespace q4s {
 namespace {
@@ -30,15 +31,62 @@ namespace {
 constexpr int kHd = kAttnHeadDim;     // 128
 constexpr int kSplit = kAttnSplit;    // 64 positions per split
 
+// op(v, v of lane ^ D), the same value in both lanes of each pair (op is
+// commutative: max or +), by lane swaps (D = 32, 16) and DPP moves (D = 8, 4, 2,
+// 1) instead of LDS permutes.  Called by a whole wave.
+template <int D, class Op>
+__device__ __forceinline__ float xor_combine(float v, Op op) {
+    const uint32_t x = __float_as_uint(v);
+    auto dpp = [](uint32_t y, auto ctrl) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)y, decltype(ctrl)::value, 0xF, 0xF, true);
+    };
+    if constexpr (D == 32 || D == 16) {
+        const auto sw = D == 32 ? __builtin_amdgcn_permlane32_swap(x, x, false, false)
+                                : __builtin_amdgcn_permlane16_swap(x, x, false, false);  // {own, partner}
+        return op(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    } else {
+        uint32_t y;
+        if constexpr (D == 8) {
+            y = dpp(x, std::integral_constant<int, 0x128>{});  // row_ror:8
+        } else if constexpr (D == 4) {  // row_shl:4 (lane i + 4) or row_shr:4 (lane i - 4) by lane bit 2
+            const uint32_t up = dpp(x, std::integral_constant<int, 0x104>{});
+            const uint32_t down = dpp(x, std::integral_constant<int, 0x114>{});
+            y = (threadIdx.x & 4) ? down : up;
+        } else if constexpr (D == 2) {
+            y = dpp(x, std::integral_constant<int, 0x4E>{});  // quad_perm [2,3,0,1]
+        } else {
+            y = dpp(x, std::integral_constant<int, 0xB1>{});  // quad_perm [1,0,3,2]
+        }
+        return op(v, __uint_as_float(y));
+    }
+}
+constexpr auto kMax = [](float a, float b) { return fmaxf(a, b); };
+constexpr auto kAdd = [](float a, float b) { return a + b; };
+
+// The wave's maximum / sum by the xor butterfly 32, 16, 8, 4, 2, 1.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+    v = xor_combine<32>(v, kMax);
+    v = xor_combine<16>(v, kMax);
+    v = xor_combine<8>(v, kMax);
+    v = xor_combine<4>(v, kMax);
+    v = xor_combine<2>(v, kMax);
+    return xor_combine<1>(v, kMax);
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v = xor_combine<32>(v, kAdd);
+    v = xor_combine<16>(v, kAdd);
+    v = xor_combine<8>(v, kAdd);
+    v = xor_combine<4>(v, kAdd);
+    v = xor_combine<2>(v, kAdd);
+    return xor_combine<1>(v, kAdd);
+}
+// Over the lanes 4, 8, 16 and 32 apart (the combine's 16 slices of a wave), in that order.
+template <class Op>
+__device__ __forceinline__ float slices_combine(float v, Op op) {
+    v = xor_combine<4>(v, op);
+    v = xor_combine<8>(v, op);
+    v = xor_combine<16>(v, op);
+    return xor_combine<32>(v, op);
 }
 
 // workspace (S * attn_split_floats(n_q) floats), head-major so that the combine reads
@@ -205,8 +253,8 @@ __global__ __launch_bounds__(kCombSlices * kCombQuads) void k_attn_combine(AttnP
     for (int i = 0; i < kCombBatch; ++i)
         if (s0 + i < s1) mk = fmaxf(mk, mm[i]);
     for (int b = s0 + kCombBatch; b < s1; ++b) mk = fmaxf(mk, om[b]);
-#pragma unroll
-    for (int off = kCombQuads; off < 64; off <<= 1) mk = fmaxf(mk, __shfl_xor(mk, off, 64));
+    static_assert(kCombQuads == 4, "the slices of a wave sit 4, 8, 16 and 32 lanes apart");
+    mk = slices_combine(mk, kMax);
     if (lane == 0) mred[wv] = mk;
     __syncthreads();
     float M = mred[0];
@@ -226,11 +274,8 @@ __global__ __launch_bounds__(kCombSlices * kCombQuads) void k_attn_combine(AttnP
         }
     }
 #pragma unroll
-    for (int off = kCombQuads; off < 64; off <<= 1) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) nu[c] += __shfl_xor(nu[c], off, 64);
-        de += __shfl_xor(de, off, 64);
-    }
+    for (int c = 0; c < 4; ++c) nu[c] = slices_combine(nu[c], kAdd);
+    de = slices_combine(de, kAdd);
     if (lane < kCombQuads) num[wv][dq] = nu;
     if (lane == 0) den[wv] = de;
     __syncthreads();
