@@ -115,7 +115,24 @@ def test_chain_wide_hidden_unpaired(oracle, mode):
     _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, "wide hidden")
 
 
-@pytest.mark.parametrize("F,workgroups", [(4608, 0), (4608, 5), (17408, 0), (17408, 5), (32768, 0), (32768, 5)],
+@pytest.mark.parametrize("workgroups", [0, 5], ids=["per_cu", "wg5"])
+def test_chain_norm_vector_shared_at_its_limit(oracle, workgroups):
+    """Tagged phases read a norm phase's vector once per workgroup into LDS when it
+    has at most 4096 elements: hidden 4096 fills that copy (16 chunks).  With 5
+    workgroups each one runs many tiles of every norm phase, so most tiles find
+    the phase's vector already claimed and wait for it instead of loading it;
+    two layers make each workgroup claim a new phase after an old one."""
+    require_gpu()
+    L, E, D, F, V = 2, 4096, 64, 384, 320
+    shapes, ws, h0 = _inputs(49, L, E, D, F, V, scale=0.05, outliers=0)
+    ref_acts, ref_logits = oracle.chain_step(ws, E, D, F, V, h0)
+    wp, h0d, acts, logits = _device(shapes, ws, h0, L, E, D, F, V)
+    vals, tags, lg, info = _run(wp, h0d, acts, logits, L, E, D, F, V, q.CHAIN_TAGGED, workgroups, steps=2)
+    assert (tags == 2).all()
+    _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, f"hidden 4096, {workgroups} workgroups")
+
+
+@pytest.mark.parametrize("F,workgroups",[(4608, 0), (4608, 5), (17408, 0), (17408, 5), (32768, 0), (32768, 5)],
                          ids=["ranges4_per_cu", "ranges4_wg5", "ranges17_per_cu", "ranges17_wg5",
                               "ranges32_per_cu", "ranges32_wg5"])
 def test_chain_k_range_tiles_bit_exact(oracle, F, workgroups):
