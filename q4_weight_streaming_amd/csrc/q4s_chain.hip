@@ -635,11 +635,13 @@ __device__ __forceinline__ void chain_tile(const ChainMat& cm, int64_t gset, flo
 // tile) or, for at most 8 chunks, 2 waves (wpg = 2: two groups per tile).  Wave lw of a group stages
 // and multiplies chunks [ceil(lw C/wpg), ceil((lw+1) C/wpg)) and leaves each
 // block's exact integer sum (as int16: |s| <= 32512) and its binary16 d_w in
-// the group's term table; then wave lw < ks of the group runs the fixed-order
-// fp32 chain of K range lw over those terms -- the same fmaf(d_w/16 * d_x,
-// 16 s, chain) per block, in the same order, as wave_task -- and the ranges are
-// added in order.  So the result is bit-identical to the one-wave-per-range
-// tile, with 1/wpg of the serial work per wave.
+// the group's term table, and its blocks' d_x in the d_x table; then K range r
+// of the group runs on its waves 2r (chain A, blocks 0-3 of every chunk) and
+// 2r + 1 (chain B, blocks 4-7) -- wave_task's chains, in its order, each term
+// fmaf(d_w * d_x, s, p), the bits of wave_task's fmaf(d_w/16 * d_x, 16 s, p)
+// -- and the ranges' 0 + (A + B) are added in order.  So the result is
+// bit-identical to the one-wave-per-range tile, with 1/wpg of the integer work
+// per wave.
 constexpr int kChainSplitChunks = 16;  // chunks of a matrix with ks <= 2
 constexpr int kChainTermWords = kChainSplitChunks * kChunkBlocks * 64;  // one group's term table
 // the workgroup's term table: a split tile's group(s), or a K-range tile's range
