@@ -546,7 +546,7 @@ q4s_status q4s_sweep_run(const q4s_plan* p, void* stream) {
     if (!p->quant.empty()) {
         hipError_t e = launch_quantize_batch((const QuantDesc*)(p->dev + p->off_quant),
                                              (const uint32_t*)(p->dev + p->off_qtiles),
-                                             (int64_t)p->qtiles.size() / 2, st);
+                                             (int64_t)p->qtiles.size() / 2, p->n, st);
         if (e != hipSuccess) return hip_status(e, "sweep quantize launch");
     }
     if (p->split_tiles)

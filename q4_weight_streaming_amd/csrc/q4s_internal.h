@@ -77,7 +77,8 @@ hipError_t launch_repack(const uint8_t* w, uint8_t* packed, int64_t rows, int64_
                          hipStream_t st);
 hipError_t launch_quantize(const QuantDesc& d, hipStream_t st);
 constexpr int kQuantTileBlocks = 32;   // Q8_0 blocks per workgroup of the batched quantizer
-hipError_t launch_quantize_batch(const QuantDesc* dev_descs, const uint32_t* dev_tiles, int64_t n_tiles,
+// n: the sweep's activation rows (non-temporal stores up to kTokTile rows)
+hipError_t launch_quantize_batch(const QuantDesc* dev_descs, const uint32_t* dev_tiles, int64_t n_tiles, int n,
                                  hipStream_t st);
 hipError_t launch_gemv(const MatDesc& m, int n, int64_t n_gsets, hipStream_t st);
 // Tiles are (matrix, group set) pairs; with n == 1 a single-split matrix's tiles are its row groups.
