@@ -377,9 +377,10 @@ __device__ __forceinline__ void quant_local(const QuantDesc& qd, int64_t lb, boo
 }
 
 // Standalone quantization: 32 blocks per 256-thread workgroup.
+template <bool kNt>
 __global__ __launch_bounds__(256) void k_quantize(QuantDesc qd, int64_t total_blocks) {
     const int64_t lb = (int64_t)blockIdx.x * kQuantTileBlocks + (threadIdx.x >> 3);
-    quant_local<false>(qd, lb, lb < total_blocks);
+    quant_local<kNt>(qd, lb, lb < total_blocks);
 }
 
 // Batched quantization for the sweep: workgroup i takes tile i = (activation,
@@ -643,7 +644,10 @@ hipError_t launch_quantize(const QuantDesc& d, hipStream_t st) {
     const int64_t total = (int64_t)d.n * (d.cols / 32);
     if (total == 0) return hipSuccess;
     const int64_t grid = (total + kQuantTileBlocks - 1) / kQuantTileBlocks;
-    hipLaunchKernelGGL(k_quantize, dim3((unsigned)grid), dim3(256), 0, st, d, total);
+    if (d.n <= kTokTile)
+        hipLaunchKernelGGL(k_quantize<true>, dim3((unsigned)grid), dim3(256), 0, st, d, total);
+    else
+        hipLaunchKernelGGL(k_quantize<false>, dim3((unsigned)grid), dim3(256), 0, st, d, total);
     return hipGetLastError();
 }
 
