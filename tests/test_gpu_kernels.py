@@ -46,7 +46,9 @@ def test_quantize_golden_blocks(oracle):
         assert list(got[0, i, 2:].view(np.int8)) == [int(t) for t in c["q"]]
 
 
-@pytest.mark.parametrize("n,cols", [(1, 1536), (3, 8960), (8, 3584), (8, 18944), (2, 32), (5, 96)])
+# up to 8 rows the quantizer stores with the non-temporal hint, past 8 without: both are covered
+@pytest.mark.parametrize("n,cols", [(1, 1536), (3, 8960), (8, 3584), (8, 18944), (2, 32), (5, 96),
+                                    (9, 1536), (24, 288), (17, 8960)])
 def test_quantize_bit_exact(oracle, n, cols):
     x = synth.activation(n, cols, synth.generator(7, n, cols, 1))
     got = q8_canonical(q.quantize_q8_0(to_dev(x)), n, cols)

@@ -194,11 +194,11 @@ def _adversarial_blocks(rng, nblk):
     return blocks
 
 
-@pytest.mark.parametrize("n", [1, 4, 8])
+@pytest.mark.parametrize("n", [1, 4, 8, 16])
 def test_sweep_quantizers_near_ties_and_extreme_scales(oracle, n):
-    # the sweep's quantizers (one row: inside the GEMV launch; 2..8 rows: the batched quantize
-    # launch) on adversarial activations: x_q8 equals the oracle's Q8_0 bytes, y the GEMV of
-    # those bytes
+    # the sweep's quantizers (one row: inside the GEMV launch; 2..24 rows: the batched quantize
+    # launch, storing with the non-temporal hint up to 8 rows and without past 8) on adversarial
+    # activations: x_q8 equals the oracle's Q8_0 bytes, y the GEMV of those bytes
     require_gpu()
     rng = np.random.default_rng(300 + n)
     shapes = [synth.MatShape("a", 130, 4096), synth.MatShape("b", 64, 1056)]
