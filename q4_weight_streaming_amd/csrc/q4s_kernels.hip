@@ -402,20 +402,22 @@ __global__ __launch_bounds__(256) void k_quantize_batch(const QuantDesc* __restr
 // A 1-row GEMV or sweep whose matrices all have one K split (C <= 8 chunks):
 // each row group (a table entry: matrix, row group) gets its own workgroup of
 // kSplitWaves waves.  Wave w takes chunks [ceil(wC/W), ceil((w+1)C/W)) -- one
-// chunk at most with 8 waves -- issues its loads at once, and leaves each
-// block's exact integer sum (int16: |s| <= 32512) and binary16 d_w in LDS,
-// plus the chunk's d_x when it quantized the activation itself.  Waves 0 and 1
-// then run chains A (blocks 0-3) and B (blocks 4-7) over all chunks in order
-// with wave_task's fmaf, and wave 0 adds 0 + (A + B): bit-identical to a wave
-// task over the whole row, with every weight load of the row group in flight
-// from the start.  (A lone output head, 2374 row groups of 6 chunks, is too
+// chunk at most with 8 waves -- issues its loads at once, and leaves in LDS
+// each block's exact integer sum (int16: |s| <= 32512) and the fp32 product
+// (d_w / 16) * d_x, formed as wave_task forms it.  Waves 0 and 1 then read
+// all of their factors at once and run chains A (blocks 0-3) and B (blocks
+// 4-7) over all chunks in order with wave_task's fmaf, and wave 0 adds
+// 0 + (A + B): bit-identical to a wave task over the whole row, with every
+// weight load of the row group in flight from the start.  (Reading d_x inside
+// the chain cost the GEMV over quantized codes a global load per chunk: the
+// lone head 22.3 -> 21.8 us with the products formed by the chunk's wave.)  (A lone output head, 2374 row groups of 6 chunks, is too
 // small for waves that stream their chunks two at a time: one wave per row
 // group took 22.7 us as a plain GEMV and 23.1 us quantizing on the fly, 8 waves
 // take 22.6 and 22.2 us; 2 and 4 waves were slower.)
 constexpr int kSplitWaves = 8;
 struct SplitLds {
-    uint32_t terms[kChunkBlocks * kChunkBlocks * 64];  // [chunk][block][lane], C <= 8
-    uint32_t dx[kChunkBlocks * kChunkBlocks];          // fp32 bits of d_x per block
+    float a[kChunkBlocks * kChunkBlocks * 64];      // [chunk][block][lane]: (d_w / 16) * d_x, fp32
+    uint32_t s[kChunkBlocks * kChunkBlocks / 2 * 64]; // [chunk][block pair][lane]: the two exact sums, int16 each
     float chain_b[64];
 };
 
@@ -444,6 +446,7 @@ __device__ __forceinline__ void split_group(const MatDesc& m, int g, SplitLds& l
             const int c = i0 + k;
             if (c >= i1) break;
             int s16[kChunkBlocks];
+            float dx[kChunkBlocks];
             if constexpr (kFused) {
                 const auto pr = aq.prepare(k, c);
                 uint32_t y[4];
@@ -458,35 +461,52 @@ __device__ __forceinline__ void split_group(const MatDesc& m, int g, SplitLds& l
 #pragma unroll
                     for (int x = 0; x < 4; ++x) s16[4 * h + x] = sh[x];
                 }
-                if ((lane & 7) == 0) l.dx[c * kChunkBlocks + (lane >> 3)] = pr.dbits;
+#pragma unroll
+                for (int b = 0; b < kChunkBlocks; ++b) dx[b] = aq.d(pr, 0, 0, b);
             } else {
 #pragma unroll
                 for (int b = 0; b < kChunkBlocks; ++b) {
                     // padding blocks of the last chunk have zero nibbles; read a valid block
                     const int blk = min(c * kChunkBlocks + b, m.nb - 1);
                     s16[b] = block_dot16(unpack(ch[k].nib[b]), act_q(m.xq, (int64_t)blk * 32));
+                    dx[b] = act_d(m.xd, blk);
                 }
             }
+            // the chain's factors, formed here with the chain's own fp32 operations
 #pragma unroll
             for (int b = 0; b < kChunkBlocks; ++b) {
                 const uint32_t sw = ch[k].scale[b >> 1];
-                const uint32_t dw_bits = (b & 1) ? (sw >> 16) : (sw & 0xffffu);
-                l.terms[(c * kChunkBlocks + b) * 64 + lane] = (uint32_t)(uint16_t)(int16_t)(s16[b] >> 4) | (dw_bits << 16);
+                const float dw16 = ((b & 1) ? half_hi(sw) : half_lo(sw)) * 0.0625f;
+                l.a[(c * kChunkBlocks + b) * 64 + lane] = dw16 * dx[b];
             }
+#pragma unroll
+            for (int b = 0; b < kChunkBlocks; b += 2)
+                l.s[(c * (kChunkBlocks / 2) + b / 2) * 64 + lane] =
+                    (uint32_t)(uint16_t)(int16_t)(s16[b] >> 4) | ((uint32_t)(uint16_t)(int16_t)(s16[b + 1] >> 4) << 16);
         }
     }
     __syncthreads();
     float p = 0.0f;
     if (wave < 2) {
-        for (int c = 0; c < C; ++c) {
+        // every factor of the chain is read before its first fmaf, so the
+        // dependent chain does not wait on LDS between chunks
+        float av[kChunkBlocks][4];
+        uint32_t sv[kChunkBlocks][2];
+#pragma unroll
+        for (int c = 0; c < kChunkBlocks; ++c) {
+            if (c >= C) break;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) av[c][x] = l.a[(c * kChunkBlocks + 4 * wave + x) * 64 + lane];
+#pragma unroll
+            for (int y = 0; y < 2; ++y) sv[c][y] = l.s[(c * (kChunkBlocks / 2) + 2 * wave + y) * 64 + lane];
+        }
+#pragma unroll
+        for (int c = 0; c < kChunkBlocks; ++c) {
+            if (c >= C) break;
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                const int b = 4 * wave + x;
-                const uint32_t t = l.terms[(c * kChunkBlocks + b) * 64 + lane];
-                const float dw16 = half_hi(t) * 0.0625f;
-                const float dx = kFused ? __uint_as_float(l.dx[c * kChunkBlocks + b])
-                                        : act_d(m.xd, min(c * kChunkBlocks + b, m.nb - 1));
-                p = fmaf(dw16 * dx, (float)((int)(int16_t)(t & 0xffffu) * 16), p);
+                const int sb = (int)(int16_t)(uint16_t)(sv[c][x >> 1] >> (16 * (x & 1)));
+                p = fmaf(av[c][x], (float)(sb * 16), p);
             }
         }
         if (wave == 1) l.chain_b[lane] = p;
@@ -500,8 +520,9 @@ __device__ __forceinline__ void split_group(const MatDesc& m, int g, SplitLds& l
     }
 }
 
+// At most 64 VGPRs, so that 4 workgroups of 8 waves stay resident per CU.
 template <bool kFused, int kW, bool kTrace>
-__global__ __launch_bounds__(64 * kW) void k_sweep_split(const MatDesc* __restrict__ mats,
+__global__ __launch_bounds__(64 * kW, 8) void k_sweep_split(const MatDesc* __restrict__ mats,
                                                           const uint32_t* __restrict__ tiles,
                                                           uint64_t* __restrict__ trace) {
     __shared__ SplitLds l;
@@ -512,7 +533,7 @@ __global__ __launch_bounds__(64 * kW) void k_sweep_split(const MatDesc* __restri
 }
 
 template <int kW>
-__global__ __launch_bounds__(64 * kW) void k_gemv_split(MatDesc m) {
+__global__ __launch_bounds__(64 * kW, 8) void k_gemv_split(MatDesc m) {
     __shared__ SplitLds l;
     split_group<false, kW>(m, blockIdx.x, l);
 }
