@@ -86,6 +86,24 @@ def test_chain_small_bit_exact(oracle, mode, workgroups):
     _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, f"mode {mode}")
 
 
+@pytest.mark.parametrize("workgroups", [0, 5], ids=["per_cu", "wg5"])
+@pytest.mark.parametrize("E,F", [(768, 2304), (1280, 1024)], ids=["ranges_3_4_5", "ranges_5_4"])
+def test_chain_split_range_lengths(oracle, E, F, workgroups):
+    """Split tiles whose K ranges hold 3, 4 and 5 chunks (hidden 768: 3 chunks; ff 2304: 9
+    chunks in two K splits of 4 and 5; hidden 1280: 5 chunks; ff 1024: 4), each range's chain
+    read and added as one batch of exactly its chunks; on 256 and on 5 workgroups (coarser
+    layouts): bit-exact against the oracle's fixed order, tagged phases."""
+    require_gpu()
+    L, D, V = 2, 64, 320
+    shapes, ws, h0 = _inputs(44, L, E, D, F, V)
+    ref_acts, ref_logits = oracle.chain_step(ws, E, D, F, V, h0)
+    wp, h0d, acts, logits = _device(shapes, ws, h0, L, E, D, F, V)
+    vals, tags, lg, info = _run(wp, h0d, acts, logits, L, E, D, F, V, q.CHAIN_TAGGED, workgroups)
+    assert info["n_phases"] == 4 * L + 1
+    assert (tags == 1).all()
+    _compare(ref_acts, ref_logits, vals, lg, L, E, D, F, f"E={E} F={F}")
+
+
 @pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
 def test_chain_ragged_shapes(oracle, mode):
     """hidden 96 and ff 160 (partial chunks), kv_dim 5 and vocab 77 (partial row groups),
